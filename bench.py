@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark: Lloyd iterations/s of exact batched K-Means on one MI355X.
+
+One step = one Lloyd iteration over the whole batch: centroid norms,
+FlashAssign, sort-inverse update (histogram, scan, inverse permutation,
+segment reduction, finalize). The timed region is one fk_lloyd call running
+exactly --steps iterations (tol = 0) on inputs already resident in HBM,
+bracketed by device synchronisations. Per-phase GPU times come from HIP
+events the library records on the same stream during that call.
+
+Default workload: B=32, N=75600, d=128, K=1000, fp16 (the API example shape),
+i.i.d. N(0,1) points, K random points per problem as initial centroids.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_F16 = 2500.0       # TFLOP/s, dense fp16/bf16
+PEAK_HBM = 8000.0            # GB/s
+PEAK_VALU_F32 = 157.3        # TFLOP/s
+METRIC = "Lloyd iter/s + assign/update ms at B32 N75600 K1000 d128 fp16; % MFMA/HBM peak"
+WORKLOADS = ("api_example", "io_breakdown", "large_k_zipf", "split_d", "tiny_f32")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def elem_bytes(dtype: str) -> int:
+    return 4 if dtype == "f32" else 2
+
+
+def assign_flop(B, N, d, K) -> float:
+    return 2.0 * B * N * K * d
+
+
+def assign_bytes(B, N, d, K, s) -> float:
+    # reads X and the centroid copy once, writes ids once (+ norms)
+    return B * (N * d * s + K * d * s + 4 * N + 4 * K)
+
+
+def update_bytes(B, N, d, K, s) -> float:
+    # x gathered once; ids read twice, perm written and read; sums written and
+    # read, old centroids read, new written; counts/offsets
+    return B * N * d * s + 16.0 * B * N + 16.0 * B * K * d + 16.0 * B * K
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("assign.hip", "fk_internal.hpp"):
+        with open(os.path.join(ROOT, "exact_means_clustering_flashassign_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per assign launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_batches: int):
+    """The oracle, untuned, on a bounded sample: one Lloyd iteration over
+    n_batches of the B problems (full N, K, d), scaled to the whole batch."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    nb = min(n_batches, w.B)
+    x64 = w.x64()[:nb]
+    c0 = w.init64()[:nb]
+    t0 = time.perf_counter()
+    oracle.lloyd(x64, c0, 1, 0.0, w.dtype, want_near=False)
+    dt = time.perf_counter() - t0
+    per_iter_full = dt * w.B / nb
+    return {"value": 1.0 / per_iter_full, "unit": "iter/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"1 Lloyd iteration of {nb} of the {w.B} problems (full N, K, d), "
+                      f"fp64 NumPy on the host, {dt:.1f} s, scaled by {w.B}/{nb}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="api_example", choices=WORKLOADS)
+    ap.add_argument("--cpu-batches", type=int, default=8,
+                    help="problems in the CPU-baseline sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every box here has one GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthdata
+    import exact_means_clustering_flashassign_amd as fk
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fk.load()
+    dev = torch.device("cuda:0")
+    w = synthdata.make_workload(args.workload)
+    x = synthdata.to_torch(w.x, w.dtype).to(dev)
+    init = synthdata.to_torch(w.init, w.dtype).to(dev)
+    B, N, d, K = w.B, w.N, w.d, w.K
+    ids = torch.empty((B, N), dtype=torch.int32, device=dev)
+    centers = torch.empty((B, K, d), dtype=torch.float32, device=dev)
+    ws = fk.workspace(x.dtype, B, N, d, K, dev)
+
+    if args.warmup > 0:
+        fk.fk_lloyd(x, init, args.warmup, 0.0, ids=ids, centers=centers, ws=ws)
+    torch.cuda.synchronize()
+    fk.fk_trace_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, _, n_iter = fk.fk_lloyd(x, init, args.steps, 0.0, ids=ids, centers=centers, ws=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tr = fk.fk_trace_end()
+    assert n_iter == args.steps and tr["iterations"] == args.steps
+
+    elapsed = t1 - t0
+    ms_step = 1e3 * elapsed / args.steps
+    s = elem_bytes(w.dtype)
+    a_ms = tr["assign_ms"] / tr["iterations"]
+    u_ms = tr["update_ms"] / tr["iterations"]
+    n_ms = tr["norms_ms"] / tr["iterations"]
+    flop = assign_flop(B, N, d, K)
+    a_bytes = assign_bytes(B, N, d, K, s)
+    u_bytes = update_bytes(B, N, d, K, s)
+    if w.dtype == "f32":
+        bound, peak, unit = "alu", PEAK_VALU_F32, "TFLOP/s"
+        achieved = flop / (a_ms * 1e-3) / 1e12
+    elif flop / a_bytes > PEAK_MFMA_F16 * 1e12 / (PEAK_HBM * 1e9):
+        bound, peak, unit = "mfma", PEAK_MFMA_F16, "TFLOP/s"
+        achieved = flop / (a_ms * 1e-3) / 1e12
+    else:
+        bound, peak, unit = "hbm", PEAK_HBM, "GB/s"
+        achieved = a_bytes / (a_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": args.steps / elapsed,
+        "unit": "iter/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={B} N={N} d={d} K={K} {w.dtype}, "
+                               f"{args.steps} Lloyd iterations, tol=0",
+                   "B": B, "N": N, "d": d, "K": K},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "assign (FlashAssign)"},
+        "phases_ms": {"norms": n_ms, "assign": a_ms, "update": u_ms},
+        "update_roofline": {"bound": "hbm", "achieved": u_bytes / (u_ms * 1e-3) / 1e9,
+                            "peak": PEAK_HBM, "unit": "GB/s",
+                            "frac": u_bytes / (u_ms * 1e-3) / 1e9 / PEAK_HBM},
+    }
+    if args.cpu_batches > 0 and w.N * w.K * w.d <= 2e10:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_batches)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

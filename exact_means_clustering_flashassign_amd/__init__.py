@@ -1,0 +1,25 @@
+"""Exact batched Lloyd's K-Means on MI355X: FlashAssign + sort-inverse update.
+
+All computation runs in the hand-written HIP kernels of ``libfkmeans.so``
+(C ABI in ``include/fkmeans.h``); this package only marshals arguments.
+"""
+from ._binding import (  # noqa: F401
+    FK_BF16,
+    FK_F16,
+    FK_F32,
+    FKError,
+    LIB_PATH,
+    dtype_code,
+    fk_assign,
+    fk_lloyd,
+    fk_norms,
+    fk_status_string,
+    fk_trace_begin,
+    fk_trace_end,
+    fk_update,
+    fk_version,
+    fk_workspace_size,
+    load,
+    torch_dtype,
+    workspace,
+)

@@ -1,0 +1,249 @@
+// C ABI of libfkmeans: argument validation, workspace layout, path dispatch,
+// the Lloyd loop and the optional timing trace. Every numeric step runs in
+// the kernels of norms.hip, assign.hip and update.hip.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "fk_internal.hpp"
+
+namespace {
+
+using fk::UpdateWs;
+
+constexpr int64_t kI32Max = 0x7FFFFFFF;
+constexpr int64_t kElemLimit = (int64_t)1 << 62;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int elem_bytes(int dt) { return dt == FK_F32 ? 4 : 2; }
+
+bool valid_dt(int dt) { return dt == FK_F32 || dt == FK_F16 || dt == FK_BF16; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t c) {
+  if (a == 0 || b == 0 || c == 0) return true;
+  if (a > kElemLimit / b) return false;
+  const int64_t ab = a * b;
+  return ab <= kElemLimit / c;
+}
+
+bool valid_sizes(int64_t B, int64_t N, int64_t d, int64_t K) {
+  if (B < 0 || N < 0 || d < 1 || K < 1) return false;
+  if (N >= kI32Max || K >= kI32Max || d >= kI32Max || B >= kI32Max) return false;
+  return mul_ok(B, N, d) && mul_ok(B, K, d);
+}
+
+fk_status_t hip_status(hipError_t e) { return e == hipSuccess ? FK_OK : FK_ERR_HIP; }
+
+bool force_splitd() {
+  const char* v = getenv("FK_FORCE_SPLITD");
+  return v && v[0] == '1';
+}
+
+hipError_t run_assign(const void* x, const void* c_lp, const float* cn, int dt, int64_t B,
+                      int64_t N, int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
+  if (dt == FK_F32)
+    return fk::launch_assign_f32((const float*)x, (const float*)c_lp, cn, B, N, d, K, ids, s);
+  if (!force_splitd() && fk::smalld_supported(dt, d))
+    return fk::launch_assign_smalld(x, c_lp, cn, dt, B, N, d, K, ids, s);
+  return fk::launch_assign_splitd(x, c_lp, cn, dt, B, N, d, K, ids, s);
+}
+
+// Workspace beyond the update's: rounded centroids, norms, counts, shift.
+struct LloydWs {
+  UpdateWs upd;
+  void* c_lp;
+  float* cnorm;
+  int32_t* counts;
+  float* shift;
+};
+
+size_t lloyd_extra_bytes(int dt, int64_t B, int64_t d, int64_t K) {
+  return align256((size_t)B * K * d * elem_bytes(dt)) + align256((size_t)B * K * 4) * 2 +
+         align256((size_t)B * 4);
+}
+
+LloydWs carve_lloyd(void* base, int dt, int64_t B, int64_t N, int64_t d, int64_t K) {
+  LloydWs w;
+  w.upd = fk::carve_update_ws(base, B, N, d, K);
+  char* p = static_cast<char*>(base) + fk::update_ws_bytes(B, N, d, K);
+  w.c_lp = p;
+  p += align256((size_t)B * K * d * elem_bytes(dt));
+  w.cnorm = reinterpret_cast<float*>(p);
+  p += align256((size_t)B * K * 4);
+  w.counts = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)B * K * 4);
+  w.shift = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// trace
+struct Trace {
+  bool on = false;
+  int32_t capacity = 0;
+  int32_t used = 0;
+  std::vector<hipEvent_t> ev;   // 4 per iteration: norms, assign, update, end
+};
+Trace g_trace;
+
+void trace_release() {
+  for (hipEvent_t e : g_trace.ev) hipEventDestroy(e);
+  g_trace.ev.clear();
+  g_trace.on = false;
+  g_trace.capacity = g_trace.used = 0;
+}
+
+hipEvent_t trace_event(int32_t it, int which) {
+  return g_trace.ev[(size_t)it * 4 + which];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fk_status_string(fk_status_t st) {
+  switch (st) {
+    case FK_OK: return "FK_OK";
+    case FK_ERR_INVALID: return "FK_ERR_INVALID: invalid argument";
+    case FK_ERR_UNSUPPORTED: return "FK_ERR_UNSUPPORTED: shape not supported";
+    case FK_ERR_WORKSPACE: return "FK_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case FK_ERR_HIP: return "FK_ERR_HIP: HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t fk_version(void) { return 100; }
+
+size_t fk_workspace_size(fk_dtype_t dt, int64_t B, int64_t N, int64_t d, int64_t K) {
+  if (!valid_dt(dt) || !valid_sizes(B, N, d, K)) return 0;
+  const size_t n = fk::update_ws_bytes(B, N, d, K) + lloyd_extra_bytes(dt, B, d, K);
+  return n < 256 ? 256 : n;   // never 0 for a valid problem (0 flags bad arguments)
+}
+
+fk_status_t fk_norms(const float* c, void* c_lp, float* cnorm, fk_dtype_t dt, int64_t B,
+                     int64_t K, int64_t d, hipStream_t stream) {
+  if (!valid_dt(dt) || !valid_sizes(B, 0, d, K)) return FK_ERR_INVALID;
+  if (B > 0 && (!c || !c_lp || !cnorm)) return FK_ERR_INVALID;
+  return hip_status(fk::launch_norms(c, c_lp, cnorm, dt, B * K, d, stream));
+}
+
+fk_status_t fk_assign(const void* x, const void* c_lp, const float* cnorm, fk_dtype_t dt,
+                      int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,
+                      hipStream_t stream) {
+  if (!valid_dt(dt) || !valid_sizes(B, N, d, K)) return FK_ERR_INVALID;
+  if (B * N > 0 && (!x || !c_lp || !cnorm || !ids)) return FK_ERR_INVALID;
+  const hipError_t e = run_assign(x, c_lp, cnorm, dt, B, N, d, K, ids, stream);
+  if (e == hipErrorNotSupported || e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+fk_status_t fk_update(const void* x, const int32_t* ids, fk_dtype_t dt, int64_t B, int64_t N,
+                      int64_t d, int64_t K, float* c, int32_t* counts, float* shift, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dt(dt) || !valid_sizes(B, N, d, K)) return FK_ERR_INVALID;
+  if (B > 0 && (!c || !counts || !shift)) return FK_ERR_INVALID;
+  if (B * N > 0 && (!x || !ids)) return FK_ERR_INVALID;
+  if (B == 0) return FK_OK;
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < fk::update_ws_bytes(B, N, d, K))
+    return FK_ERR_WORKSPACE;
+  const UpdateWs w = fk::carve_update_ws(ws, B, N, d, K);
+  const hipError_t e = fk::launch_update(x, ids, dt, B, N, d, K, c, counts, shift, w, stream);
+  if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t d, int64_t K,
+                     const void* init, int32_t max_iter, float tol, int32_t* ids, float* centers,
+                     int32_t* n_iter, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dt(dt) || !valid_sizes(B, N, d, K)) return FK_ERR_INVALID;
+  if (max_iter < 0 || !(tol >= 0.f) || !n_iter) return FK_ERR_INVALID;
+  if (B > 0 && (!init || !centers)) return FK_ERR_INVALID;
+  if (B * N > 0 && (!x || !ids)) return FK_ERR_INVALID;
+  *n_iter = 0;
+  if (B == 0) return FK_OK;
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < fk_workspace_size(dt, B, N, d, K))
+    return FK_ERR_WORKSPACE;
+  const LloydWs w = carve_lloyd(ws, dt, B, N, d, K);
+  hipError_t e = fk::launch_widen(init, centers, dt, B * K * d, stream);
+  if (e != hipSuccess) return FK_ERR_HIP;
+  if (max_iter == 0) return hip_status(fk::launch_fill_i32(ids, 0, B * N, stream));
+
+  std::vector<float> host_shift(tol > 0.f ? (size_t)B : 0);
+  int32_t done = 0;
+  for (int32_t t = 0; t < max_iter; ++t) {
+    const bool tr = g_trace.on && g_trace.used < g_trace.capacity;
+    const int32_t slot = g_trace.used;
+    if (tr && hipEventRecord(trace_event(slot, 0), stream) != hipSuccess) return FK_ERR_HIP;
+    e = fk::launch_norms(centers, w.c_lp, w.cnorm, dt, B * K, d, stream);
+    if (e != hipSuccess) return FK_ERR_HIP;
+    if (tr && hipEventRecord(trace_event(slot, 1), stream) != hipSuccess) return FK_ERR_HIP;
+    e = run_assign(x, w.c_lp, w.cnorm, dt, B, N, d, K, ids, stream);
+    if (e == hipErrorNotSupported || e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
+    if (e != hipSuccess) return FK_ERR_HIP;
+    if (tr && hipEventRecord(trace_event(slot, 2), stream) != hipSuccess) return FK_ERR_HIP;
+    e = fk::launch_update(x, ids, dt, B, N, d, K, centers, w.counts, w.shift, w.upd, stream);
+    if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
+    if (e != hipSuccess) return FK_ERR_HIP;
+    if (tr) {
+      if (hipEventRecord(trace_event(slot, 3), stream) != hipSuccess) return FK_ERR_HIP;
+      ++g_trace.used;
+    }
+    done = t + 1;
+    if (tol > 0.f) {
+      if (hipMemcpyAsync(host_shift.data(), w.shift, (size_t)B * sizeof(float),
+                         hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return FK_ERR_HIP;
+      if (hipStreamSynchronize(stream) != hipSuccess) return FK_ERR_HIP;
+      float mx = host_shift[0];
+      for (int64_t b = 1; b < B; ++b) mx = host_shift[b] > mx ? host_shift[b] : mx;
+      if (mx < tol) break;
+    }
+  }
+  *n_iter = done;
+  return FK_OK;
+}
+
+fk_status_t fk_trace_begin(int32_t capacity) {
+  if (capacity < 1) return FK_ERR_INVALID;
+  trace_release();
+  g_trace.ev.resize((size_t)capacity * 4);
+  for (auto& e : g_trace.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      trace_release();
+      return FK_ERR_HIP;
+    }
+  }
+  g_trace.capacity = capacity;
+  g_trace.used = 0;
+  g_trace.on = true;
+  return FK_OK;
+}
+
+fk_status_t fk_trace_end(fk_trace_t* out) {
+  if (!out) return FK_ERR_INVALID;
+  memset(out, 0, sizeof(*out));
+  if (!g_trace.on) return FK_ERR_INVALID;
+  fk_status_t st = FK_OK;
+  for (int32_t i = 0; i < g_trace.used && st == FK_OK; ++i) {
+    float a = 0.f, b = 0.f, c = 0.f;
+    if (hipEventSynchronize(trace_event(i, 3)) != hipSuccess ||
+        hipEventElapsedTime(&a, trace_event(i, 0), trace_event(i, 1)) != hipSuccess ||
+        hipEventElapsedTime(&b, trace_event(i, 1), trace_event(i, 2)) != hipSuccess ||
+        hipEventElapsedTime(&c, trace_event(i, 2), trace_event(i, 3)) != hipSuccess) {
+      st = FK_ERR_HIP;
+      break;
+    }
+    out->norms_ms += a;
+    out->assign_ms += b;
+    out->update_ms += c;
+    out->iterations += 1;
+  }
+  trace_release();
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,466 @@
+// FlashAssign for gfx950: fused point-centroid distance + online argmin.
+//
+// What is computed (per problem b and point n):
+//   ids[b,n] = argmin_k  ||c_k||^2 - 2 x_n . c_k      (lowest k on ties)
+// maximised here in the equivalent, exactly scaled form
+//   score_k = x_n . c_k - ||c_k||^2 / 2.
+// The B x N x K distance matrix is never written: point tiles and centroid
+// tiles stream through on-chip memory and each point keeps a running
+// (best score, best index) in registers ("flash-kmeans and the return of
+// exact K-Means on the GPU", section "The point of the kernel is that the
+// distance matrix never exists"; itinai.com summary, second paragraph;
+// "Flash-KMeans: Implementação Exata de K-Means…", section "FlashAssign").
+//
+// Small-D path (d <= 512): a block owns 4 waves x NF x 32 points whose
+// fragments are loaded once into VGPRs; centroid tiles of TK rows are
+// double-buffered through LDS. v_mfma_f32_32x32x16_{f16,bf16}: A = 32
+// centroid rows from LDS, B = 32 points from registers, C-input = -||c||^2/2
+// of those rows, so the accumulator is the score itself. Each lane holds 16
+// centroid scores for one point; the running max stays in-lane across all
+// tiles and one lane swap at the end merges the two lanes that share a point.
+//
+// Split-D path (d > 512): the same tiles with the d loop innermost: a block
+// keeps a (256 points x 128 centroids) score block in registers across the d
+// loop (outer K loop, inner D loop), staging each centroid d-chunk in LDS and
+// reading point d-chunks straight into registers.
+//
+// fp32 inputs use a VALU kernel (exact fp32 products, fp32 fma chain).
+#include <math.h>
+
+#include "fk_internal.hpp"
+
+namespace fk {
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kWaves = 4;
+
+// ---- 16-byte loads of 8 stored elements, zero outside [0,limit) -----------
+template <bool VEC>
+__device__ __forceinline__ uint4 load8(const uint16_t* row, int col, int limit) {
+  if (VEC) {
+    if (col < limit) return *reinterpret_cast<const uint4*>(row + col);
+    return make_uint4(0, 0, 0, 0);
+  } else {
+    uint16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = (col + i < limit) ? row[col + i] : (uint16_t)0;
+    uint4 v;
+    v.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+    v.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+    v.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
+    v.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
+    return v;
+  }
+}
+
+// Running argmax over one 32x32 accumulator: lane holds rows
+// 8*(r/4) + 4*half + r%4 of the tile; the 4*half term is added at the merge.
+__device__ __forceinline__ void argmax_update(const floatx16_t& acc, int base, float& best,
+                                              int& bidx) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float v = acc[r];
+    const bool gt = v > best;
+    best = gt ? v : best;
+    bidx = gt ? base + 8 * (r >> 2) + (r & 3) : bidx;
+  }
+}
+
+// Merge the two lanes (half 0 and half 1) that hold the same point.
+__device__ __forceinline__ int merge_halves(float best, int bidx, int half) {
+  int idx = bidx + 4 * half;
+  const float ob = __shfl_xor(best, 32, 64);
+  const int oi = __shfl_xor(idx, 32, 64);
+  if (ob > best || (ob == best && oi < idx)) idx = oi;
+  return idx;
+}
+
+// ===========================================================================
+// small-D
+// ===========================================================================
+template <int DT, int KS, int NF, int TK, bool VEC>
+__global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ c,
+    const float* __restrict__ cnorm, int32_t* __restrict__ ids, int N, int d, int K,
+    int blocks_per_batch, int grid) {
+  constexpr int DP = KS * 16;            // padded dimension
+  constexpr int PITCH = DP + 8;          // LDS row pitch (elements): +16 B against bank conflicts
+  constexpr int NSUB = TK / 32;          // MFMA row blocks per tile
+  constexpr int BN = kWaves * NF * 32;   // points per block
+  constexpr int VPR = DP / 8;            // 16-byte vectors per centroid row
+  constexpr int NV = (TK * VPR + kThreads - 1) / kThreads;   // vectors per thread per tile
+  __shared__ __align__(16) uint16_t lds_c[2][TK * PITCH];
+  __shared__ __align__(16) float lds_h[2][TK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int64_t logical = xcd_remap(blockIdx.x, grid);
+  const int b = (int)(logical / blocks_per_batch);
+  const int nblk = (int)(logical % blocks_per_batch) * BN + wave * NF * 32;
+  const uint16_t* xb = x + (int64_t)b * N * d;
+  const uint16_t* cb = c + (int64_t)b * K * d;
+  const float* cnb = cnorm + (int64_t)b * K;
+
+  // point fragments, resident for the whole kernel
+  uint4 xf[NF][KS];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int n = nblk + f * 32 + r32;
+    const uint16_t* row = xb + (int64_t)(n < N ? n : 0) * d;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      xf[f][s] = (n < N) ? load8<VEC>(row, s * 16 + half * 8, d) : make_uint4(0, 0, 0, 0);
+  }
+
+  const int ntiles = (K + TK - 1) / TK;
+  uint4 pre[NV];
+  float pre_h = 0.f;
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int v = tid + kThreads * q;
+      const int row = v / VPR, col = (v % VPR) * 8;
+      const int k = t * TK + row;
+      pre[q] = (v < TK * VPR && k < K) ? load8<VEC>(cb + (int64_t)k * d, col, d)
+                                       : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < TK) {
+      const int k = t * TK + tid;
+      pre_h = k < K ? -0.5f * cnb[k] : -INFINITY;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int v = tid + kThreads * q;
+      if (v < TK * VPR) {
+        const int row = v / VPR, col = (v % VPR) * 8;
+        *reinterpret_cast<uint4*>(&lds_c[buf][row * PITCH + col]) = pre[q];
+      }
+    }
+    if (tid < TK) lds_h[buf][tid] = pre_h;
+  };
+
+  float best[NF];
+  int bidx[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    best[f] = -INFINITY;
+    bidx[f] = 0;
+  }
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) fetch(t + 1);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      floatx16_t cinit;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 hv = *reinterpret_cast<const float4*>(&lds_h[buf][sub * 32 + 8 * i + 4 * half]);
+        cinit[4 * i + 0] = hv.x;
+        cinit[4 * i + 1] = hv.y;
+        cinit[4 * i + 2] = hv.z;
+        cinit[4 * i + 3] = hv.w;
+      }
+      floatx16_t acc[NF];
+      const uint16_t* arow = &lds_c[buf][(sub * 32 + r32) * PITCH + half * 8];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint4 a = *reinterpret_cast<const uint4*>(arow + s * 16);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[f] = Mfma<DT>::run(a, xf[f][s], s == 0 ? cinit : acc[f]);
+      }
+      const int base = t * TK + sub * 32;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) argmax_update(acc[f], base, best[f], bidx[f]);
+    }
+    if (t + 1 < ntiles) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  int32_t* ib = ids + (int64_t)b * N;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int idx = merge_halves(best[f], bidx[f], half);
+    const int n = nblk + f * 32 + r32;
+    if (half == 0 && n < N) ib[n] = idx;
+  }
+}
+
+// ===========================================================================
+// split-D
+// ===========================================================================
+constexpr int kSplitDC = 64;     // d-chunk (4 MFMA k-steps)
+constexpr int kSplitTK = 128;    // centroids per outer tile (4 row blocks)
+constexpr int kSplitNF = 2;      // point fragments per wave
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void assign_splitd_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ c,
+    const float* __restrict__ cnorm, int32_t* __restrict__ ids, int N, int d, int K,
+    int blocks_per_batch, int grid) {
+  constexpr int KSC = kSplitDC / 16;
+  constexpr int PITCH = kSplitDC + 8;
+  constexpr int NSUB = kSplitTK / 32;
+  constexpr int NF = kSplitNF;
+  constexpr int BN = kWaves * NF * 32;
+  constexpr int VPR = kSplitDC / 8;
+  constexpr int NV = kSplitTK * VPR / kThreads;
+  static_assert(kSplitTK * VPR % kThreads == 0, "tile split");
+  __shared__ __align__(16) uint16_t lds_c[2][kSplitTK * PITCH];
+  __shared__ __align__(16) float lds_h[kSplitTK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, r32 = lane & 31;
+  const int64_t logical = xcd_remap(blockIdx.x, grid);
+  const int b = (int)(logical / blocks_per_batch);
+  const int nblk = (int)(logical % blocks_per_batch) * BN + wave * NF * 32;
+  const uint16_t* xb = x + (int64_t)b * N * d;
+  const uint16_t* cb = c + (int64_t)b * K * d;
+  const float* cnb = cnorm + (int64_t)b * K;
+
+  const uint16_t* xrow[NF];
+  bool xval[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int n = nblk + f * 32 + r32;
+    xval[f] = n < N;
+    xrow[f] = xb + (int64_t)(n < N ? n : 0) * d;
+  }
+
+  const int nchunks = (d + kSplitDC - 1) / kSplitDC;
+  const int ktiles = (K + kSplitTK - 1) / kSplitTK;
+  float best[NF];
+  int bidx[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    best[f] = -INFINITY;
+    bidx[f] = 0;
+  }
+
+  uint4 pre[NV];
+  auto fetch = [&](int kt, int ch) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int v = tid + kThreads * q;
+      const int row = v / VPR, col = ch * kSplitDC + (v % VPR) * 8;
+      const int k = kt * kSplitTK + row;
+      pre[q] = (k < K) ? load8<VEC>(cb + (int64_t)k * d, col, d) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int v = tid + kThreads * q;
+      const int row = v / VPR, col = (v % VPR) * 8;
+      *reinterpret_cast<uint4*>(&lds_c[buf][row * PITCH + col]) = pre[q];
+    }
+  };
+
+  for (int kt = 0; kt < ktiles; ++kt) {
+    if (tid < kSplitTK) {
+      const int k = kt * kSplitTK + tid;
+      lds_h[tid] = k < K ? -0.5f * cnb[k] : -INFINITY;
+    }
+    fetch(kt, 0);
+    stash(0);
+    __syncthreads();
+    floatx16_t acc[NSUB][NF];
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      floatx16_t cinit;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 hv = *reinterpret_cast<const float4*>(&lds_h[sub * 32 + 8 * i + 4 * half]);
+        cinit[4 * i + 0] = hv.x;
+        cinit[4 * i + 1] = hv.y;
+        cinit[4 * i + 2] = hv.z;
+        cinit[4 * i + 3] = hv.w;
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[sub][f] = cinit;
+    }
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int buf = ch & 1;
+      uint4 xf[NF][KSC];
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int s = 0; s < KSC; ++s)
+          xf[f][s] = xval[f] ? load8<VEC>(xrow[f], ch * kSplitDC + s * 16 + half * 8, d)
+                             : make_uint4(0, 0, 0, 0);
+      if (ch + 1 < nchunks) fetch(kt, ch + 1);
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        const uint16_t* arow = &lds_c[buf][(sub * 32 + r32) * PITCH + half * 8];
+#pragma unroll
+        for (int s = 0; s < KSC; ++s) {
+          const uint4 a = *reinterpret_cast<const uint4*>(arow + s * 16);
+#pragma unroll
+          for (int f = 0; f < NF; ++f) acc[sub][f] = Mfma<DT>::run(a, xf[f][s], acc[sub][f]);
+        }
+      }
+      if (ch + 1 < nchunks) stash(buf ^ 1);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        argmax_update(acc[sub][f], kt * kSplitTK + sub * 32, best[f], bidx[f]);
+  }
+
+  int32_t* ib = ids + (int64_t)b * N;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int idx = merge_halves(best[f], bidx[f], half);
+    const int n = nblk + f * 32 + r32;
+    if (half == 0 && n < N) ib[n] = idx;
+  }
+}
+
+// ===========================================================================
+// fp32 (VALU)
+// ===========================================================================
+constexpr int kF32TK = 32;   // centroids per tile
+constexpr int kF32DC = 32;   // dims per chunk
+
+__global__ __launch_bounds__(kThreads) void assign_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ c, const float* __restrict__ cnorm,
+    int32_t* __restrict__ ids, int N, int d, int K, int blocks_per_batch, int grid) {
+  __shared__ float lds_c[kF32TK][kF32DC + 1];
+  __shared__ float lds_h[kF32TK];
+  const int tid = threadIdx.x;
+  const int64_t logical = xcd_remap(blockIdx.x, grid);
+  const int b = (int)(logical / blocks_per_batch);
+  const int n = (int)(logical % blocks_per_batch) * kThreads + tid;
+  const bool valid = n < N;
+  const float* xr = x + ((int64_t)b * N + (valid ? n : 0)) * d;
+  const float* cb = c + (int64_t)b * K * d;
+  const float* cnb = cnorm + (int64_t)b * K;
+
+  float best = -INFINITY;
+  int bidx = 0;
+  for (int k0 = 0; k0 < K; k0 += kF32TK) {
+    __syncthreads();
+    if (tid < kF32TK) lds_h[tid] = (k0 + tid < K) ? -0.5f * cnb[k0 + tid] : -INFINITY;
+    float acc[kF32TK];
+#pragma unroll
+    for (int k = 0; k < kF32TK; ++k) acc[k] = 0.f;
+    for (int j0 = 0; j0 < d; j0 += kF32DC) {
+      __syncthreads();
+      for (int e = tid; e < kF32TK * kF32DC; e += kThreads) {
+        const int k = e / kF32DC, j = e % kF32DC;
+        lds_c[k][j] = (k0 + k < K && j0 + j < d) ? cb[(int64_t)(k0 + k) * d + j0 + j] : 0.f;
+      }
+      __syncthreads();
+      const int jn = (d - j0) < kF32DC ? (d - j0) : kF32DC;
+      for (int j = 0; j < jn; ++j) {
+        const float xv = valid ? xr[j0 + j] : 0.f;
+#pragma unroll
+        for (int k = 0; k < kF32TK; ++k) acc[k] = fmaf(xv, lds_c[k][j], acc[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kF32TK; ++k) {
+      const float v = acc[k] + lds_h[k];
+      if (v > best) {
+        best = v;
+        bidx = k0 + k;
+      }
+    }
+  }
+  if (valid) ids[(int64_t)b * N + n] = bidx;
+}
+
+// ===========================================================================
+// dispatch
+// ===========================================================================
+// 16-byte vector loads need rows of whole 8-element vectors and aligned bases.
+bool vec_ok(const void* x, const void* c, int64_t d) {
+  return d % 8 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)c % 16) == 0;
+}
+
+template <int DT, int KS, int NF, int TK>
+hipError_t run_smalld(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
+                      int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
+  constexpr int BN = kWaves * NF * 32;
+  const int bpb = (int)((N + BN - 1) / BN);
+  const int64_t grid = B * bpb;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (vec_ok(x, c, d))
+    assign_smalld_kernel<DT, KS, NF, TK, true><<<(unsigned)grid, kThreads, 0, s>>>(
+        (const uint16_t*)x, (const uint16_t*)c, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
+  else
+    assign_smalld_kernel<DT, KS, NF, TK, false><<<(unsigned)grid, kThreads, 0, s>>>(
+        (const uint16_t*)x, (const uint16_t*)c, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t smalld_dt(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
+                     int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
+  if (d <= 32) return run_smalld<DT, 2, 2, 64>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 64) return run_smalld<DT, 4, 2, 64>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 128) return run_smalld<DT, 8, 2, 64>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 256) return run_smalld<DT, 16, 2, 64>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 512) return run_smalld<DT, 32, 1, 32>(x, c, cn, B, N, d, K, ids, s);
+  return hipErrorNotSupported;
+}
+
+template <int DT>
+hipError_t splitd_dt(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
+                     int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
+  constexpr int BN = kWaves * kSplitNF * 32;
+  const int bpb = (int)((N + BN - 1) / BN);
+  const int64_t grid = B * bpb;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (vec_ok(x, c, d))
+    assign_splitd_kernel<DT, true><<<(unsigned)grid, kThreads, 0, s>>>(
+        (const uint16_t*)x, (const uint16_t*)c, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
+  else
+    assign_splitd_kernel<DT, false><<<(unsigned)grid, kThreads, 0, s>>>(
+        (const uint16_t*)x, (const uint16_t*)c, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The small-D tiles fit LDS for every d <= 512 (largest: 2 x 32 x 520 x 2 B).
+bool smalld_supported(int dt, int64_t d) { return (dt == FK_F16 || dt == FK_BF16) && d <= 512; }
+
+hipError_t launch_assign_smalld(const void* x, const void* c_lp, const float* cnorm, int dt,
+                                int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,
+                                hipStream_t s) {
+  if (B == 0 || N == 0) return hipSuccess;
+  if (dt == FK_F16) return smalld_dt<FK_F16>(x, c_lp, cnorm, B, N, d, K, ids, s);
+  if (dt == FK_BF16) return smalld_dt<FK_BF16>(x, c_lp, cnorm, B, N, d, K, ids, s);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_assign_splitd(const void* x, const void* c_lp, const float* cnorm, int dt,
+                                int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,
+                                hipStream_t s) {
+  if (B == 0 || N == 0) return hipSuccess;
+  if (dt == FK_F16) return splitd_dt<FK_F16>(x, c_lp, cnorm, B, N, d, K, ids, s);
+  if (dt == FK_BF16) return splitd_dt<FK_BF16>(x, c_lp, cnorm, B, N, d, K, ids, s);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_assign_f32(const float* x, const float* c, const float* cnorm, int64_t B,
+                             int64_t N, int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
+  if (B == 0 || N == 0) return hipSuccess;
+  const int bpb = (int)((N + kThreads - 1) / kThreads);
+  const int64_t grid = B * bpb;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  assign_f32_kernel<<<(unsigned)grid, kThreads, 0, s>>>(x, c, cnorm, ids, (int)N, (int)d,
+                                                         (int)K, bpb, (int)grid);
+  return hipGetLastError();
+}
+
+}  // namespace fk

@@ -1,0 +1,120 @@
+// Internal declarations shared by the libfkmeans translation units.
+// Device helpers (element types, rounding, wave reductions) and the host-side
+// launchers each kernel file exports to the API layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fkmeans.h"
+
+namespace fk {
+
+// ---------------------------------------------------------------------------
+// element types
+// ---------------------------------------------------------------------------
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+// Widening of one stored 16-bit element (raw bits) to fp32 -- exact.
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, h);
+  return (float)v;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// Rounding fp32 -> 16-bit storage, nearest-even. fp16 uses the hardware
+// convert (default round-to-nearest-even mode); bf16 adds half an ulp minus
+// one plus the kept lsb, so exact halves go to the even neighbour.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 v = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<FK_F16> {
+  static constexpr int bytes = 2;
+  __device__ static __forceinline__ float widen(uint16_t h) { return f16_bits_to_f32(h); }
+  __device__ static __forceinline__ uint16_t narrow(float f) { return f32_to_f16_bits(f); }
+};
+template <> struct Elem<FK_BF16> {
+  static constexpr int bytes = 2;
+  __device__ static __forceinline__ float widen(uint16_t h) { return bf16_bits_to_f32(h); }
+  __device__ static __forceinline__ uint16_t narrow(float f) { return f32_to_bf16_bits(f); }
+};
+
+// 32x32x16 MFMA with fp32 accumulate; A rows = centroids, B cols = points.
+template <int DT> struct Mfma;
+template <> struct Mfma<FK_F16> {
+  __device__ static __forceinline__ floatx16_t run(uint4 a, uint4 b, floatx16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                 __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<FK_BF16> {
+  __device__ static __forceinline__ floatx16_t run(uint4 a, uint4 b, floatx16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// wave helpers (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Block id -> logical tile so that each XCD (blocks are dealt round-robin to
+// the 8 XCDs) works on a contiguous range of tiles and keeps them in its L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t grid) {
+  const int64_t q = grid / 8, r = grid % 8;
+  const int64_t xcd = bid % 8, slot = bid / 8;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// ---------------------------------------------------------------------------
+// launchers (host); each returns hipSuccess or the launch error
+// ---------------------------------------------------------------------------
+hipError_t launch_norms(const float* c, void* c_lp, float* cnorm, int dt, int64_t rows,
+                        int64_t d, hipStream_t s);
+hipError_t launch_widen(const void* src, float* dst, int dt, int64_t count, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t count, hipStream_t s);
+
+// Assignment paths. Each returns hipErrorNotSupported when it cannot run the shape.
+bool smalld_supported(int dt, int64_t d);
+hipError_t launch_assign_smalld(const void* x, const void* c_lp, const float* cnorm, int dt,
+                                int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,
+                                hipStream_t s);
+hipError_t launch_assign_splitd(const void* x, const void* c_lp, const float* cnorm, int dt,
+                                int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,
+                                hipStream_t s);
+hipError_t launch_assign_f32(const float* x, const float* c, const float* cnorm, int64_t B,
+                             int64_t N, int64_t d, int64_t K, int32_t* ids, hipStream_t s);
+
+// Sort-inverse update; workspace carved by the API layer.
+struct UpdateWs {
+  float* sums;        // (B,K,d) fp32
+  int32_t* offsets;   // (B,K+1) segment starts
+  int32_t* cursor;    // (B,K) scatter cursors
+  int32_t* perm;      // (B,N) point index per sorted position
+};
+size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K);
+UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K);
+hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, int64_t N,
+                         int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
+                         const UpdateWs& ws, hipStream_t s,
+                         hipEvent_t ev_after_hist = nullptr);
+
+}  // namespace fk

@@ -112,34 +112,29 @@ SEEDS = {"tiny_f32": 1001, "api_example": 1002, "io_breakdown": 1003,
          "large_k_zipf": 1004, "split_d": 1005}
 
 
-def _fill_noise(rng, out32: np.ndarray, chunk_rows: int = 1 << 16) -> None:
-    """out32[...] = standard normal, row chunk by row chunk (flattened rows)."""
-    rows = out32.reshape(-1, out32.shape[-1])
-    for r0 in range(0, rows.shape[0], chunk_rows):
-        r1 = min(rows.shape[0], r0 + chunk_rows)
-        rows[r0:r1] = rng.standard_normal((r1 - r0, rows.shape[1]), dtype=np.float32)
-
-
-def _store_chunked(x32_fn, shape, dtype, chunk_rows=1 << 16):
-    """Build a (B,N,d) array in storage dtype from fp32 row chunks."""
-    B, N, d = shape
-    sdt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
-    out = np.empty(shape, dtype=sdt)
-    for b in range(B):
-        for n0 in range(0, N, chunk_rows):
-            n1 = min(N, n0 + chunk_rows)
-            out[b, n0:n1] = to_storage(x32_fn(b, n0, n1), dtype)
-    return out
+def _workers() -> int:
+    try:
+        import os
+        n = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        n = 4
+    return max(1, min(16, n))
 
 
 def make_mixture(B, N, d, K, dtype, *, n_comp, mean_std, weights=None,
                  seed, subspace_rank=None, iid=False, chunk_rows=1 << 16):
     """Gaussian-mixture points plus per-batch random-point initial centroids.
 
-    Draw order from one PCG64 stream: component means (all batches), labels,
-    then noise row chunk by row chunk, then the init indices.
+    One PCG64 stream seeded with ``seed`` draws, in order: the component means
+    (all batches), the labels, then the init indices. The unit-variance noise
+    of row chunk j (chunks of ``chunk_rows`` rows, batch-major) comes from its
+    own stream, child j of ``SeedSequence(seed)``, so chunks can be drawn in
+    parallel and the result does not depend on the thread count.
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
+    import concurrent.futures as cf
+
+    ss = np.random.SeedSequence(seed)
+    rng = np.random.Generator(np.random.PCG64(ss))
     labels = None
     if iid:
         means = None
@@ -161,18 +156,28 @@ def make_mixture(B, N, d, K, dtype, *, n_comp, mean_std, weights=None,
             p = p / p.sum()
             labels = rng.choice(n_comp, size=(B, N), p=p)
         labels = labels.astype(np.int32)
+    init_idx = [rng.choice(N, size=K, replace=False) if K <= N else None for _ in range(B)]
 
-    def rows(b, n0, n1):
-        z = rng.standard_normal((n1 - n0, d), dtype=np.float32)
+    sdt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+    x = np.empty((B, N, d), dtype=sdt)
+    per_b = (N + chunk_rows - 1) // chunk_rows
+    children = ss.spawn(B * per_b)
+
+    def fill(j):
+        b, c = divmod(j, per_b)
+        n0 = c * chunk_rows
+        n1 = min(N, n0 + chunk_rows)
+        g = np.random.Generator(np.random.PCG64(children[j]))
+        z = g.standard_normal((n1 - n0, d), dtype=np.float32)
         if means is not None:
             z += means[b][labels[b, n0:n1]]
-        return z
+        x[b, n0:n1] = to_storage(z, dtype)
 
-    x = _store_chunked(rows, (B, N, d), dtype, chunk_rows)
-    init = np.empty((B, K, d), dtype=x.dtype)
-    for b in range(B):
-        idx = rng.choice(N, size=K, replace=False)
-        init[b] = x[b, idx]
+    with cf.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(fill, range(B * per_b)))
+    if any(i is None for i in init_idx):
+        raise ValueError("K > N: initial centroids are drawn without replacement")
+    init = np.stack([x[b, init_idx[b]] for b in range(B)])
     return x, init, labels
 
 

@@ -1,0 +1,100 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/fkmeans.h, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fkmeans.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fk_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_means_clustering_flashassign_amd import _binding
+
+    if not os.path.exists(_binding.LIB_PATH):
+        pytest.fail("libfkmeans.so is not built (run __graft_entry__.build())")
+    return _binding.load()
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for want in ("fk_norms", "fk_assign", "fk_update", "fk_lloyd", "fk_workspace_size",
+                 "fk_status_string", "fk_version", "fk_trace_begin", "fk_trace_end"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_python_binding_names_match_the_abi():
+    import exact_means_clustering_flashassign_amd as fk
+
+    for name in header_functions():
+        assert callable(getattr(fk, name, None)), name
+
+
+def test_status_strings(lib):
+    for code, tag in [(0, "FK_OK"), (1, "FK_ERR_INVALID"), (2, "FK_ERR_UNSUPPORTED"),
+                      (3, "FK_ERR_WORKSPACE"), (4, "FK_ERR_HIP")]:
+        assert lib.fk_status_string(code).decode().startswith(tag)
+    assert lib.fk_status_string(99).decode() == "unknown status"
+    assert lib.fk_version() >= 100
+
+
+def test_workspace_size(lib):
+    ws = lib.fk_workspace_size
+    big = ws(1, 32, 75600, 128, 1000)
+    # sums, offsets, cursor, perm, rounded centroids, norms, counts, shift
+    need = 32 * 1000 * 128 * 4 + 32 * 1001 * 4 + 32 * 1000 * 4 + 32 * 75600 * 4 + \
+        32 * 1000 * 128 * 2 + 32 * 1000 * 4 * 2 + 32 * 4
+    assert need <= big <= need + 8 * 256
+    assert ws(1, 32, 75600, 128, 1000) < ws(0, 32, 75600, 128, 1000)   # fp32 copy is larger
+    for bad in [(7, 1, 10, 4, 2), (1, -1, 10, 4, 2), (1, 1, -1, 4, 2), (1, 1, 10, 0, 2),
+                (1, 1, 10, 4, 0), (1, 1, 1 << 31, 4, 2), (1, 1, 10, 4, 1 << 31)]:
+        assert ws(*bad) == 0, bad
+    assert ws(1, 0, 10, 4, 2) > 0 and ws(1, 3, 0, 4, 2) > 0       # empty problems are valid
+
+
+def test_validation_rejects_before_launch(lib):
+    null = None
+    INVALID, WORKSPACE = 1, 3
+    # bad element type / sizes
+    assert lib.fk_norms(null, null, null, 5, 1, 4, 8, null) == INVALID
+    assert lib.fk_norms(null, null, null, 1, 1, 4, 0, null) == INVALID
+    assert lib.fk_norms(null, null, null, 1, 1, 4, 8, null) == INVALID     # null buffers
+    assert lib.fk_assign(null, null, null, 1, 1, 16, 8, 0, null, null) == INVALID
+    assert lib.fk_assign(null, null, null, 1, 1, 16, 8, 4, null, null) == INVALID
+    # update: missing workspace is reported as such once the buffers are given
+    dummy = ctypes.c_void_p(256)
+    assert lib.fk_update(dummy, dummy, 1, 1, 16, 8, 4, dummy, dummy, dummy, null, 0, null) == WORKSPACE
+    assert lib.fk_update(dummy, dummy, 1, 1, 16, 8, 4, dummy, dummy, dummy,
+                         ctypes.c_void_p(257), 1 << 20, null) == WORKSPACE      # misaligned
+    assert lib.fk_update(dummy, dummy, 1, 1, 16, 8, 4, dummy, dummy, dummy, dummy, 16, null) == WORKSPACE
+    # lloyd: bad max_iter / tol / n_iter pointer
+    n_iter = ctypes.c_int32(-7)
+    args = dict(x=dummy, dt=1, B=1, N=16, d=8, K=4, init=dummy)
+    call = lambda mi, tol, ni: lib.fk_lloyd(args["x"], 1, 1, 16, 8, 4, dummy, mi, tol, dummy,
+                                            dummy, ni, null, 0, null)
+    assert call(-1, 0.0, ctypes.byref(n_iter)) == INVALID
+    assert call(3, -1.0, ctypes.byref(n_iter)) == INVALID
+    assert call(3, float("nan"), ctypes.byref(n_iter)) == INVALID
+    assert call(3, 0.0, None) == INVALID
+    assert call(3, 0.0, ctypes.byref(n_iter)) == WORKSPACE and n_iter.value == 0
+    # empty batch: nothing to do, n_iter = 0
+    n_iter.value = 5
+    assert lib.fk_lloyd(null, 1, 0, 16, 8, 4, null, 3, 0.0, null, null, ctypes.byref(n_iter),
+                        null, 0, null) == 0 and n_iter.value == 0
+    # trace
+    assert lib.fk_trace_begin(0) == INVALID
+    assert lib.fk_trace_end(None) == INVALID
