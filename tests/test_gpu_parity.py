@@ -117,7 +117,7 @@ def test_assign_parity(fk, monkeypatch, dtype, B, N, d, K, force):
     else:
         monkeypatch.delenv("FK_FORCE_SPLITD", raising=False)
     seed = stable_seed(dtype, B, N, d, K)
-    x, _ = synthdata.make_mixture(B, N, d, 1, dtype, n_comp=max(2, K // 3), mean_std=1.5,
+    x, _, _ = synthdata.make_mixture(B, N, d, 1, dtype, n_comp=max(2, K // 3), mean_std=1.5,
                                   seed=seed)
     x64 = synthdata.to_f64(x, dtype)
     c_hat = make_centroids(x64, K, dtype, seed + 1)
@@ -159,7 +159,7 @@ def _ids(kind, B, N, K, seed):
 def test_update_parity(fk, dtype, B, N, d, K, kind):
     torch = _torch()
     seed = stable_seed(dtype, B, N, d, K, kind)
-    x, _ = synthdata.make_mixture(B, N, d, 1, dtype, n_comp=8, mean_std=1.0, seed=seed)
+    x, _, _ = synthdata.make_mixture(B, N, d, 1, dtype, n_comp=8, mean_std=1.0, seed=seed)
     x64 = synthdata.to_f64(x, dtype)
     ids = _ids(kind, B, N, K, seed + 1)
     c_old = np.random.default_rng(seed + 2).standard_normal((B, K, d)).astype(np.float32)
