@@ -79,7 +79,24 @@ __device__ __forceinline__ int merge_halves(float best, int bidx, int half) {
 // ===========================================================================
 // small-D
 // ===========================================================================
-template <int DT, int KS, int NF, int TK, bool VEC>
+// One argmax step on element e of an accumulator set: e / 16 selects the
+// point fragment, e % 16 the row slot. Strict '>' over increasing rows keeps
+// the lowest index among equal scores. The index is kept relative to the
+// subtile being drained (`rel`, rebased by -32 per subtile), so the candidate
+// is an inline constant and the select needs no extra register move.
+template <int NF>
+__device__ __forceinline__ void argmax_elem(const floatx16_t (&acc)[NF], int e,
+                                            float (&best)[NF], int (&rel)[NF]) {
+  const int f = e >> 4, r = e & 15;
+  const float v = acc[f][r];
+  const bool gt = v > best[f];
+  best[f] = gt ? v : best[f];
+  rel[f] = gt ? 8 * (r >> 2) + (r & 3) : rel[f];
+}
+
+// FULL: d == 16*KS, so every column of a row is real and loads need no
+// column guard; otherwise columns >= d read as zero.
+template <int DT, int KS, int NF, int TK, bool VEC, bool FULL>
 __global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ c,
     const float* __restrict__ cnorm, int32_t* __restrict__ ids, int N, int d, int K,
@@ -90,8 +107,12 @@ __global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
   constexpr int BN = kWaves * NF * 32;   // points per block
   constexpr int VPR = DP / 8;            // 16-byte vectors per centroid row
   constexpr int NV = (TK * VPR + kThreads - 1) / kThreads;   // vectors per thread per tile
+  constexpr int NE = 16 * NF;            // accumulator elements per lane per subtile
+  constexpr int EPS = (NE + KS - 1) / KS;   // epilogue elements per k-step
+  static_assert(NSUB % 2 == 0, "accumulator sets alternate by subtile");
+  static_assert(TK <= kThreads, "one norm per thread");
   __shared__ __align__(16) uint16_t lds_c[2][TK * PITCH];
-  __shared__ __align__(16) float lds_h[2][TK];
+  __shared__ __align__(16) float lds_h[2][kThreads];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, r32 = lane & 31;
@@ -102,93 +123,128 @@ __global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
   const uint16_t* cb = c + (int64_t)b * K * d;
   const float* cnb = cnorm + (int64_t)b * K;
 
-  // point fragments, resident for the whole kernel
+  // point fragments, resident for the whole kernel; rows past N repeat row
+  // N-1 (their results are never stored)
   uint4 xf[NF][KS];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int n = nblk + f * 32 + r32;
-    const uint16_t* row = xb + (int64_t)(n < N ? n : 0) * d;
+    const int n = min(nblk + f * 32 + r32, N - 1);
+    const uint16_t* row = xb + (int64_t)n * d;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      xf[f][s] = (n < N) ? load8<VEC>(row, s * 16 + half * 8, d) : make_uint4(0, 0, 0, 0);
+      xf[f][s] = FULL ? *reinterpret_cast<const uint4*>(row + s * 16 + half * 8)
+                      : load8<VEC>(row, s * 16 + half * 8, d);
   }
 
+  // Tile loads: rows past K repeat row K-1 and get -inf norms, so they never
+  // win. Loads and stores are unconditional (tile indices clamp, every
+  // thread owns an lds_h slot) so one tile iteration is a single basic block
+  // the scheduler can interleave.
   const int ntiles = (K + TK - 1) / TK;
   uint4 pre[NV];
-  float pre_h = 0.f;
+  float pre_n = 0.f;
   auto fetch = [&](int t) {
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       const int v = tid + kThreads * q;
-      const int row = v / VPR, col = (v % VPR) * 8;
-      const int k = t * TK + row;
-      pre[q] = (v < TK * VPR && k < K) ? load8<VEC>(cb + (int64_t)k * d, col, d)
-                                       : make_uint4(0, 0, 0, 0);
+      if (TK * VPR % kThreads == 0 || v < TK * VPR) {
+        const int row = v / VPR, col = (v % VPR) * 8;
+        const int k = min(t * TK + row, K - 1);
+        pre[q] = FULL ? *reinterpret_cast<const uint4*>(cb + (int64_t)k * d + col)
+                      : load8<VEC>(cb + (int64_t)k * d, col, d);
+      }
     }
-    if (tid < TK) {
-      const int k = t * TK + tid;
-      pre_h = k < K ? -0.5f * cnb[k] : -INFINITY;
-    }
+    pre_n = cnb[min(t * TK + (tid % TK), K - 1)];
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int t, int buf) {
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       const int v = tid + kThreads * q;
-      if (v < TK * VPR) {
+      if (TK * VPR % kThreads == 0 || v < TK * VPR) {
         const int row = v / VPR, col = (v % VPR) * 8;
         *reinterpret_cast<uint4*>(&lds_c[buf][row * PITCH + col]) = pre[q];
       }
     }
-    if (tid < TK) lds_h[buf][tid] = pre_h;
+    lds_h[buf][tid] = (t * TK + tid < K) ? -0.5f * pre_n : -INFINITY;
   };
 
   float best[NF];
-  int bidx[NF];
+  int rel[NF];          // best row relative to the subtile being drained
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     best[f] = -INFINITY;
-    bidx[f] = 0;
+    rel[f] = 0;
   }
 
+  // Two accumulator sets alternate by subtile: while the MFMAs of subtile g
+  // fill one set, the argmax of subtile g-1 drains the other, EPS elements
+  // per k-step, so VALU work issues in the shadow of the matrix core. The
+  // first drain is of an all -inf set standing for subtile -1.
+  floatx16_t acc0[NF], acc1[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc1[f][r] = -INFINITY;
+
+  auto subtile = [&](int buf, int sub, floatx16_t (&cur)[NF], const floatx16_t (&prev)[NF]) {
+    floatx16_t cinit;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 hv =
+          *reinterpret_cast<const float4*>(&lds_h[buf][sub * 32 + 8 * i + 4 * half]);
+      cinit[4 * i + 0] = hv.x;
+      cinit[4 * i + 1] = hv.y;
+      cinit[4 * i + 2] = hv.z;
+      cinit[4 * i + 3] = hv.w;
+    }
+    const uint16_t* arow = &lds_c[buf][(sub * 32 + r32) * PITCH + half * 8];
+    uint4 a = *reinterpret_cast<const uint4*>(arow);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) rel[f] -= 32;     // rebase onto the subtile drained now
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 an = a;
+      if (s + 1 < KS) an = *reinterpret_cast<const uint4*>(arow + (s + 1) * 16);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) cur[f] = Mfma<DT>::run(a, xf[f][s], s == 0 ? cinit : cur[f]);
+#pragma unroll
+      for (int e = s * EPS; e < (s + 1) * EPS && e < NE; ++e)
+        argmax_elem<NF>(prev, e, best, rel);
+      a = an;
+      // pin the interleave: NF MFMAs, the step's argmax ops, the next A read
+      __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
   fetch(0);
-  stash(0);
+  stash(0, 0);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1);
+    fetch(t + 1 < ntiles ? t + 1 : t);     // the last fetch is a harmless repeat
 #pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      floatx16_t cinit;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 hv = *reinterpret_cast<const float4*>(&lds_h[buf][sub * 32 + 8 * i + 4 * half]);
-        cinit[4 * i + 0] = hv.x;
-        cinit[4 * i + 1] = hv.y;
-        cinit[4 * i + 2] = hv.z;
-        cinit[4 * i + 3] = hv.w;
-      }
-      floatx16_t acc[NF];
-      const uint16_t* arow = &lds_c[buf][(sub * 32 + r32) * PITCH + half * 8];
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const uint4 a = *reinterpret_cast<const uint4*>(arow + s * 16);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) acc[f] = Mfma<DT>::run(a, xf[f][s], s == 0 ? cinit : acc[f]);
-      }
-      const int base = t * TK + sub * 32;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) argmax_update(acc[f], base, best[f], bidx[f]);
+    for (int sub = 0; sub < NSUB; sub += 2) {
+      subtile(buf, sub, acc0, acc1);
+      subtile(buf, sub + 1, acc1, acc0);
     }
-    if (t + 1 < ntiles) stash(buf ^ 1);
+    stash(t + 1, buf ^ 1);                 // never read after the last tile
     __syncthreads();
   }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) rel[f] -= 32;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) argmax_elem<NF>(acc1, e, best, rel);
 
+  // rel is relative to the last subtile, which starts at row 32*(subtiles-1)
+  const int last_base = 32 * (ntiles * NSUB - 1);
   int32_t* ib = ids + (int64_t)b * N;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int idx = merge_halves(best[f], bidx[f], half);
+    const int idx = merge_halves(best[f], rel[f] + last_base, half);
     const int n = nblk + f * 32 + r32;
-    if (half == 0 && n < N) ib[n] = idx;
+    if (half == 0 && n < N) ib[n] = min(max(idx, 0), K - 1);
   }
 }
 
@@ -393,12 +449,17 @@ hipError_t run_smalld(const void* x, const void* c, const float* cn, int64_t B, 
   const int bpb = (int)((N + BN - 1) / BN);
   const int64_t grid = B * bpb;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (vec_ok(x, c, d))
-    assign_smalld_kernel<DT, KS, NF, TK, true><<<(unsigned)grid, kThreads, 0, s>>>(
-        (const uint16_t*)x, (const uint16_t*)c, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
+  const uint16_t* xp = (const uint16_t*)x;
+  const uint16_t* cp = (const uint16_t*)c;
+  if (vec_ok(x, c, d) && d == 16 * KS)
+    assign_smalld_kernel<DT, KS, NF, TK, true, true><<<(unsigned)grid, kThreads, 0, s>>>(
+        xp, cp, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
+  else if (vec_ok(x, c, d))
+    assign_smalld_kernel<DT, KS, NF, TK, true, false><<<(unsigned)grid, kThreads, 0, s>>>(
+        xp, cp, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
   else
-    assign_smalld_kernel<DT, KS, NF, TK, false><<<(unsigned)grid, kThreads, 0, s>>>(
-        (const uint16_t*)x, (const uint16_t*)c, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
+    assign_smalld_kernel<DT, KS, NF, TK, false, false><<<(unsigned)grid, kThreads, 0, s>>>(
+        xp, cp, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
   return hipGetLastError();
 }
 
@@ -409,7 +470,7 @@ hipError_t smalld_dt(const void* x, const void* c, const float* cn, int64_t B, i
   if (d <= 64) return run_smalld<DT, 4, 2, 64>(x, c, cn, B, N, d, K, ids, s);
   if (d <= 128) return run_smalld<DT, 8, 2, 64>(x, c, cn, B, N, d, K, ids, s);
   if (d <= 256) return run_smalld<DT, 16, 2, 64>(x, c, cn, B, N, d, K, ids, s);
-  if (d <= 512) return run_smalld<DT, 32, 1, 32>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 512) return run_smalld<DT, 32, 1, 64>(x, c, cn, B, N, d, K, ids, s);
   return hipErrorNotSupported;
 }
 

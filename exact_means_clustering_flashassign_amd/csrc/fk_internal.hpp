@@ -109,12 +109,12 @@ struct UpdateWs {
   int32_t* offsets;   // (B,K+1) segment starts
   int32_t* cursor;    // (B,K) scatter cursors
   int32_t* perm;      // (B,N) point index per sorted position
+  float* part;        // (B, runs + finalize blocks) partial squared moves
 };
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K);
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K);
 hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, int64_t N,
                          int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
-                         const UpdateWs& ws, hipStream_t s,
-                         hipEvent_t ev_after_hist = nullptr);
+                         const UpdateWs& ws, hipStream_t s);
 
 }  // namespace fk

@@ -10,20 +10,24 @@
 // Update"; "Flash-KMeans: Fast and Memory-Efficient Exact K-Means", Abstract).
 //
 // Steps (one launch each, all on the caller's stream):
-//   zero      sums, counts and shift start at zero;
+//   zero      counts and shift start at zero;
 //   hist      counts[b,k]: per-block LDS histogram, one global atomic per
 //             (block, non-empty bin);
 //   scan      offsets[b,0..K] = exclusive prefix sum of counts; cursor = copy;
+//             the fp32 sums of clusters that straddle a run (below) are zeroed;
 //   scatter   perm[b, offsets[id] + rank] = n: per-block LDS ranks, one
 //             cursor atomic per (block, non-empty bin);
 //   segreduce sums[b,k,:] = sum of x[b, perm[i], :] over segment k; each wave
 //             owns a fixed run of sorted positions (balanced by position, not
 //             by segment, so a hot cluster spreads over many waves); a segment
-//             lying wholly inside the run is written with plain stores, a
-//             piece of a longer segment with one fp32 atomic add per element;
-//             at most (K + number of runs) * d atomics per problem;
-//   finalize  c = sums / counts where counts > 0, else unchanged;
-//             shift[b] += sum (c_new - c_old)^2.
+//             lying wholly inside the run is finished by that wave
+//             (c = sum / count, its squared move added to the shift); a piece
+//             of a longer segment is added to sums with one fp32 atomic per
+//             element: at most (K + number of runs) * d atomics per problem;
+//   finalize_split  c = sums / count for the straddling clusters;
+//   shift_reduce    shift[b] = sum of the per-wave / per-block squared moves
+//             (partials in the workspace, summed in a fixed order).
+// Empty clusters are never touched, so they keep their centroid.
 #include "fk_internal.hpp"
 
 namespace fk {
@@ -36,18 +40,17 @@ constexpr int kSegRun = 256;           // sorted positions per wave in segreduce
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void zero_kernel(float* __restrict__ sums, int64_t nsums,
-                                                        int32_t* __restrict__ counts,
-                                                        int64_t ncounts, float* __restrict__ shift,
-                                                        int64_t B) {
+__global__ __launch_bounds__(kThreads) void zero_kernel(int32_t* __restrict__ counts,
+                                                        int64_t ncounts) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  float4* s4 = reinterpret_cast<float4*>(sums);
-  const int64_t n4 = nsums / 4;
-  for (int64_t i = i0; i < n4; i += stride) s4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t i = n4 * 4 + i0; i < nsums; i += stride) sums[i] = 0.f;
   for (int64_t i = i0; i < ncounts; i += stride) counts[i] = 0;
-  for (int64_t i = i0; i < B; i += stride) shift[i] = 0.f;
+}
+
+__global__ __launch_bounds__(kThreads) void fill_f32_kernel(float* __restrict__ p, float v,
+                                                            int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -84,10 +87,19 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// scan: one block per problem; exclusive prefix sum of counts.
+// scan: one block per problem; exclusive prefix sum of counts. Also zeroes
+// the fp32 sums of clusters whose segment straddles a segreduce run.
+// A cluster's segment [lo, hi) of sorted positions straddles a segreduce run
+// boundary: it is then summed piecewise with atomics and finished in
+// finalize_split; otherwise one wave sums it and finishes it.
+__device__ __forceinline__ bool straddles(int lo, int hi) {
+  return hi > lo && lo / kSegRun != (hi - 1) / kSegRun;
+}
+
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ cursor, int K) {
+                                                    int32_t* __restrict__ cursor,
+                                                    float* __restrict__ sums, int K, int d) {
   __shared__ int32_t part[1024];
   const int b = blockIdx.x, t = threadIdx.x;
   const int64_t per = ((int64_t)K + 1023) / 1024;
@@ -108,10 +120,21 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   int run = t ? part[t - 1] : 0;
   int32_t* ob = offsets + (int64_t)b * (K + 1);
   int32_t* kb = cursor + (int64_t)b * K;
+  float* sbase = sums + (int64_t)b * K * d;
   for (int64_t i = lo; i < hi; ++i) {
     ob[i] = run;
     kb[i] = run;
-    run += cb[i];
+    const int next = run + cb[i];
+    if (straddles(run, next)) {      // its pieces are summed with atomics: start at zero
+      float* row = sbase + i * d;
+      if ((d & 3) == 0) {
+        float4* r4 = reinterpret_cast<float4*>(row);
+        for (int j = 0; j < d / 4; ++j) r4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        for (int j = 0; j < d; ++j) row[j] = 0.f;
+      }
+    }
+    run = next;
   }
   if (t == 1023) ob[K] = part[1023];
 }
@@ -163,92 +186,55 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// segreduce: one wave per run of kSegRun sorted positions. Lane l owns
-// dims [db + l*V, db + l*V + V) of the row; DT element type, V elements.
+// segreduce: one wave per run of kSegRun sorted positions.
+//
+// The wave stages its run of perm in LDS, then walks the segments that
+// intersect the run. Rows are read as 16-byte vectors: LPR lanes cover one
+// row (VPL vectors each), so a wave instruction reads 64/LPR rows and each
+// lane keeps U row-iterations of loads in flight. At the end of a piece the
+// row groups are summed with lane shuffles. A segment wholly inside the run
+// is finished here: c = sum / count, and its squared move is added to the
+// shift. A piece of a longer segment is added to `sums` with one fp32 atomic
+// per element; finalize_split completes those clusters.
 template <int DT>
-struct RowLoad;
-template <>
-struct RowLoad<FK_F32> {
-  static constexpr int bytes = 4;
-  __device__ static __forceinline__ float get(const void* p, int64_t i) {
-    return reinterpret_cast<const float*>(p)[i];
-  }
-};
-template <>
-struct RowLoad<FK_F16> {
-  static constexpr int bytes = 2;
-  __device__ static __forceinline__ float get(const void* p, int64_t i) {
-    return f16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
-  }
-};
-template <>
-struct RowLoad<FK_BF16> {
-  static constexpr int bytes = 2;
-  __device__ static __forceinline__ float get(const void* p, int64_t i) {
-    return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
-  }
-};
-
-// V elements starting at element index i of a row, widened to fp32; only the
-// first `nvalid` are read (the rest are zero). VEC: when nvalid >= V the V
-// elements are contiguous and aligned to V*bytes.
-template <int DT, int V, bool VEC>
-__device__ __forceinline__ void load_row(const void* x, int64_t i, int nvalid, float (&v)[V]) {
-  if (VEC && nvalid >= V) {
-    if constexpr (DT == FK_F32) {
-      if constexpr (V == 1) {
-        v[0] = reinterpret_cast<const float*>(x)[i];
-      } else if constexpr (V == 2) {
-        const float2 t = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(x) + i);
-        v[0] = t.x; v[1] = t.y;
-      } else {
-#pragma unroll
-        for (int e = 0; e < V; e += 4) {
-          const float4 t = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + i + e);
-          v[e] = t.x; v[e + 1] = t.y; v[e + 2] = t.z; v[e + 3] = t.w;
-        }
-      }
-    } else {
-      const uint16_t* p = reinterpret_cast<const uint16_t*>(x) + i;
-      uint16_t h[V];
-      if constexpr (V == 1) {
-        h[0] = p[0];
-      } else if constexpr (V == 2) {
-        const uint32_t t = *reinterpret_cast<const uint32_t*>(p);
-        h[0] = (uint16_t)t; h[1] = (uint16_t)(t >> 16);
-      } else if constexpr (V == 4) {
-        const uint2 t = *reinterpret_cast<const uint2*>(p);
-        h[0] = (uint16_t)t.x; h[1] = (uint16_t)(t.x >> 16);
-        h[2] = (uint16_t)t.y; h[3] = (uint16_t)(t.y >> 16);
-      } else {
-#pragma unroll
-        for (int e = 0; e < V; e += 8) {
-          const uint4 t = *reinterpret_cast<const uint4*>(p + e);
-          h[e + 0] = (uint16_t)t.x; h[e + 1] = (uint16_t)(t.x >> 16);
-          h[e + 2] = (uint16_t)t.y; h[e + 3] = (uint16_t)(t.y >> 16);
-          h[e + 4] = (uint16_t)t.z; h[e + 5] = (uint16_t)(t.z >> 16);
-          h[e + 6] = (uint16_t)t.w; h[e + 7] = (uint16_t)(t.w >> 16);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < V; ++e)
-        v[e] = (DT == FK_F16) ? f16_bits_to_f32(h[e]) : bf16_bits_to_f32(h[e]);
-    }
+__device__ __forceinline__ void widen16(const uint4 v, float* out) {
+  if constexpr (DT == FK_F32) {
+    out[0] = __builtin_bit_cast(float, v.x);
+    out[1] = __builtin_bit_cast(float, v.y);
+    out[2] = __builtin_bit_cast(float, v.z);
+    out[3] = __builtin_bit_cast(float, v.w);
   } else {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int e = 0; e < V; ++e) v[e] = e < nvalid ? RowLoad<DT>::get(x, i + e) : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = Elem<DT>::widen((uint16_t)(w[i] & 0xFFFFu));
+      out[2 * i + 1] = Elem<DT>::widen((uint16_t)(w[i] >> 16));
+    }
   }
 }
 
-template <int DT, int V, bool VEC>
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* x, int64_t i) {
+  if constexpr (DT == FK_F32) return reinterpret_cast<const float*>(x)[i];
+  else return Elem<DT>::widen(reinterpret_cast<const uint16_t*>(x)[i]);
+}
+
+template <int DT, int LPR, int VPL, bool VEC>
 __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     const void* __restrict__ x, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ offsets, float* __restrict__ sums, int N, int d, int K,
-    int runs_per_batch, int64_t total_runs) {
-  constexpr int U = 8;   // rows in flight per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (wid >= total_runs) return;
+    const int32_t* __restrict__ offsets, float* __restrict__ sums, float* __restrict__ c,
+    float* __restrict__ moved_part, int N, int d, int K, int runs_per_batch, int64_t total_runs,
+    int dbase, int parts_per_batch) {
+  constexpr int R = 64 / LPR;                    // rows per wave instruction
+  constexpr int EB = DT == FK_F32 ? 4 : 2;
+  constexpr int EV = 16 / EB;                    // elements per 16-byte vector
+  constexpr int NE = VPL * EV;                   // elements per lane
+  constexpr int U = VPL >= 8 ? 1 : (VPL == 4 ? 2 : (VPL == 2 ? 4 : 8));
+  __shared__ int32_t lperm[kThreads / 64][kSegRun];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane / LPR, li = lane % LPR;
+  const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + wv;
+  if (wid >= total_runs) return;                 // whole wave; no block barrier follows
   const int b = (int)(wid / runs_per_batch);
   const int p0 = (int)(wid % runs_per_batch) * kSegRun;
   const int p1 = p0 + kSegRun < N ? p0 + kSegRun : N;
@@ -256,115 +242,177 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   const int32_t* pb = perm + (int64_t)b * N;
   const int64_t xoff = (int64_t)b * N * d;
   float* sb = sums + (int64_t)b * K * d;
+  float* cb = c + (int64_t)b * K * d;
 
-  // cluster holding position p0: the last k with offsets[k] <= p0
-  int lo = 0, hi = K;   // invariant: offsets[lo] <= p0 < offsets[hi+1]... search on [0,K)
+  for (int j = lane; j < p1 - p0; j += 64) lperm[wv][j] = pb[p0 + j];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // first cluster of the run: the last k with offsets[k] <= p0
+  int lo = 0, hi = K;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (__builtin_amdgcn_readfirstlane(ob[mid]) <= p0) lo = mid; else hi = mid - 1;
   }
-  const int k_first = lo;
+  int k = lo;
 
-  for (int db = 0; db < d; db += 64 * V) {
-    const int col = db + lane * V;
-    const bool ok = col < d;
-    const int nvalid = d - col;
-    int k = k_first;
-    int seg_lo = __builtin_amdgcn_readfirstlane(ob[k]);
-    while (seg_lo < p1) {
-      const int seg_hi = __builtin_amdgcn_readfirstlane(ob[k + 1]);
-      if (seg_hi > seg_lo) {
-        const int a = seg_lo > p0 ? seg_lo : p0;
-        const int e = seg_hi < p1 ? seg_hi : p1;
-        float acc[V];
+  int col[VPL];                                  // first element of each of my vectors
 #pragma unroll
-        for (int j = 0; j < V; ++j) acc[j] = 0.f;
-        int i = a;
-        for (; i + U <= e; i += U) {
-          float v[U][V];
+  for (int q = 0; q < VPL; ++q) col[q] = dbase + (li + LPR * q) * EV;
+
+  float moved = 0.f;
+  int seg_lo = __builtin_amdgcn_readfirstlane(ob[k]);
+  while (seg_lo < p1) {
+    const int seg_hi = __builtin_amdgcn_readfirstlane(ob[k + 1]);
+    if (seg_hi > seg_lo) {
+      const int a = seg_lo > p0 ? seg_lo : p0;
+      const int e = seg_hi < p1 ? seg_hi : p1;
+      float acc[NE];
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int n = __builtin_amdgcn_readfirstlane(pb[i + u]);
-            load_row<DT, V, VEC>(x, xoff + (int64_t)n * d + col, nvalid, v[u]);
-          }
+      for (int i = 0; i < NE; ++i) acc[i] = 0.f;
+      for (int base = a; base < e; base += U * R) {
+        int n[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int p = base + u * R + g;
+          n[u] = p < e ? lperm[wv][p - p0] : -1;
+        }
+        if constexpr (VEC) {
+          uint4 v[U][VPL];
 #pragma unroll
           for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < V; ++j) acc[j] += v[u][j];
-        }
-        for (; i < e; ++i) {
-          float v[V];
-          const int n = __builtin_amdgcn_readfirstlane(pb[i]);
-          load_row<DT, V, VEC>(x, xoff + (int64_t)n * d + col, nvalid, v);
-#pragma unroll
-          for (int j = 0; j < V; ++j) acc[j] += v[j];
-        }
-        float* dst = sb + (int64_t)k * d + col;
-        const bool whole = seg_lo >= p0 && seg_hi <= p1;
-        if (ok) {
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            if (col + j < d) {
-              if (whole) dst[j] = acc[j];
-              else unsafeAtomicAdd(dst + j, acc[j]);
+            for (int q = 0; q < VPL; ++q) {
+              const bool ok = n[u] >= 0 && col[q] < d;
+              const int64_t idx = xoff + (int64_t)(ok ? n[u] : 0) * d + (ok ? col[q] : 0);
+              v[u][q] = ok ? *reinterpret_cast<const uint4*>(
+                                 reinterpret_cast<const char*>(x) + idx * EB)
+                           : make_uint4(0, 0, 0, 0);
             }
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int q = 0; q < VPL; ++q) {
+              float f[EV];
+              widen16<DT>(v[u][q], f);
+#pragma unroll
+              for (int i = 0; i < EV; ++i) acc[q * EV + i] += f[i];
+            }
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (n[u] < 0) continue;
+            const int64_t row = xoff + (int64_t)n[u] * d;
+#pragma unroll
+            for (int q = 0; q < VPL; ++q)
+#pragma unroll
+              for (int i = 0; i < EV; ++i)
+                if (col[q] + i < d) acc[q * EV + i] += load_elem<DT>(x, row + col[q] + i);
           }
         }
       }
-      ++k;
-      if (k >= K) break;
-      seg_lo = seg_hi;
+      // sum the R row groups
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int i = 0; i < NE; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
+      const bool whole = seg_lo >= p0 && seg_hi <= p1;
+      if (g == 0) {
+        const float cnt = (float)(seg_hi - seg_lo);
+#pragma unroll
+        for (int q = 0; q < VPL; ++q)
+#pragma unroll
+          for (int i = 0; i < EV; ++i) {
+            const int j = col[q] + i;
+            if (j < d) {
+              const int64_t o = (int64_t)k * d + j;
+              if (whole) {
+                const float nw = acc[q * EV + i] / cnt;
+                const float dl = nw - cb[o];
+                cb[o] = nw;
+                moved = fmaf(dl, dl, moved);
+              } else {
+                unsafeAtomicAdd(sb + o, acc[q * EV + i]);
+              }
+            }
+          }
+      }
     }
+    ++k;
+    if (k >= K) break;
+    seg_lo = seg_hi;
+  }
+  // this wave's share of the shift; several d passes accumulate in order
+  moved = wave_sum(moved);
+  if (lane == 0) {
+    float* slot = moved_part + (int64_t)b * parts_per_batch + (wid % runs_per_batch);
+    *slot = dbase == 0 ? moved : *slot + moved;
   }
 }
 
 // ---------------------------------------------------------------------------
-// finalize: block (chunk of one problem's K*d elements, b).
-constexpr int kFinPerThread = 4;
-__global__ __launch_bounds__(kThreads) void finalize_kernel(const float* __restrict__ sums,
-                                                            const int32_t* __restrict__ counts,
-                                                            float* __restrict__ c,
-                                                            float* __restrict__ shift, int64_t Kd,
-                                                            int d, int K, int chunks_per_batch) {
-  __shared__ float part[kThreads / 64];
-  const int b = blockIdx.x / chunks_per_batch;
-  const int64_t e0 = (int64_t)(blockIdx.x % chunks_per_batch) * kThreads * kFinPerThread;
-  const float* sb = sums + (int64_t)b * Kd;
-  const int32_t* nb = counts + (int64_t)b * K;
-  float* cbp = c + (int64_t)b * Kd;
-  float acc = 0.f;
-#pragma unroll
-  for (int q = 0; q < kFinPerThread; ++q) {
-    const int64_t e = e0 + (int64_t)q * kThreads + threadIdx.x;
-    if (e < Kd) {
-      const int k = (int)(e / d);
-      const int n = nb[k];
-      if (n > 0) {
-        const float old = cbp[e];
-        const float nw = sb[e] / (float)n;
-        cbp[e] = nw;
-        const float dl = nw - old;
-        acc = fmaf(dl, dl, acc);
-      }
+// finalize_split: clusters whose segment straddles a run boundary. Block j of
+// problem b scans rows j*4+w, j*4+w+4*fb, ... (w = wave); straddling rows get
+// c = sums / count; the block's squared moves go to its partial slot.
+constexpr int kFinBlocks = 64;   // blocks per problem (at most)
+
+__global__ __launch_bounds__(kThreads) void finalize_split_kernel(
+    const float* __restrict__ sums, const int32_t* __restrict__ offsets, float* __restrict__ c,
+    float* __restrict__ moved_part, int d, int K, int fb, int parts_per_batch, int part0) {
+  __shared__ float wsum[kThreads / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int b = blockIdx.x / fb, j = blockIdx.x % fb;
+  const int32_t* ob = offsets + (int64_t)b * (K + 1);
+  float moved = 0.f;
+  for (int k = j * (kThreads / 64) + wv; k < K; k += fb * (kThreads / 64)) {
+    const int lo = ob[k], hi = ob[k + 1];
+    if (!straddles(lo, hi)) continue;
+    const float cnt = (float)(hi - lo);
+    const float* srow = sums + ((int64_t)b * K + k) * d;
+    float* crow = c + ((int64_t)b * K + k) * d;
+    for (int i = lane; i < d; i += 64) {
+      const float nw = srow[i] / cnt;
+      const float dl = nw - crow[i];
+      crow[i] = nw;
+      moved = fmaf(dl, dl, moved);
     }
   }
-  acc = wave_sum(acc);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  moved = wave_sum(moved);
+  if (lane == 0) wsum[wv] = moved;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
+    moved_part[(int64_t)b * parts_per_batch + part0 + j] = t;
+  }
+}
+
+// shift[b] = sum of the problem's partials (fixed order: deterministic).
+__global__ __launch_bounds__(kThreads) void shift_reduce_kernel(const float* __restrict__ part,
+                                                                float* __restrict__ shift,
+                                                                int parts_per_batch) {
+  __shared__ float wsum[kThreads / 64];
+  const int b = blockIdx.x;
+  const float* p = part + (int64_t)b * parts_per_batch;
+  float t = 0.f;
+  for (int i = threadIdx.x; i < parts_per_batch; i += kThreads) t += p[i];
+  t = wave_sum(t);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = t;
   __syncthreads();
   if (threadIdx.x == 0) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) s += part[w];
-    if (s != 0.f) unsafeAtomicAdd(&shift[b], s);
+    for (int w = 0; w < kThreads / 64; ++w) s += wsum[w];
+    shift[b] = s;
   }
 }
 
 // ---------------------------------------------------------------------------
 template <int IPT>
 hipError_t run_hist_scatter(const int32_t* ids, int32_t* counts, int32_t* cursor, int32_t* perm,
-                            const int32_t* offsets_unused, int64_t B, int64_t N, int64_t K,
-                            bool scatter, hipStream_t s) {
-  (void)offsets_unused;
+                            int64_t B, int64_t N, int64_t K, bool scatter, hipStream_t s) {
   constexpr int CH = kThreads * IPT;
   const int nchunks = (int)((N + CH - 1) / CH);
   const int nranges = (int)((K + kMaxLdsBins - 1) / kMaxLdsBins);
@@ -400,32 +448,50 @@ hipError_t run_hist_scatter(const int32_t* ids, int32_t* counts, int32_t* cursor
   return hipGetLastError();
 }
 
-template <int DT, int V>
+template <int DT, int LPR, int VPL>
 hipError_t run_segreduce(const void* x, const int32_t* perm, const int32_t* offsets, float* sums,
-                         int64_t B, int64_t N, int64_t d, int64_t K, hipStream_t s) {
+                         float* c, float* part, int parts, int64_t B, int64_t N, int64_t d,
+                         int64_t K, hipStream_t s) {
+  constexpr int EB = DT == FK_F32 ? 4 : 2;
+  constexpr int span = LPR * VPL * (16 / EB);    // elements covered per pass
   const int runs = (int)((N + kSegRun - 1) / kSegRun);
   const int64_t total = B * runs;
   const int64_t grid = (total + 3) / 4;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const int eb = DT == FK_F32 ? 4 : 2;
-  const bool vec = (d % V) == 0 && ((uintptr_t)x % (uintptr_t)(V * eb)) == 0;
-  if (vec)
-    segreduce_kernel<DT, V, true><<<(unsigned)grid, kThreads, 0, s>>>(
-        x, perm, offsets, sums, (int)N, (int)d, (int)K, runs, total);
-  else
-    segreduce_kernel<DT, V, false><<<(unsigned)grid, kThreads, 0, s>>>(
-        x, perm, offsets, sums, (int)N, (int)d, (int)K, runs, total);
-  return hipGetLastError();
+  const bool vec = (d * EB) % 16 == 0 && ((uintptr_t)x % 16) == 0;
+  for (int64_t db = 0; db < d; db += span) {
+    if (vec)
+      segreduce_kernel<DT, LPR, VPL, true><<<(unsigned)grid, kThreads, 0, s>>>(
+          x, perm, offsets, sums, c, part, (int)N, (int)d, (int)K, runs, total, (int)db, parts);
+    else
+      segreduce_kernel<DT, LPR, VPL, false><<<(unsigned)grid, kThreads, 0, s>>>(
+          x, perm, offsets, sums, c, part, (int)N, (int)d, (int)K, runs, total, (int)db, parts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
+// Lanes per row: enough 16-byte vectors to cover the row, as a power of two;
+// rows wider than 64 vectors take VPL vectors per lane (several passes above
+// 64*8 vectors).
 template <int DT>
 hipError_t segreduce_dt(const void* x, const int32_t* perm, const int32_t* offsets, float* sums,
-                        int64_t B, int64_t N, int64_t d, int64_t K, hipStream_t s) {
-  if (d <= 64) return run_segreduce<DT, 1>(x, perm, offsets, sums, B, N, d, K, s);
-  if (d <= 128) return run_segreduce<DT, 2>(x, perm, offsets, sums, B, N, d, K, s);
-  if (d <= 256) return run_segreduce<DT, 4>(x, perm, offsets, sums, B, N, d, K, s);
-  if (d <= 512) return run_segreduce<DT, 8>(x, perm, offsets, sums, B, N, d, K, s);
-  return run_segreduce<DT, 16>(x, perm, offsets, sums, B, N, d, K, s);
+                        float* c, float* part, int parts, int64_t B, int64_t N, int64_t d,
+                        int64_t K, hipStream_t s) {
+  constexpr int EV = DT == FK_F32 ? 4 : 8;
+  const int64_t nvec = (d + EV - 1) / EV;
+#define FK_SEG(L, V) \
+  run_segreduce<DT, L, V>(x, perm, offsets, sums, c, part, parts, B, N, d, K, s)
+  if (nvec <= 4) return FK_SEG(4, 1);
+  if (nvec <= 8) return FK_SEG(8, 1);
+  if (nvec <= 16) return FK_SEG(16, 1);
+  if (nvec <= 32) return FK_SEG(32, 1);
+  if (nvec <= 64) return FK_SEG(64, 1);
+  if (nvec <= 128) return FK_SEG(64, 2);
+  if (nvec <= 256) return FK_SEG(64, 4);
+  return FK_SEG(64, 8);
+#undef FK_SEG
 }
 
 #define FK_CHECK(call)                   \
@@ -436,9 +502,17 @@ hipError_t segreduce_dt(const void* x, const int32_t* perm, const int32_t* offse
 
 }  // namespace
 
+int fin_blocks(int64_t K) {
+  const int64_t fb = (K + 63) / 64;
+  return (int)(fb < kFinBlocks ? fb : kFinBlocks);
+}
+
+int64_t shift_parts(int64_t N, int64_t K) { return (N + kSegRun - 1) / kSegRun + fin_blocks(K); }
+
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K) {
   return align256((size_t)B * K * d * 4) + align256((size_t)B * (K + 1) * 4) +
-         align256((size_t)B * K * 4) + align256((size_t)B * N * 4);
+         align256((size_t)B * K * 4) + align256((size_t)B * N * 4) +
+         align256((size_t)B * shift_parts(N, K) * 4);
 }
 
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K) {
@@ -451,50 +525,60 @@ UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K)
   w.cursor = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)B * K * 4);
   w.perm = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)B * N * 4);
+  w.part = reinterpret_cast<float*>(p);
   return w;
 }
 
 hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, int64_t N,
                          int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
-                         const UpdateWs& ws, hipStream_t s, hipEvent_t) {
+                         const UpdateWs& ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
+  const int parts = (int)shift_parts(N, K);
+  const int runs = (int)((N + kSegRun - 1) / kSegRun);
+  const int fb = fin_blocks(K);
   {
-    const int64_t work = B * K * d / 4 + B * K;
-    int64_t g = (work + kThreads - 1) / kThreads;
+    int64_t g = (B * K + kThreads - 1) / kThreads;
     g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
-    zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(ws.sums, B * K * d, counts, B * K, shift, B);
+    zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
     FK_CHECK(hipGetLastError());
   }
   if (N > 0) {
-    if (K <= 4096) {
-      FK_CHECK(run_hist_scatter<16>(ids, counts, nullptr, nullptr, nullptr, B, N, K, false, s));
-    } else {
-      FK_CHECK(run_hist_scatter<64>(ids, counts, nullptr, nullptr, nullptr, B, N, K, false, s));
-    }
-    scan_kernel<<<(unsigned)B, 1024, 0, s>>>(counts, ws.offsets, ws.cursor, (int)K);
-    FK_CHECK(hipGetLastError());
-    if (K <= 4096) {
-      FK_CHECK(run_hist_scatter<16>(ids, nullptr, ws.cursor, ws.perm, nullptr, B, N, K, true, s));
-    } else {
-      FK_CHECK(run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, nullptr, B, N, K, true, s));
-    }
-    if (dt == FK_F16)
-      FK_CHECK(segreduce_dt<FK_F16>(x, ws.perm, ws.offsets, ws.sums, B, N, d, K, s));
-    else if (dt == FK_BF16)
-      FK_CHECK(segreduce_dt<FK_BF16>(x, ws.perm, ws.offsets, ws.sums, B, N, d, K, s));
+    if (K <= 4096)
+      FK_CHECK(run_hist_scatter<16>(ids, counts, nullptr, nullptr, B, N, K, false, s));
     else
-      FK_CHECK(segreduce_dt<FK_F32>(x, ws.perm, ws.offsets, ws.sums, B, N, d, K, s));
-  }
-  {
-    const int64_t Kd = K * d;
-    const int64_t per = (int64_t)kThreads * kFinPerThread;
-    const int chunks = (int)((Kd + per - 1) / per);
-    const int64_t grid = B * chunks;
+      FK_CHECK(run_hist_scatter<64>(ids, counts, nullptr, nullptr, B, N, K, false, s));
+    scan_kernel<<<(unsigned)B, 1024, 0, s>>>(counts, ws.offsets, ws.cursor, ws.sums, (int)K,
+                                             (int)d);
+    FK_CHECK(hipGetLastError());
+    if (K <= 4096)
+      FK_CHECK(run_hist_scatter<16>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
+    else
+      FK_CHECK(run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
+    if (dt == FK_F16)
+      FK_CHECK(segreduce_dt<FK_F16>(x, ws.perm, ws.offsets, ws.sums, c, ws.part, parts, B, N, d,
+                                    K, s));
+    else if (dt == FK_BF16)
+      FK_CHECK(segreduce_dt<FK_BF16>(x, ws.perm, ws.offsets, ws.sums, c, ws.part, parts, B, N,
+                                     d, K, s));
+    else
+      FK_CHECK(segreduce_dt<FK_F32>(x, ws.perm, ws.offsets, ws.sums, c, ws.part, parts, B, N, d,
+                                    K, s));
+    const int64_t grid = B * fb;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    finalize_kernel<<<(unsigned)grid, kThreads, 0, s>>>(ws.sums, counts, c, shift, Kd, (int)d,
-                                                        (int)K, chunks);
+    finalize_split_kernel<<<(unsigned)grid, kThreads, 0, s>>>(ws.sums, ws.offsets, c, ws.part,
+                                                              (int)d, (int)K, fb, parts, runs);
+    FK_CHECK(hipGetLastError());
+  } else {
+    // no point: every cluster is empty and keeps its centroid; zero the partials
+    const int64_t n = B * parts;
+    int64_t g = (n + kThreads - 1) / kThreads;
+    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+    fill_f32_kernel<<<(unsigned)g, kThreads, 0, s>>>(ws.part, 0.f, n);
     FK_CHECK(hipGetLastError());
   }
+  shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, parts);
+  FK_CHECK(hipGetLastError());
   return hipSuccess;
 }
 
