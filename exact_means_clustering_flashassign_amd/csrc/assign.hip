@@ -79,19 +79,62 @@ __device__ __forceinline__ int merge_halves(float best, int bidx, int half) {
 // ===========================================================================
 // small-D
 // ===========================================================================
-// One argmax step on element e of an accumulator set: e / 16 selects the
-// point fragment, e % 16 the row slot. Strict '>' over increasing rows keeps
-// the lowest index among equal scores. The index is kept relative to the
-// subtile being drained (`rel`, rebased by -32 per subtile), so the candidate
-// is an inline constant and the select needs no extra register move.
-template <int NF>
-__device__ __forceinline__ void argmax_elem(const floatx16_t (&acc)[NF], int e,
-                                            float (&best)[NF], int (&rel)[NF]) {
-  const int f = e >> 4, r = e & 15;
-  const float v = acc[f][r];
-  const bool gt = v > best[f];
-  best[f] = gt ? v : best[f];
-  rel[f] = gt ? 8 * (r >> 2) + (r & 3) : rel[f];
+// Running argmax, per point fragment f, over the 16 scores a lane holds for
+// one 32-row subtile (rows 8*(r/4) + 4*half + r%4 of the subtile, r = 0..15):
+//   m     = max of the 16 scores                      (v_max3 tree, 8 ops)
+//   if m > best: best = m, btile = subtile, saved = the 16 scores
+// Strict '>' keeps the first subtile that reaches the maximum; the row is
+// located once at the end as the first slot of `saved` equal to best, so the
+// lowest index among equal scores wins, exactly as a sequential scan would.
+struct Argmax {
+  float best;
+  int btile;
+  float saved[16];
+};
+
+// Part `part` (0..7) of draining accumulator `acc` of subtile g into st.
+// The work is split so it can be spread over the k-steps of the next
+// subtile: parts 0-3 build the max tree, part 4 compares, parts 4-7 save.
+__device__ __forceinline__ void drain_part(const floatx16_t& acc, int part, int g, Argmax& st,
+                                           float (&m)[6], bool& gt) {
+  switch (part) {
+    case 0:
+      m[0] = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+      m[1] = fmaxf(fmaxf(acc[3], acc[4]), acc[5]);
+      break;
+    case 1:
+      m[2] = fmaxf(fmaxf(acc[6], acc[7]), acc[8]);
+      m[3] = fmaxf(fmaxf(acc[9], acc[10]), acc[11]);
+      break;
+    case 2:
+      m[4] = fmaxf(fmaxf(acc[12], acc[13]), acc[14]);
+      m[5] = fmaxf(fmaxf(m[0], m[1]), m[2]);
+      break;
+    case 3:
+      m[0] = fmaxf(fmaxf(m[3], m[4]), acc[15]);
+      m[0] = fmaxf(m[5], m[0]);
+      break;
+    case 4:
+      gt = m[0] > st.best;
+      st.best = gt ? m[0] : st.best;
+      st.btile = gt ? g : st.btile;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st.saved[r] = gt ? acc[r] : st.saved[r];
+      break;
+    default: {
+      const int r0 = 4 * (part - 4);
+#pragma unroll
+      for (int r = r0; r < r0 + 4; ++r) st.saved[r] = gt ? acc[r] : st.saved[r];
+    }
+  }
+}
+
+// Row of the maximum, relative to the kernel's first row, for half `half`.
+__device__ __forceinline__ int argmax_row(const Argmax& st, int half) {
+  int slot = 15;
+#pragma unroll
+  for (int r = 15; r >= 0; --r) slot = st.saved[r] == st.best ? r : slot;
+  return st.btile * 32 + 8 * (slot >> 2) + 4 * half + (slot & 3);
 }
 
 // FULL: d == 16*KS, so every column of a row is real and loads need no
@@ -168,53 +211,45 @@ __global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
     lds_h[buf][tid] = (t * TK + tid < K) ? -0.5f * pre_n : -INFINITY;
   };
 
-  float best[NF];
-  int rel[NF];          // best row relative to the subtile being drained
+  Argmax st[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    best[f] = -INFINITY;
-    rel[f] = 0;
+    st[f].best = -INFINITY;
+    st[f].btile = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[f].saved[r] = -INFINITY;
   }
 
   // Two accumulator sets alternate by subtile: while the MFMAs of subtile g
-  // fill one set, the argmax of subtile g-1 drains the other, EPS elements
-  // per k-step, so VALU work issues in the shadow of the matrix core. The
-  // first drain is of an all -inf set standing for subtile -1.
-  floatx16_t acc0[NF], acc1[NF];
+  // fill one set, the argmax of subtile g-1 drains the other, spread over the
+  // k-steps, so VALU work issues in the shadow of the matrix core. The first
+  // drain is of an all -inf set standing for subtile -1.
+  floatx16_t acc[2][NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc1[f][r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) acc[1][f][r] = -INFINITY;
 
-  auto subtile = [&](int buf, int sub, floatx16_t (&cur)[NF], const floatx16_t (&prev)[NF]) {
-    floatx16_t cinit;
+  // LDS operands of a step, read ahead of use: A fragments two k-steps ahead
+  // (ring of three), C inputs (-||c||^2/2 of the lane's rows) one subtile
+  // ahead (two sets, alternating by subtile).
+  constexpr int STEPS = NSUB * KS;              // k-steps per tile
+  constexpr int PARTS = 8 * NF;                 // drain parts per subtile
+  constexpr int PPS = (PARTS + KS - 1) / KS;    // drain parts per k-step
+  auto read_a = [&](int buf, int q) -> uint4 {
+    const int sub = q / KS, kk = q % KS;
+    return *reinterpret_cast<const uint4*>(
+        &lds_c[buf][(sub * 32 + r32) * PITCH + half * 8 + kk * 16]);
+  };
+  auto read_c = [&](int buf, int sub, floatx16_t& ci) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 hv =
           *reinterpret_cast<const float4*>(&lds_h[buf][sub * 32 + 8 * i + 4 * half]);
-      cinit[4 * i + 0] = hv.x;
-      cinit[4 * i + 1] = hv.y;
-      cinit[4 * i + 2] = hv.z;
-      cinit[4 * i + 3] = hv.w;
-    }
-    const uint16_t* arow = &lds_c[buf][(sub * 32 + r32) * PITCH + half * 8];
-    uint4 a = *reinterpret_cast<const uint4*>(arow);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) rel[f] -= 32;     // rebase onto the subtile drained now
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 an = a;
-      if (s + 1 < KS) an = *reinterpret_cast<const uint4*>(arow + (s + 1) * 16);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) cur[f] = Mfma<DT>::run(a, xf[f][s], s == 0 ? cinit : cur[f]);
-#pragma unroll
-      for (int e = s * EPS; e < (s + 1) * EPS && e < NE; ++e)
-        argmax_elem<NF>(prev, e, best, rel);
-      a = an;
-      // pin the interleave: NF MFMAs, the step's argmax ops, the next A read
-      __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3 * EPS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      ci[4 * i + 0] = hv.x;
+      ci[4 * i + 1] = hv.y;
+      ci[4 * i + 2] = hv.z;
+      ci[4 * i + 3] = hv.w;
     }
   };
 
@@ -224,25 +259,47 @@ __global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     fetch(t + 1 < ntiles ? t + 1 : t);     // the last fetch is a harmless repeat
+    floatx16_t ci[2];
+    uint4 ar[3];
+    read_c(buf, 0, ci[0]);
+    ar[0] = read_a(buf, 0);
+    ar[1] = read_a(buf, 1 % STEPS);
+    read_c(buf, 1 % NSUB, ci[1]);
+    float m[NF][6];
+    bool gt[NF];
 #pragma unroll
-    for (int sub = 0; sub < NSUB; sub += 2) {
-      subtile(buf, sub, acc0, acc1);
-      subtile(buf, sub + 1, acc1, acc0);
+    for (int q = 0; q < STEPS; ++q) {
+      const int sub = q / KS, kk = q % KS;
+      const int g = t * NSUB + sub;          // global subtile index
+      floatx16_t (&cur)[NF] = acc[sub & 1];
+      const floatx16_t (&prev)[NF] = acc[(sub + 1) & 1];
+      if (q + 2 < STEPS) ar[(q + 2) % 3] = read_a(buf, q + 2);
+      if (kk == 1 && sub + 2 < NSUB) read_c(buf, sub + 2, ci[sub & 1]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        cur[f] = Mfma<DT>::run(ar[q % 3], xf[f][kk], kk == 0 ? ci[sub & 1] : cur[f]);
+#pragma unroll
+      for (int p = kk * PPS; p < (kk + 1) * PPS && p < PARTS; ++p)
+        drain_part(prev[p % NF], p / NF, g - 1, st[p % NF], m[p % NF], gt[p % NF]);
+      // keep program order across steps: the reads above stay ahead of use
+      __builtin_amdgcn_sched_barrier(0);
     }
     stash(t + 1, buf ^ 1);                 // never read after the last tile
     __syncthreads();
   }
+  {
+    const int g = ntiles * NSUB - 1;       // the last subtile, still in acc[1]
+    float m[NF][6];
+    bool gt[NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) rel[f] -= 32;
-#pragma unroll
-  for (int e = 0; e < NE; ++e) argmax_elem<NF>(acc1, e, best, rel);
+    for (int p = 0; p < 8 * NF; ++p)
+      drain_part(acc[1][p % NF], p / NF, g, st[p % NF], m[p % NF], gt[p % NF]);
+  }
 
-  // rel is relative to the last subtile, which starts at row 32*(subtiles-1)
-  const int last_base = 32 * (ntiles * NSUB - 1);
   int32_t* ib = ids + (int64_t)b * N;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    const int idx = merge_halves(best[f], rel[f] + last_base, half);
+    const int idx = merge_halves(st[f].best, argmax_row(st[f], half) - 4 * half, half);
     const int n = nblk + f * 32 + r32;
     if (half == 0 && n < N) ib[n] = min(max(idx, 0), K - 1);
   }
