@@ -15,7 +15,6 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -51,50 +50,68 @@ def update_bytes(B, N, d, K, s) -> float:
     return B * N * d * s + 16.0 * B * N + 16.0 * B * K * d + 16.0 * B * K
 
 
-def kernel_source_digest() -> str:
-    h = hashlib.sha256()
-    for name in ("assign.hip", "fk_internal.hpp"):
-        with open(os.path.join(ROOT, "exact_means_clustering_flashassign_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def measured_traffic(workload: str, phase: str):
+    """HBM bytes per launch of one phase from the committed rocprofv3 counter
+    table, if it was taken on the current kernel source; else None."""
+    from exact_means_clustering_flashassign_amd.profiling import source_digest
 
-
-def measured_traffic(workload: str):
-    """HBM bytes per assign launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(workload)
-    if not e or e.get("kernel_source_digest") != kernel_source_digest():
+    e = (t.get(workload) or {}).get(phase)
+    if not e or e.get("kernel_source_digest") != source_digest(phase):
         return None
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, n_batches: int):
-    """The oracle, untuned, on a bounded sample: one Lloyd iteration over
-    n_batches of the B problems (full N, K, d), scaled to the whole batch."""
+# Oracle sample per workload: (problems, rows per problem); None = all rows.
+CPU_SAMPLE = {"tiny_f32": (1, None), "api_example": (32, None), "io_breakdown": (32, None),
+              "large_k_zipf": (1, 1 << 17), "split_d": (8, None)}
+
+
+def cpu_baseline(w, name: str, min_seconds: float = 10.0):
+    """The oracle, untuned, on a bounded sample of the workload: one Lloyd
+    iteration over the first problems and rows of CPU_SAMPLE, repeated until
+    about min_seconds of CPU time have passed, scaled to the whole batch."""
     import numpy as np
     import oracle
+    import synthdata
 
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    nb = min(n_batches, w.B)
-    x64 = w.x64()[:nb]
+    nb, rows = CPU_SAMPLE[name]
+    nb, rows = min(nb, w.B), min(rows or w.N, w.N)
+    x64 = synthdata.to_f64(np.ascontiguousarray(w.x[:nb, :rows]), w.dtype)
     c0 = w.init64()[:nb]
-    t0 = time.perf_counter()
-    oracle.lloyd(x64, c0, 1, 0.0, w.dtype, want_near=False)
-    dt = time.perf_counter() - t0
-    per_iter_full = dt * w.B / nb
+    total, reps = 0.0, 0
+    while reps == 0 or (total < min_seconds and reps < 50):
+        t0 = time.perf_counter()
+        oracle.lloyd(x64, c0, 1, 0.0, w.dtype, want_near=False)
+        total += time.perf_counter() - t0
+        reps += 1
+    per_iter_full = total / reps * (w.B / nb) * (w.N / rows)
+    part = f"{nb} of the {w.B} problems" + ("" if rows == w.N else f", first {rows} of {w.N} rows")
     return {"value": 1.0 / per_iter_full, "unit": "iter/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"1 Lloyd iteration of {nb} of the {w.B} problems (full N, K, d), "
-                      f"fp64 NumPy on the host, {dt:.1f} s, scaled by {w.B}/{nb}"}
+            "sample": f"1 Lloyd iteration on {part} (full K, d), fp64 NumPy on the host, "
+                      f"{reps} run(s) in {total:.1f} s, scaled by problems and rows to the whole batch"}
+
+
+def copy_calibration(mib: int, dev):
+    """A plain elementwise kernel over a buffer of known size, for scaling
+    the HBM byte counters (reads and writes mib MiB each)."""
+    import torch
+
+    src = torch.empty(mib * 2**18, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -103,8 +120,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="api_example", choices=WORKLOADS)
-    ap.add_argument("--cpu-batches", type=int, default=8,
-                    help="problems in the CPU-baseline sample (0 = skip)")
+    ap.add_argument("--cpu-batches", type=int, default=1,
+                    help="1 = time the oracle on its bounded sample, 0 = skip")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="after the timed region, run a copy kernel of this size (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -158,7 +177,10 @@ def main():
     else:
         bound, peak, unit = "hbm", PEAK_HBM, "GB/s"
         achieved = a_bytes / (a_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload, "assign")
+    u_traffic = measured_traffic(args.workload, "update")
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration, dev)
     out = {
         "metric": METRIC,
         "value": args.steps / elapsed,
@@ -181,12 +203,10 @@ def main():
         "phases_ms": {"norms": n_ms, "assign": a_ms, "update": u_ms},
         "update_roofline": {"bound": "hbm", "achieved": u_bytes / (u_ms * 1e-3) / 1e9,
                             "peak": PEAK_HBM, "unit": "GB/s",
-                            "frac": u_bytes / (u_ms * 1e-3) / 1e9 / PEAK_HBM},
+                            "frac": u_bytes / (u_ms * 1e-3) / 1e9 / PEAK_HBM,
+                            "traffic": u_traffic},
     }
-    if args.cpu_batches > 0 and w.N * w.K * w.d <= 2e10:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_batches)
-    else:
-        out["cpu_baseline"] = None
+    out["cpu_baseline"] = cpu_baseline(w, args.workload) if args.cpu_batches > 0 else None
     print(json.dumps(out))
 
 

@@ -1,0 +1,287 @@
+"""rocprofv3 driver and summariser for one Lloyd workload.
+
+Runs ``bench.py`` under rocprofv3 three times, each pass a child process
+under its own hard time limit, and writes short text summaries plus the
+per-launch HBM traffic table that ``bench.py`` reports:
+
+1. ``--kernel-trace --stats``: calls, average and minimum duration and
+   share of GPU time per kernel, beside the per-phase times that bench.py
+   measured with HIP events in the same run;
+2. ``--pmc FETCH_SIZE``: KiB read from HBM per dispatch;
+3. ``--pmc WRITE_SIZE``: KiB written to HBM per dispatch.
+
+Each pass also runs bench.py's copy calibration: a plain elementwise kernel
+(``dst = -src`` in fp32) over a buffer of known size, so that each counter's
+reading converts to bytes by the ratio of the copy's known bytes to what the
+counter reports for it.
+
+Usage (on a machine with the GPU; the raw rocprofv3 output stays under
+``--raw``)::
+
+    python3 -m exact_means_clustering_flashassign_amd.profiling --workload api_example
+
+This module only reads files and starts child processes; it never touches
+the GPU itself.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import shlex
+import subprocess
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+COPY_MIB = 1024
+COPY_TAG = "neg_kernel"
+
+# Kernel sources whose text decides a kernel's counter readings.
+PHASE_SOURCES = {
+    "assign": ("assign.hip", "fk_internal.hpp"),
+    "update": ("update.hip", "fk_internal.hpp"),
+}
+
+
+def source_digest(phase: str) -> str:
+    h = hashlib.sha256()
+    for name in PHASE_SOURCES[phase]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def phase_of(kernel: str) -> str:
+    k = kernel.replace("(anonymous namespace)", "").split("(")[0]
+    if "assign_" in k:
+        return "assign"
+    if "norms_kernel" in k:
+        return "norms"
+    if COPY_TAG in k:
+        return "copy"
+    if "fk::" in k and ("widen_kernel" in k or "fill_i32_kernel" in k):
+        return "setup"
+    if "fk::" in k:
+        return "update"
+    return "other"
+
+
+def short_name(kernel: str) -> str:
+    k = kernel.replace("fk::(anonymous namespace)::", "").replace("void ", "")
+    head = k.split("(")[0]
+    if COPY_TAG in k:
+        return "torch neg_kernel (copy calibration)"
+    if "at::native::" in k:
+        return "torch " + k.split("at::native::")[-1].split("<")[0].split("(")[0][:60]
+    return head[:70]
+
+
+def _run(cmd, log, limit):
+    """One profiled pass as a child process; returns its exit status."""
+    env = dict(os.environ, TMPDIR="/tmp")
+    full = ["timeout", "-s", "KILL", str(limit)] + cmd
+    print("$ " + " ".join(shlex.quote(c) for c in full), flush=True)
+    with open(log, "w") as f:
+        r = subprocess.run(full, cwd="/tmp", env=env, stdout=f, stderr=subprocess.STDOUT)
+    print(f"  rc={r.returncode}", flush=True)
+    return r.returncode
+
+
+def _bench_cmd(args):
+    return ["python3", os.path.join(ROOT, "bench.py"), "--workload", args.workload,
+            "--steps", str(args.steps), "--warmup", str(args.warmup), "--cpu-batches", "0",
+            "--copy-calibration", str(COPY_MIB)]
+
+
+def _find(d, suffix):
+    hits = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def _bench_json(log):
+    line = None
+    with open(log) as f:
+        for ln in f:
+            if ln.startswith("{\"metric\""):
+                line = ln
+    return json.loads(line) if line else None
+
+
+def read_stats(path):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append({"kernel": r["Name"], "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                         "total_ms": float(r["TotalDurationNs"]) / 1e6,
+                         "pct": float(r["Percentage"])})
+    return rows
+
+
+def read_counter(path, counter):
+    """Mean counter value per dispatch, by kernel name."""
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            s = acc.setdefault(r["Kernel_Name"], [0.0, 0])
+            s[0] += float(r["Counter_Value"])
+            s[1] += 1
+    return {k: v[0] / v[1] for k, v in acc.items()}
+
+
+def _cmd_lines(cmds):
+    return ["  " + (c if isinstance(c, str) else " ".join(c)) for c in cmds]
+
+
+def stats_text(cmds, rows, bench):
+    out = ["rocprofv3 kernel statistics", "", "command (passes run from /tmp with TMPDIR=/tmp):"]
+    out += _cmd_lines(cmds) + [""]
+    if bench:
+        cfg = bench["config"]["workload"]
+        out += [f"workload: {cfg}", ""]
+    out.append(f"{'kernel':72s} {'phase':7s} {'calls':>5s} {'avg us':>9s} {'min us':>9s} {'share':>6s}")
+    for r in sorted(rows, key=lambda r: -r["total_ms"]):
+        out.append(f"{short_name(r['kernel']):72s} {phase_of(r['kernel']):7s} {r['calls']:5d} "
+                   f"{r['avg_us']:9.1f} {r['min_us']:9.1f} {r['pct']:5.1f}%")
+    if bench:
+        ph = bench["phases_ms"]
+        out += ["", "same run, HIP events recorded by the library on the launch stream "
+                    "(average per iteration over the timed region):"]
+        out += [f"  {k:7s} {1e3 * v:9.1f} us" for k, v in ph.items()]
+        out.append(f"  iter/s {bench['value']:.1f} (timed region under the tracer)")
+    return "\n".join(out) + "\n"
+
+
+def traffic_summary(fetch, write, nbytes_copy):
+    """Per-kernel bytes per dispatch, scaled by the copy calibration."""
+    cf = [v for k, v in fetch.items() if COPY_TAG in k]
+    cw = [v for k, v in write.items() if COPY_TAG in k]
+    if not cf or not cw:
+        raise RuntimeError("copy-calibration kernel missing from the counter output")
+    f_fetch = nbytes_copy / (cf[0] * 1024.0)
+    f_write = nbytes_copy / (cw[0] * 1024.0)
+    per = {}
+    for k in set(fetch) | set(write):
+        rd = fetch.get(k, 0.0) * 1024.0 * f_fetch
+        wr = write.get(k, 0.0) * 1024.0 * f_write
+        per[k] = {"fetch_kib": fetch.get(k, 0.0), "write_kib": write.get(k, 0.0),
+                  "read_bytes": rd, "write_bytes": wr, "phase": phase_of(k)}
+    return per, f_fetch, f_write
+
+
+def traffic_text(cmds, per, f_fetch, f_write, nbytes_copy, algo):
+    out = ["rocprofv3 HBM traffic per dispatch (FETCH_SIZE, WRITE_SIZE)", "",
+           "command (passes run from /tmp with TMPDIR=/tmp):"]
+    out += _cmd_lines(cmds)
+    out += ["", f"calibration: dst = -src over {nbytes_copy / 2**20:.0f} MiB fp32 reads and writes "
+                f"{nbytes_copy:.0f} B each way;",
+            f"  bytes per counter KiB: FETCH_SIZE x{f_fetch:.3f}, WRITE_SIZE x{f_write:.3f}", ""]
+    out.append(f"{'kernel':72s} {'phase':7s} {'FETCH KiB':>11s} {'WRITE KiB':>11s} {'read MB':>9s} {'write MB':>9s}")
+    for k, v in sorted(per.items(), key=lambda kv: -(kv[1]["read_bytes"] + kv[1]["write_bytes"])):
+        out.append(f"{short_name(k):72s} {v['phase']:7s} {v['fetch_kib']:11.0f} {v['write_kib']:11.0f} "
+                   f"{v['read_bytes'] / 1e6:9.2f} {v['write_bytes'] / 1e6:9.2f}")
+    out.append("")
+    for ph, a in algo.items():
+        meas = sum(v["read_bytes"] + v["write_bytes"] for v in per.values() if v["phase"] == ph)
+        out.append(f"{ph}: measured {meas / 1e6:.1f} MB per launch vs algorithmic {a / 1e6:.1f} MB "
+                   f"(x{meas / a:.2f})")
+    return "\n".join(out) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--workload", default="api_example")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profiles"),
+                    help="where the text summaries and traffic.json go")
+    ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "rocprof"),
+                    help="where rocprofv3 writes its raw output")
+    ap.add_argument("--limit", type=int, default=240, help="seconds per pass")
+    ap.add_argument("--summarize-only", action="store_true",
+                    help="do not run anything; summarise the raw output of an earlier run")
+    args = ap.parse_args(argv)
+    sys.path.insert(0, ROOT)
+    import bench  # algorithmic byte counts; bench imports torch lazily
+
+    wl = args.workload
+    raw = os.path.join(args.raw, wl)
+    os.makedirs(raw, exist_ok=True)
+    os.makedirs(args.out, exist_ok=True)
+    bcmd = _bench_cmd(args)
+    top = "python3 -m exact_means_clustering_flashassign_amd.profiling --workload " + wl
+    passes = {
+        "stats": ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+                  os.path.join(raw, "stats"), "-o", "run", "--"] + bcmd,
+        "fetch_size": ["rocprofv3", "--pmc", "FETCH_SIZE", "--output-format", "csv", "-d",
+                       os.path.join(raw, "fetch_size"), "-o", "run", "--"] + bcmd,
+        "write_size": ["rocprofv3", "--pmc", "WRITE_SIZE", "--output-format", "csv", "-d",
+                       os.path.join(raw, "write_size"), "-o", "run", "--"] + bcmd,
+    }
+    meta_path = os.path.join(raw, "sources.json")
+    if not args.summarize_only:
+        with open(meta_path, "w") as f:
+            json.dump({ph: source_digest(ph) for ph in PHASE_SOURCES}, f)
+        for name, cmd in passes.items():
+            rc = _run(cmd, os.path.join(raw, name + ".log"), args.limit if name == "stats" else min(args.limit, 120))
+            if rc != 0:
+                return rc
+    with open(meta_path) as f:
+        digests = json.load(f)
+
+    def clean(t):
+        return t.replace(ROOT + "/", "").replace(args.raw, "gpurun_out/rocprof")
+
+    rows = read_stats(_find(os.path.join(raw, "stats"), "_kernel_stats.csv"))
+    txt = stats_text([top, "  which runs:", passes["stats"]], rows,
+                     _bench_json(os.path.join(raw, "stats.log")))
+    with open(os.path.join(args.out, f"kernels_{wl}.txt"), "w") as f:
+        f.write(clean(txt))
+    print(clean(txt), flush=True)
+
+    counters = {ctr: read_counter(_find(os.path.join(raw, ctr.lower()), "_counter_collection.csv"), ctr)
+                for ctr in ("FETCH_SIZE", "WRITE_SIZE")}
+    nbytes = COPY_MIB * 2**20
+    per, ff, fw = traffic_summary(counters["FETCH_SIZE"], counters["WRITE_SIZE"], nbytes)
+    from synthdata import SHAPES
+    B, N, d_, K, dt, _, _ = SHAPES[wl]
+    s = bench.elem_bytes(dt)
+    algo = {"assign": bench.assign_bytes(B, N, d_, K, s), "update": bench.update_bytes(B, N, d_, K, s)}
+    txt = traffic_text([top, "  which runs:", passes["fetch_size"], passes["write_size"]], per, ff, fw,
+                       nbytes, algo)
+    with open(os.path.join(args.out, f"traffic_{wl}.txt"), "w") as f:
+        f.write(clean(txt))
+    print(clean(txt), flush=True)
+
+    tpath = os.path.join(args.out, "traffic.json")
+    table = {}
+    for base in (os.path.join(ROOT, "profiles", "traffic.json"), tpath):   # keep other workloads
+        try:
+            with open(base) as f:
+                table.update(json.load(f))
+        except (OSError, ValueError):
+            pass
+    entry = {"factor_fetch": ff, "factor_write": fw}
+    for ph in ("assign", "update"):
+        rd = sum(v["read_bytes"] for v in per.values() if v["phase"] == ph)
+        wr = sum(v["write_bytes"] for v in per.values() if v["phase"] == ph)
+        entry[ph] = {"kernel_source_digest": digests[ph], "read_bytes": rd, "write_bytes": wr,
+                     "hbm_bytes_per_launch": rd + wr}
+    table[wl] = entry
+    with open(tpath, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
