@@ -105,11 +105,12 @@ hipError_t launch_assign_f32(const float* x, const float* c, const float* cnorm,
 
 // Sort-inverse update; workspace carved by the API layer.
 struct UpdateWs {
-  float* sums;        // (B,K,d) fp32
-  int32_t* offsets;   // (B,K+1) segment starts
-  int32_t* cursor;    // (B,K) scatter cursors
-  int32_t* perm;      // (B,N) point index per sorted position
-  float* part;        // (B, runs + finalize blocks) partial squared moves
+  float* sums;          // (B,K,d) fp32: short clusters' means, long clusters' sums
+  int32_t* offsets;     // (B,K+1) segment starts
+  int32_t* cursor;      // (B,K) scatter cursors (multi-block sort)
+  int32_t* perm;        // (B,N) point index per sorted position
+  int32_t* run_first;   // (B,runs) cluster holding each run's first position
+  float* part;          // (B, finalize blocks) partial squared moves
 };
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K);
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K);

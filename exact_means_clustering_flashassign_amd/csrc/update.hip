@@ -2,49 +2,65 @@
 //
 // The assignment vector is counting-sorted by cluster id into contiguous
 // segments through an inverse permutation of point indices; the point matrix
-// itself never moves. Each segment is then reduced on chip and each block
-// issues one atomic add per segment piece instead of one scatter atomic per
-// point (itinai.com summary, third paragraph; "Flash-KMeans：IO感知的精确
-// K-Means…", section "它攻克的两大瓶颈" and the update-contention panel of
+// itself never moves. Each segment is then reduced on chip, and a cluster
+// whose segment is longer than one run of sorted positions is summed in
+// pieces, with one atomic add per element per piece instead of one scatter
+// atomic per point (itinai.com summary, third paragraph; "Flash-KMeans：IO感知
+// 的精确K-Means…", section "它攻克的两大瓶颈" and the update-contention panel of
 // "交互式讲解"; "Flash-KMeans: Implementação Exata…", section "Sort-Inverse
 // Update"; "Flash-KMeans: Fast and Memory-Efficient Exact K-Means", Abstract).
 //
-// Steps (one launch each, all on the caller's stream):
-//   zero      counts and shift start at zero;
-//   hist      counts[b,k]: per-block LDS histogram, one global atomic per
-//             (block, non-empty bin);
-//   scan      offsets[b,0..K] = exclusive prefix sum of counts; cursor = copy;
-//             the fp32 sums of clusters that straddle a run (below) are zeroed;
-//   scatter   perm[b, offsets[id] + rank] = n: per-block LDS ranks, one
-//             cursor atomic per (block, non-empty bin);
-//   segreduce sums[b,k,:] = sum of x[b, perm[i], :] over segment k; each wave
-//             owns a fixed run of sorted positions (balanced by position, not
-//             by segment, so a hot cluster spreads over many waves); a segment
-//             lying wholly inside the run is finished by that wave
-//             (c = sum / count, its squared move added to the shift); a piece
-//             of a longer segment is added to sums with one fp32 atomic per
-//             element: at most (K + number of runs) * d atomics per problem;
-//   finalize_split  c = sums / count for the straddling clusters;
-//   shift_reduce    shift[b] = sum of the per-wave / per-block squared moves
-//             (partials in the workspace, summed in a fixed order).
-// Empty clusters are never touched, so they keep their centroid.
+// Terms. Sorted positions of a problem are cut into runs of kSegRun; the
+// segment [lo, hi) of cluster k is short when it holds at most kSegRun
+// positions, long otherwise.
+//
+// Steps:
+//   sort      counts, offsets (exclusive prefix sum of counts), perm
+//             (perm[offsets[id] + rank] = n) and, per run, the cluster that
+//             holds its first position. Long clusters get zeroed sums rows.
+//             Up to kSortOneBlockN points per problem: one 1024-thread block
+//             per problem does it all in LDS. Larger problems: hist (per-block
+//             LDS histograms + one global atomic per non-empty bin), scan,
+//             prep (run starts, zeroed rows) and scatter (LDS ranks + one
+//             cursor atomic per non-empty bin).
+//   segreduce one wave per (run, column slice). A short segment is summed
+//             whole by the wave whose run holds its first position (it may
+//             read up to kSegRun - 1 positions past its run) and finished in
+//             place: c = sum / count, squared move into the wave's partial.
+//             A long segment is summed piecewise, one piece per run it
+//             touches, into fp32 sums with one atomic per element: at most
+//             (number of long clusters + number of runs) * d atomics per
+//             problem, none at all when every cluster is short.
+//   finalize  long clusters: c = sums / count; squared moves into the
+//             block's partial; the last block of a problem to finish sums
+//             that problem's partials in a fixed order into shift[b].
+// Empty clusters are never touched, so they keep their centroid. Ids outside
+// [0, K) are skipped: they count nowhere and add to no cluster.
 #include "fk_internal.hpp"
 
 namespace fk {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxLdsBins = 32768;     // 128 KB of LDS bins per block
-constexpr int kSegRun = 256;           // sorted positions per wave in segreduce
+constexpr int kMaxLdsBins = 32768;            // 128 KB of LDS bins per block
+constexpr int kSegRun = 256;                  // sorted positions per segreduce run
+constexpr int kSortThreads = 1024;
+constexpr int kSortUnroll = 16;               // ids in flight per thread in the one-block sort
+constexpr int64_t kSortOneBlockN = 1 << 18;   // one sort block per problem up to this N
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+__device__ __forceinline__ bool is_long(int lo, int hi) { return hi - lo > kSegRun; }
+
+// Runs whose first position lies in [lo, hi) start inside cluster k.
+__device__ __forceinline__ void mark_runs(int32_t* rf, int k, int lo, int hi) {
+  for (int64_t r = (lo + (int64_t)kSegRun - 1) / kSegRun; r * kSegRun < hi; ++r) rf[r] = k;
+}
+
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void zero_kernel(int32_t* __restrict__ counts,
-                                                        int64_t ncounts) {
+__global__ __launch_bounds__(kThreads) void zero_kernel(int32_t* __restrict__ p, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (int64_t i = i0; i < ncounts; i += stride) counts[i] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0;
 }
 
 __global__ __launch_bounds__(kThreads) void fill_f32_kernel(float* __restrict__ p, float v,
@@ -53,7 +69,105 @@ __global__ __launch_bounds__(kThreads) void fill_f32_kernel(float* __restrict__ 
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
 }
 
+// Exclusive prefix sum over the kSortThreads threads of a block; `total`
+// receives the block sum. wtot: kSortThreads / 64 ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wtot, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kSortThreads / 64; ++i) {
+    const int t = wtot[i];
+    before += i < w ? t : 0;
+    all += t;
+  }
+  __syncthreads();
+  total = all;
+  return before + incl - v;
+}
+
 // ---------------------------------------------------------------------------
+// sort, one block per problem: LDS histogram, LDS scan, run starts, zeroed
+// rows of long clusters, then the inverse permutation with LDS ranks.
+__global__ __launch_bounds__(kSortThreads) void sort_kernel(
+    const int32_t* __restrict__ ids, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ run_first, float* __restrict__ sums, int N,
+    int K, int d, int runs) {
+  extern __shared__ int32_t bins[];            // K + 1
+  __shared__ int32_t wtot[kSortThreads / 64];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int32_t* ib = ids + (int64_t)b * N;
+  for (int i = t; i <= K; i += kSortThreads) bins[i] = 0;
+  __syncthreads();
+  // kSortUnroll ids per thread in flight per step
+  for (int n0 = 0; n0 < N; n0 += kSortThreads * kSortUnroll) {
+    int kk[kSortUnroll];
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q) {
+      const int n = n0 + q * kSortThreads + t;
+      kk[q] = n < N ? ib[n] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q)
+      if ((unsigned)kk[q] < (unsigned)K) atomicAdd(&bins[kk[q]], 1);
+  }
+  __syncthreads();
+  const int per = (K + kSortThreads - 1) / kSortThreads;
+  const int lo = min(t * per, K), hi = min(lo + per, K);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += bins[i];
+  int total;
+  int run = block_exclusive_scan(s, wtot, total);
+  int32_t* cb = counts + (int64_t)b * K;
+  int32_t* ob = offsets + (int64_t)b * (K + 1);
+  int32_t* rf = run_first + (int64_t)b * runs;
+  for (int i = lo; i < hi; ++i) {
+    const int c = bins[i];
+    cb[i] = c;
+    ob[i] = run;
+    bins[i] = run;
+    if (c > 0) mark_runs(rf, i, run, run + c);
+    run += c;
+  }
+  if (t == 0) {
+    ob[K] = total;
+    bins[K] = total;
+  }
+  for (int64_t r = (total + (int64_t)kSegRun - 1) / kSegRun + t; r < runs; r += kSortThreads)
+    rf[r] = K;                                   // runs past the last valid position
+  __syncthreads();
+  float* sb = sums + (int64_t)b * K * d;
+  for (int k = w; k < K; k += kSortThreads / 64) {
+    if (!is_long(bins[k], bins[k + 1])) continue;
+    float* row = sb + (int64_t)k * d;
+    for (int j = lane; j < d; j += 64) row[j] = 0.f;
+  }
+  __syncthreads();
+  int32_t* pb = perm + (int64_t)b * N;
+  for (int n0 = 0; n0 < N; n0 += kSortThreads * kSortUnroll) {
+    int kk[kSortUnroll];
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q) {
+      const int n = n0 + q * kSortThreads + t;
+      kk[q] = n < N ? ib[n] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q)
+      if ((unsigned)kk[q] < (unsigned)K)
+        pb[atomicAdd(&bins[kk[q]], 1)] = n0 + q * kSortThreads + t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-block sort for large problems.
 // hist: block (chunk, bin range, b). Bins of this range live in dynamic LDS.
 template <int IPT>
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ ids,
@@ -75,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
     const int n = n0 + q * kThreads + threadIdx.x;
     if (n < N) {
       const int k = ib[n] - k0;
-      if ((unsigned)k < (unsigned)nb) atomicAdd(&bins[k], 1);
+      if ((unsigned)k < (unsigned)nb && k0 + k < K) atomicAdd(&bins[k], 1);
     }
   }
   __syncthreads();
@@ -86,60 +200,59 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
   }
 }
 
-// ---------------------------------------------------------------------------
-// scan: one block per problem; exclusive prefix sum of counts. Also zeroes
-// the fp32 sums of clusters whose segment straddles a segreduce run.
-// A cluster's segment [lo, hi) of sorted positions straddles a segreduce run
-// boundary: it is then summed piecewise with atomics and finished in
-// finalize_split; otherwise one wave sums it and finishes it.
-__device__ __forceinline__ bool straddles(int lo, int hi) {
-  return hi > lo && lo / kSegRun != (hi - 1) / kSegRun;
-}
-
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ cursor,
-                                                    float* __restrict__ sums, int K, int d) {
-  __shared__ int32_t part[1024];
+// scan: one block per problem; offsets = exclusive prefix sum of counts,
+// cursor = offsets.
+__global__ __launch_bounds__(kSortThreads) void scan_kernel(const int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ cursor, int K) {
+  __shared__ int32_t wtot[kSortThreads / 64];
   const int b = blockIdx.x, t = threadIdx.x;
-  const int64_t per = ((int64_t)K + 1023) / 1024;
+  const int64_t per = ((int64_t)K + kSortThreads - 1) / kSortThreads;
   const int64_t lo = t * per < K ? t * per : K;
-  const int64_t hi = (t + 1) * per < K ? (t + 1) * per : K;
+  const int64_t hi = lo + per < K ? lo + per : K;
   const int32_t* cb = counts + (int64_t)b * K;
   int s = 0;
   for (int64_t i = lo; i < hi; ++i) s += cb[i];
-  part[t] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the 1024 partial sums
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
-  int run = t ? part[t - 1] : 0;
+  int total;
+  int run = block_exclusive_scan(s, wtot, total);
   int32_t* ob = offsets + (int64_t)b * (K + 1);
   int32_t* kb = cursor + (int64_t)b * K;
-  float* sbase = sums + (int64_t)b * K * d;
   for (int64_t i = lo; i < hi; ++i) {
     ob[i] = run;
     kb[i] = run;
-    const int next = run + cb[i];
-    if (straddles(run, next)) {      // its pieces are summed with atomics: start at zero
-      float* row = sbase + i * d;
-      if ((d & 3) == 0) {
-        float4* r4 = reinterpret_cast<float4*>(row);
-        for (int j = 0; j < d / 4; ++j) r4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      } else {
-        for (int j = 0; j < d; ++j) row[j] = 0.f;
-      }
-    }
-    run = next;
+    run += cb[i];
   }
-  if (t == 1023) ob[K] = part[1023];
+  if (t == 0) ob[K] = total;
 }
 
-// ---------------------------------------------------------------------------
+// prep: one wave per cluster marks the runs that start inside it and zeroes
+// the sums row of a long cluster; runs past the last position get K.
+__global__ __launch_bounds__(kThreads) void prep_kernel(const int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ run_first,
+                                                        float* __restrict__ sums, int K, int d,
+                                                        int runs, int blocks_per_batch) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int b = blockIdx.x / blocks_per_batch;
+  const int j = blockIdx.x % blocks_per_batch;
+  const int32_t* ob = offsets + (int64_t)b * (K + 1);
+  int32_t* rf = run_first + (int64_t)b * runs;
+  const int total = ob[K];
+  for (int k = j * (kThreads / 64) + wv; k < K; k += blocks_per_batch * (kThreads / 64)) {
+    const int lo = ob[k], hi = ob[k + 1];
+    if (hi <= lo) continue;
+    for (int64_t r = (lo + (int64_t)kSegRun - 1) / kSegRun + lane; r * kSegRun < hi; r += 64)
+      rf[r] = k;
+    if (is_long(lo, hi)) {
+      float* row = sums + ((int64_t)b * K + k) * d;
+      for (int i = lane; i < d; i += 64) row[i] = 0.f;
+    }
+  }
+  const int64_t r0 = (total + (int64_t)kSegRun - 1) / kSegRun;
+  for (int64_t r = r0 + (int64_t)j * kThreads + threadIdx.x; r < runs;
+       r += (int64_t)blocks_per_batch * kThreads)
+    rf[r] = K;
+}
+
 // scatter: perm[offset of cluster + rank] = n.
 template <int IPT>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __restrict__ ids,
@@ -165,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
     rank[q] = 0;
     if (n < N) {
       const int k = ib[n] - k0;
-      if ((unsigned)k < (unsigned)nb) {
+      if ((unsigned)k < (unsigned)nb && k0 + k < K) {
         key[q] = k;
         rank[q] = atomicAdd(&bins[k], 1);
       }
@@ -186,16 +299,22 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// segreduce: one wave per run of kSegRun sorted positions.
+// segreduce: one wave per (run, column slice).
 //
-// The wave stages its run of perm in LDS, then walks the segments that
-// intersect the run. Rows are read as 16-byte vectors: LPR lanes cover one
-// row (VPL vectors each), so a wave instruction reads 64/LPR rows and each
-// lane keeps U row-iterations of loads in flight. At the end of a piece the
-// row groups are summed with lane shuffles. A segment wholly inside the run
-// is finished here: c = sum / count, and its squared move is added to the
-// shift. A piece of a longer segment is added to `sums` with one fp32 atomic
-// per element; finalize_split completes those clusters.
+// The positions a wave owns form one contiguous range [s, E): the piece of a
+// long segment that covers the run's first position (if any), then every
+// segment that starts inside the run, the last of them possibly ending in the
+// next run (short) or cut at the run's end (long). The wave stages perm for
+// its run and the next one in LDS and lists its segments (cluster, end of its
+// rows, count) in three VGPRs, one segment per lane, 64 at a time. It then
+// streams [s, E) in batches of BR rows regardless of segment boundaries, with
+// the next batch's loads issued before the current batch is summed. Rows are
+// read as 16-byte vectors: LPR lanes cover the slice's SPAN columns of a row,
+// so one wave instruction reads R = 64/LPR rows. Inside a batch each
+// segment's rows are added under a 0/1 position weight; when a segment ends,
+// the R row groups are summed with lane shuffles and the sum goes to the
+// cluster's sums row: divided by the count for a short segment (the finished
+// mean), added with atomics for a piece of a long one.
 template <int DT>
 __device__ __forceinline__ void widen16(const uint4 v, float* out) {
   if constexpr (DT == FK_F32) {
@@ -213,169 +332,251 @@ __device__ __forceinline__ void widen16(const uint4 v, float* out) {
   }
 }
 
-template <int DT>
-__device__ __forceinline__ float load_elem(const void* x, int64_t i) {
-  if constexpr (DT == FK_F32) return reinterpret_cast<const float*>(x)[i];
-  else return Elem<DT>::widen(reinterpret_cast<const uint16_t*>(x)[i]);
-}
-
-template <int DT, int LPR, int VPL, bool VEC>
+template <int DT, int LPR, bool VEC>
 __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     const void* __restrict__ x, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ offsets, float* __restrict__ sums, float* __restrict__ c,
-    float* __restrict__ moved_part, int N, int d, int K, int runs_per_batch, int64_t total_runs,
-    int dbase, int parts_per_batch) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ run_first,
+    float* __restrict__ sums, int N, int d, int K, int runs, int slices, int64_t total_waves) {
   constexpr int R = 64 / LPR;                    // rows per wave instruction
   constexpr int EB = DT == FK_F32 ? 4 : 2;
   constexpr int EV = 16 / EB;                    // elements per 16-byte vector
-  constexpr int NE = VPL * EV;                   // elements per lane
-  constexpr int U = VPL >= 8 ? 1 : (VPL == 4 ? 2 : (VPL == 2 ? 4 : 8));
-  __shared__ int32_t lperm[kThreads / 64][kSegRun];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int SPAN = LPR * EV;                 // columns per slice
+  constexpr int U = 4;                           // row-iterations per batch
+  constexpr int BR = U * R;                      // rows per batch
+  constexpr int STAGE = 2 * kSegRun;
+  __shared__ int32_t lperm[kThreads / 64][STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int g = lane / LPR, li = lane % LPR;
   const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + wv;
-  if (wid >= total_runs) return;                 // whole wave; no block barrier follows
-  const int b = (int)(wid / runs_per_batch);
-  const int p0 = (int)(wid % runs_per_batch) * kSegRun;
-  const int p1 = p0 + kSegRun < N ? p0 + kSegRun : N;
+  if (wid >= total_waves) return;                // whole wave; no block barrier follows
+  const int per_batch = runs * slices;
+  const int b = (int)(wid / per_batch);
+  const int rem = (int)(wid % per_batch);
+  const int run = rem / slices, slice = rem % slices;
+  const int p0 = run * kSegRun;
+  const int p1 = min(p0 + kSegRun, N);
+  const int col = slice * SPAN + li * EV;        // my first column
+  const bool colok = col < d;
   const int32_t* ob = offsets + (int64_t)b * (K + 1);
-  const int32_t* pb = perm + (int64_t)b * N;
-  const int64_t xoff = (int64_t)b * N * d;
+  const char* xb = reinterpret_cast<const char*>(x) + (int64_t)b * N * d * EB;
   float* sb = sums + (int64_t)b * K * d;
-  float* cb = c + (int64_t)b * K * d;
 
-  for (int j = lane; j < p1 - p0; j += 64) lperm[wv][j] = pb[p0 + j];
+  int k = run_first[(int64_t)b * runs + run];
+  k = k < 0 ? K : k;
+  if (k >= K) return;
+  const int pend = min(p0 + STAGE, N);
+  for (int j = lane; j < pend - p0; j += 64) lperm[wv][j] = perm[(int64_t)b * N + p0 + j];
+
+  // offsets window: win holds ob[kw + lane]
+  int kw = k;
+  int win = ob[min(kw + lane, K)];
+  auto off = [&](int kk) {
+    if ((unsigned)(kk - kw) >= 64u) {            // outside the window (either side)
+      kw = kk;
+      win = ob[min(kw + lane, K)];
+    }
+    return __builtin_amdgcn_readlane(win, kk - kw);
+  };
+  // Segment list: lane i holds the (kk, end, count) of one owned segment.
+  // fill() lists up to 64 segments starting at cluster kk (whose rows begin
+  // at `start`) and returns how many; nxt receives where to continue (K: no
+  // more).
+  int sk = 0, se = 0, sc = 0;
+  auto fill = [&](int kk, int& nxt) {
+    int n = 0;
+    while (kk < K && n < 64) {
+      const int lo = off(kk);
+      if (lo >= p1) {
+        kk = K;
+        break;
+      }
+      const int hi = off(kk + 1);
+      if (hi > lo && (is_long(lo, hi) || lo >= p0)) {
+        const int end = is_long(lo, hi) ? min(hi, p1) : hi;
+        const int cnt = is_long(lo, hi) ? -(hi - lo) : hi - lo;   // negative: long
+        sk = lane == n ? kk : sk;
+        se = lane == n ? end : se;
+        sc = lane == n ? cnt : sc;
+        ++n;
+      }
+      ++kk;
+    }
+    nxt = kk;
+    return n;
+  };
+  int knext;
+  int nseg = fill(k, knext);
+  if (nseg == 0) return;
+  // first row: a long piece starts at max(lo, p0), a short segment at lo
+  const int c0 = __builtin_amdgcn_readlane(sc, 0);
+  const int s = c0 < 0 ? max(off(__builtin_amdgcn_readlane(sk, 0)), p0)
+                       : __builtin_amdgcn_readlane(se, 0) - c0;
+  // last row + 1: the end of the last owned segment
+  int E = __builtin_amdgcn_readlane(se, nseg - 1);
+  for (int kk = knext; kk < K; ++kk) {           // only with more than 64 segments
+    const int lo = off(kk);
+    if (lo >= p1) break;
+    const int hi = off(kk + 1);
+    if (hi > lo && (is_long(lo, hi) || lo >= p0)) E = is_long(lo, hi) ? min(hi, p1) : hi;
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // first cluster of the run: the last k with offsets[k] <= p0
-  int lo = 0, hi = K;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (__builtin_amdgcn_readfirstlane(ob[mid]) <= p0) lo = mid; else hi = mid - 1;
-  }
-  int k = lo;
+  // current segment: list entry si
+  int si = 0;
+  int jk = __builtin_amdgcn_readlane(sk, 0);
+  int jend = __builtin_amdgcn_readlane(se, 0);
+  int jcnt = __builtin_amdgcn_readlane(sc, 0);
+  int jstart = s;
+  float acc[EV];
+#pragma unroll
+  for (int i = 0; i < EV; ++i) acc[i] = 0.f;
 
-  int col[VPL];                                  // first element of each of my vectors
+  // Loads are unconditional (a position past E reads a valid staged row and
+  // gets weight 0), so the compiler can count them and keep the next batch in
+  // flight while this one is summed.
+  const int colc = colok ? col : 0;
+  auto load = [&](int base, uint4* v) {
 #pragma unroll
-  for (int q = 0; q < VPL; ++q) col[q] = dbase + (li + LPR * q) * EV;
-
-  float moved = 0.f;
-  int seg_lo = __builtin_amdgcn_readfirstlane(ob[k]);
-  while (seg_lo < p1) {
-    const int seg_hi = __builtin_amdgcn_readfirstlane(ob[k + 1]);
-    if (seg_hi > seg_lo) {
-      const int a = seg_lo > p0 ? seg_lo : p0;
-      const int e = seg_hi < p1 ? seg_hi : p1;
-      float acc[NE];
+    for (int u = 0; u < U; ++u) {
+      const int p = min(base + u * R + g, E - 1);
+      const int64_t row = (int64_t)lperm[wv][p - p0] * d;
+      if constexpr (VEC) {
+        v[u] = *reinterpret_cast<const uint4*>(xb + (row + colc) * EB);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < NE; ++i) acc[i] = 0.f;
-      for (int base = a; base < e; base += U * R) {
-        int n[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int p = base + u * R + g;
-          n[u] = p < e ? lperm[wv][p - p0] : -1;
+        for (int i = 0; i < EV; ++i) {
+          const int64_t e = row + (colc + i < d ? colc + i : 0);
+          uint32_t bits;
+          if constexpr (DT == FK_F32) bits = reinterpret_cast<const uint32_t*>(xb)[e];
+          else bits = reinterpret_cast<const uint16_t*>(xb)[e];
+          if constexpr (DT == FK_F32) w[i] = bits;
+          else w[i / 2] |= bits << (16 * (i & 1));
         }
-        if constexpr (VEC) {
-          uint4 v[U][VPL];
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int q = 0; q < VPL; ++q) {
-              const bool ok = n[u] >= 0 && col[q] < d;
-              const int64_t idx = xoff + (int64_t)(ok ? n[u] : 0) * d + (ok ? col[q] : 0);
-              v[u][q] = ok ? *reinterpret_cast<const uint4*>(
-                                 reinterpret_cast<const char*>(x) + idx * EB)
-                           : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int q = 0; q < VPL; ++q) {
-              float f[EV];
-              widen16<DT>(v[u][q], f);
-#pragma unroll
-              for (int i = 0; i < EV; ++i) acc[q * EV + i] += f[i];
-            }
-        } else {
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            if (n[u] < 0) continue;
-            const int64_t row = xoff + (int64_t)n[u] * d;
-#pragma unroll
-            for (int q = 0; q < VPL; ++q)
-#pragma unroll
-              for (int i = 0; i < EV; ++i)
-                if (col[q] + i < d) acc[q * EV + i] += load_elem<DT>(x, row + col[q] + i);
-          }
-        }
-      }
-      // sum the R row groups
-#pragma unroll
-      for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-        for (int i = 0; i < NE; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
-      const bool whole = seg_lo >= p0 && seg_hi <= p1;
-      if (g == 0) {
-        const float cnt = (float)(seg_hi - seg_lo);
-#pragma unroll
-        for (int q = 0; q < VPL; ++q)
-#pragma unroll
-          for (int i = 0; i < EV; ++i) {
-            const int j = col[q] + i;
-            if (j < d) {
-              const int64_t o = (int64_t)k * d + j;
-              if (whole) {
-                const float nw = acc[q * EV + i] / cnt;
-                const float dl = nw - cb[o];
-                cb[o] = nw;
-                moved = fmaf(dl, dl, moved);
-              } else {
-                unsafeAtomicAdd(sb + o, acc[q * EV + i]);
-              }
-            }
-          }
+        v[u] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
-    ++k;
-    if (k >= K) break;
-    seg_lo = seg_hi;
-  }
-  // this wave's share of the shift; several d passes accumulate in order
-  moved = wave_sum(moved);
-  if (lane == 0) {
-    float* slot = moved_part + (int64_t)b * parts_per_batch + (wid % runs_per_batch);
-    *slot = dbase == 0 ? moved : *slot + moved;
+  };
+  auto flush = [&]() {
+#pragma unroll
+    for (int sh = LPR; sh < 64; sh <<= 1)
+#pragma unroll
+      for (int i = 0; i < EV; ++i) acc[i] += __shfl_xor(acc[i], sh, 64);
+    if (g == 0 && colok) {
+      float* row = sb + (int64_t)jk * d + col;
+      if (jcnt > 0) {
+        const float cnt = (float)jcnt;
+#pragma unroll
+        for (int i = 0; i < EV; ++i)
+          if (col + i < d) row[i] = acc[i] / cnt;
+      } else {
+#pragma unroll
+        for (int i = 0; i < EV; ++i)
+          if (col + i < d) unsafeAtomicAdd(row + i, acc[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < EV; ++i) acc[i] = 0.f;
+  };
+  // sum one batch of rows [base, base + BR)
+  auto consume = [&](int base, const uint4* v) {
+    const int bend = min(base + BR, E);
+    for (;;) {
+      const int r0 = max(jstart, base), r1 = min(jend, bend);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = base + u * R + g;
+        const float m = (p >= r0 && p < r1) ? 1.f : 0.f;
+        float f[EV];
+        widen16<DT>(v[u], f);
+#pragma unroll
+        for (int i = 0; i < EV; ++i) acc[i] = fmaf(f[i], m, acc[i]);
+      }
+      if (jend > bend) return;                   // segment continues in the next batch
+      flush();
+      if (jend >= E) return;                     // owned range done
+      ++si;
+      if (si == nseg) {                          // refill the list (more than 64 segments)
+        nseg = fill(knext, knext);
+        si = 0;
+      }
+      jstart = jend;
+      jk = __builtin_amdgcn_readlane(sk, si);
+      jend = __builtin_amdgcn_readlane(se, si);
+      jcnt = __builtin_amdgcn_readlane(sc, si);
+      if (jstart >= bend) return;                // next segment starts in the next batch
+    }
+  };
+  // two batches in flight: the loads of the batch after next are issued
+  // before a batch is summed (past E they re-read a staged row and get
+  // weight 0)
+  uint4 va[U], vb[U];
+  load(s, va);
+  for (int base = s; base < E; base += 2 * BR) {
+    load(base + BR, vb);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(base, va);
+    load(base + 2 * BR, va);
+    __builtin_amdgcn_sched_barrier(0);
+    if (base + BR < E) consume(base + BR, vb);
   }
 }
 
 // ---------------------------------------------------------------------------
-// finalize_split: clusters whose segment straddles a run boundary. Block j of
-// problem b scans rows j*4+w, j*4+w+4*fb, ... (w = wave); straddling rows get
-// c = sums / count; the block's squared moves go to its partial slot.
-constexpr int kFinBlocks = 64;   // blocks per problem (at most)
+// finalize, one thread per group of kFinVec consecutive elements of a
+// problem's (K, d) centroid block: a non-empty cluster takes its new value
+// from its sums row (already the mean for a short segment; divided by the
+// count for a long one), and the block's squared moves go to its partial.
+// Empty clusters keep their centroid.
+constexpr int kFinVec = 4;
 
-__global__ __launch_bounds__(kThreads) void finalize_split_kernel(
+__global__ __launch_bounds__(kThreads) void finalize_kernel(
     const float* __restrict__ sums, const int32_t* __restrict__ offsets, float* __restrict__ c,
-    float* __restrict__ moved_part, int d, int K, int fb, int parts_per_batch, int part0) {
+    float* __restrict__ part, int d, int K, int blocks_per_batch, bool vec) {
   __shared__ float wsum[kThreads / 64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int b = blockIdx.x / fb, j = blockIdx.x % fb;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.x / blocks_per_batch, j = blockIdx.x % blocks_per_batch;
+  const int64_t per = (int64_t)K * d;
+  const int64_t e0 = ((int64_t)j * kThreads + threadIdx.x) * kFinVec;
   const int32_t* ob = offsets + (int64_t)b * (K + 1);
+  const float* sb = sums + (int64_t)b * per;
+  float* cb = c + (int64_t)b * per;
   float moved = 0.f;
-  for (int k = j * (kThreads / 64) + wv; k < K; k += fb * (kThreads / 64)) {
-    const int lo = ob[k], hi = ob[k + 1];
-    if (!straddles(lo, hi)) continue;
-    const float cnt = (float)(hi - lo);
-    const float* srow = sums + ((int64_t)b * K + k) * d;
-    float* crow = c + ((int64_t)b * K + k) * d;
-    for (int i = lane; i < d; i += 64) {
-      const float nw = srow[i] / cnt;
-      const float dl = nw - crow[i];
-      crow[i] = nw;
-      moved = fmaf(dl, dl, moved);
+  if (e0 < per) {
+    if (vec && e0 + kFinVec <= per) {         // vec: d % kFinVec == 0, c 16-byte aligned
+      const int k = (int)(e0 / d);               // the kFinVec elements share a row
+      const int lo = ob[k], hi = ob[k + 1];
+      if (hi > lo) {
+        const float4 sv = *reinterpret_cast<const float4*>(sb + e0);
+        float4 cv = *reinterpret_cast<const float4*>(cb + e0);
+        const float cnt = (float)(hi - lo);
+        const bool lng = is_long(lo, hi);
+        float nw[4] = {sv.x, sv.y, sv.z, sv.w};
+        const float od[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          nw[i] = lng ? nw[i] / cnt : nw[i];
+          const float dl = nw[i] - od[i];
+          moved = fmaf(dl, dl, moved);
+        }
+        cv = make_float4(nw[0], nw[1], nw[2], nw[3]);
+        *reinterpret_cast<float4*>(cb + e0) = cv;
+      }
+    } else {
+      for (int64_t e = e0; e < e0 + kFinVec && e < per; ++e) {
+        const int k = (int)(e / d);
+        const int lo = ob[k], hi = ob[k + 1];
+        if (hi <= lo) continue;
+        const float sv = sb[e];
+        const float nw = is_long(lo, hi) ? sv / (float)(hi - lo) : sv;
+        const float dl = nw - cb[e];
+        cb[e] = nw;
+        moved = fmaf(dl, dl, moved);
+      }
     }
   }
   moved = wave_sum(moved);
@@ -385,11 +586,11 @@ __global__ __launch_bounds__(kThreads) void finalize_split_kernel(
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
-    moved_part[(int64_t)b * parts_per_batch + part0 + j] = t;
+    part[(int64_t)b * blocks_per_batch + j] = t;
   }
 }
 
-// shift[b] = sum of the problem's partials (fixed order: deterministic).
+// shift[b] = sum of the problem's finalize partials, in index order.
 __global__ __launch_bounds__(kThreads) void shift_reduce_kernel(const float* __restrict__ part,
                                                                 float* __restrict__ shift,
                                                                 int parts_per_batch) {
@@ -448,74 +649,78 @@ hipError_t run_hist_scatter(const int32_t* ids, int32_t* counts, int32_t* cursor
   return hipGetLastError();
 }
 
-template <int DT, int LPR, int VPL>
-hipError_t run_segreduce(const void* x, const int32_t* perm, const int32_t* offsets, float* sums,
-                         float* c, float* part, int parts, int64_t B, int64_t N, int64_t d,
-                         int64_t K, hipStream_t s) {
-  constexpr int EB = DT == FK_F32 ? 4 : 2;
-  constexpr int span = LPR * VPL * (16 / EB);    // elements covered per pass
-  const int runs = (int)((N + kSegRun - 1) / kSegRun);
-  const int64_t total = B * runs;
-  const int64_t grid = (total + 3) / 4;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const bool vec = (d * EB) % 16 == 0 && ((uintptr_t)x % 16) == 0;
-  for (int64_t db = 0; db < d; db += span) {
-    if (vec)
-      segreduce_kernel<DT, LPR, VPL, true><<<(unsigned)grid, kThreads, 0, s>>>(
-          x, perm, offsets, sums, c, part, (int)N, (int)d, (int)K, runs, total, (int)db, parts);
-    else
-      segreduce_kernel<DT, LPR, VPL, false><<<(unsigned)grid, kThreads, 0, s>>>(
-          x, perm, offsets, sums, c, part, (int)N, (int)d, (int)K, runs, total, (int)db, parts);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-// Lanes per row: enough 16-byte vectors to cover the row, as a power of two;
-// rows wider than 64 vectors take VPL vectors per lane (several passes above
-// 64*8 vectors).
-template <int DT>
-hipError_t segreduce_dt(const void* x, const int32_t* perm, const int32_t* offsets, float* sums,
-                        float* c, float* part, int parts, int64_t B, int64_t N, int64_t d,
-                        int64_t K, hipStream_t s) {
-  constexpr int EV = DT == FK_F32 ? 4 : 8;
-  const int64_t nvec = (d + EV - 1) / EV;
-#define FK_SEG(L, V) \
-  run_segreduce<DT, L, V>(x, perm, offsets, sums, c, part, parts, B, N, d, K, s)
-  if (nvec <= 4) return FK_SEG(4, 1);
-  if (nvec <= 8) return FK_SEG(8, 1);
-  if (nvec <= 16) return FK_SEG(16, 1);
-  if (nvec <= 32) return FK_SEG(32, 1);
-  if (nvec <= 64) return FK_SEG(64, 1);
-  if (nvec <= 128) return FK_SEG(64, 2);
-  if (nvec <= 256) return FK_SEG(64, 4);
-  return FK_SEG(64, 8);
-#undef FK_SEG
-}
-
 #define FK_CHECK(call)                   \
   do {                                   \
     hipError_t e_ = (call);              \
     if (e_ != hipSuccess) return e_;     \
   } while (0)
 
-}  // namespace
-
-int fin_blocks(int64_t K) {
-  const int64_t fb = (K + 63) / 64;
-  return (int)(fb < kFinBlocks ? fb : kFinBlocks);
+// Lanes per row slice: enough 16-byte vectors for the row, as a power of two,
+// at most 16 (a 256-byte slice); wider rows are cut into column slices, each
+// its own wave, so a problem with few points still fills the machine.
+template <int DT>
+int seg_lanes(int64_t d) {
+  constexpr int EV = DT == FK_F32 ? 4 : 8;
+  const int64_t nvec = (d + EV - 1) / EV;
+  int l = 4;
+  while (l < 16 && l < nvec) l <<= 1;
+  return l;
 }
 
-int64_t shift_parts(int64_t N, int64_t K) { return (N + kSegRun - 1) / kSegRun + fin_blocks(K); }
+template <int DT>
+int seg_slices_dt(int64_t d) {
+  constexpr int EV = DT == FK_F32 ? 4 : 8;
+  const int64_t span = (int64_t)seg_lanes<DT>(d) * EV;
+  return (int)((d + span - 1) / span);
+}
+
+template <int DT, int LPR>
+hipError_t run_segreduce(const void* x, const UpdateWs& ws, int64_t B, int64_t N, int64_t d,
+                         int64_t K, hipStream_t s) {
+  constexpr int EB = DT == FK_F32 ? 4 : 2;
+  const int runs = (int)((N + kSegRun - 1) / kSegRun);
+  const int slices = seg_slices_dt<DT>(d);
+  const int64_t total = B * runs * slices;
+  const int64_t grid = (total + 3) / 4;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const bool vec = (d * EB) % 16 == 0 && ((uintptr_t)x % 16) == 0;
+  if (vec)
+    segreduce_kernel<DT, LPR, true><<<(unsigned)grid, kThreads, 0, s>>>(
+        x, ws.perm, ws.offsets, ws.run_first, ws.sums, (int)N, (int)d, (int)K, runs, slices,
+        total);
+  else
+    segreduce_kernel<DT, LPR, false><<<(unsigned)grid, kThreads, 0, s>>>(
+        x, ws.perm, ws.offsets, ws.run_first, ws.sums, (int)N, (int)d, (int)K, runs, slices,
+        total);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t segreduce_dt(const void* x, const UpdateWs& ws, int64_t B, int64_t N, int64_t d,
+                        int64_t K, hipStream_t s) {
+  switch (seg_lanes<DT>(d)) {
+    case 4: return run_segreduce<DT, 4>(x, ws, B, N, d, K, s);
+    case 8: return run_segreduce<DT, 8>(x, ws, B, N, d, K, s);
+    default: return run_segreduce<DT, 16>(x, ws, B, N, d, K, s);
+  }
+}
+
+}  // namespace
+
+// finalize blocks per problem: one thread per kFinVec centroid elements
+int64_t fin_blocks(int64_t K, int64_t d) {
+  return (K * d + (int64_t)kThreads * kFinVec - 1) / ((int64_t)kThreads * kFinVec);
+}
 
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K) {
+  const int64_t runs = (N + kSegRun - 1) / kSegRun;
   return align256((size_t)B * K * d * 4) + align256((size_t)B * (K + 1) * 4) +
          align256((size_t)B * K * 4) + align256((size_t)B * N * 4) +
-         align256((size_t)B * shift_parts(N, K) * 4);
+         align256((size_t)B * runs * 4) + align256((size_t)B * fin_blocks(K, d) * 4);
 }
 
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K) {
+  const int64_t runs = (N + kSegRun - 1) / kSegRun;
   char* p = static_cast<char*>(base);
   UpdateWs w;
   w.sums = reinterpret_cast<float*>(p);
@@ -526,6 +731,8 @@ UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K)
   p += align256((size_t)B * K * 4);
   w.perm = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)B * N * 4);
+  w.run_first = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)B * runs * 4);
   w.part = reinterpret_cast<float*>(p);
   return w;
 }
@@ -534,52 +741,65 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
                          int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
                          const UpdateWs& ws, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  const int parts = (int)shift_parts(N, K);
-  const int runs = (int)((N + kSegRun - 1) / kSegRun);
-  const int fb = fin_blocks(K);
-  {
+  if (N == 0) {
+    // no point: every cluster is empty and keeps its centroid
     int64_t g = (B * K + kThreads - 1) / kThreads;
     g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
     zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
     FK_CHECK(hipGetLastError());
+    fill_f32_kernel<<<1, kThreads, 0, s>>>(shift, 0.f, B);
+    return hipGetLastError();
   }
-  if (N > 0) {
+  const int runs = (int)((N + kSegRun - 1) / kSegRun);
+  const int64_t fb = fin_blocks(K, d);
+  if (N <= kSortOneBlockN && K <= kMaxLdsBins - 1) {
+    const size_t lds = (size_t)(K + 1) * sizeof(int32_t);
+    static bool attr = false;
+    if (!attr && lds > 65536) {
+      (void)hipFuncSetAttribute((const void*)sort_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kMaxLdsBins * sizeof(int32_t));
+      (void)hipGetLastError();
+      attr = true;
+    }
+    sort_kernel<<<(unsigned)B, kSortThreads, lds, s>>>(ids, counts, ws.offsets, ws.perm,
+                                                       ws.run_first, ws.sums, (int)N,
+                                                       (int)K, (int)d, runs);
+    FK_CHECK(hipGetLastError());
+  } else {
+    int64_t g = (B * K + kThreads - 1) / kThreads;
+    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+    zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
+    FK_CHECK(hipGetLastError());
     if (K <= 4096)
       FK_CHECK(run_hist_scatter<16>(ids, counts, nullptr, nullptr, B, N, K, false, s));
     else
       FK_CHECK(run_hist_scatter<64>(ids, counts, nullptr, nullptr, B, N, K, false, s));
-    scan_kernel<<<(unsigned)B, 1024, 0, s>>>(counts, ws.offsets, ws.cursor, ws.sums, (int)K,
-                                             (int)d);
+    scan_kernel<<<(unsigned)B, kSortThreads, 0, s>>>(counts, ws.offsets, ws.cursor, (int)K);
+    FK_CHECK(hipGetLastError());
+    const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);   // blocks per problem
+    prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.sums,
+                                                         (int)K, (int)d, runs, pb);
     FK_CHECK(hipGetLastError());
     if (K <= 4096)
       FK_CHECK(run_hist_scatter<16>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
     else
       FK_CHECK(run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
-    if (dt == FK_F16)
-      FK_CHECK(segreduce_dt<FK_F16>(x, ws.perm, ws.offsets, ws.sums, c, ws.part, parts, B, N, d,
-                                    K, s));
-    else if (dt == FK_BF16)
-      FK_CHECK(segreduce_dt<FK_BF16>(x, ws.perm, ws.offsets, ws.sums, c, ws.part, parts, B, N,
-                                     d, K, s));
-    else
-      FK_CHECK(segreduce_dt<FK_F32>(x, ws.perm, ws.offsets, ws.sums, c, ws.part, parts, B, N, d,
-                                    K, s));
-    const int64_t grid = B * fb;
-    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    finalize_split_kernel<<<(unsigned)grid, kThreads, 0, s>>>(ws.sums, ws.offsets, c, ws.part,
-                                                              (int)d, (int)K, fb, parts, runs);
-    FK_CHECK(hipGetLastError());
-  } else {
-    // no point: every cluster is empty and keeps its centroid; zero the partials
-    const int64_t n = B * parts;
-    int64_t g = (n + kThreads - 1) / kThreads;
-    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
-    fill_f32_kernel<<<(unsigned)g, kThreads, 0, s>>>(ws.part, 0.f, n);
-    FK_CHECK(hipGetLastError());
   }
-  shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, parts);
+  if (dt == FK_F16)
+    FK_CHECK(segreduce_dt<FK_F16>(x, ws, B, N, d, K, s));
+  else if (dt == FK_BF16)
+    FK_CHECK(segreduce_dt<FK_BF16>(x, ws, B, N, d, K, s));
+  else
+    FK_CHECK(segreduce_dt<FK_F32>(x, ws, B, N, d, K, s));
+  const int64_t grid = B * fb;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const bool fvec = d % kFinVec == 0 && ((uintptr_t)c % 16) == 0;
+  finalize_kernel<<<(unsigned)grid, kThreads, 0, s>>>(ws.sums, ws.offsets, c, ws.part, (int)d,
+                                                      (int)K, (int)fb, fvec);
   FK_CHECK(hipGetLastError());
-  return hipSuccess;
+  shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, (int)fb);
+  return hipGetLastError();
 }
 
 }  // namespace fk

@@ -55,12 +55,14 @@ def test_status_strings(lib):
 def test_workspace_size(lib):
     ws = lib.fk_workspace_size
     big = ws(1, 32, 75600, 128, 1000)
-    # sums, offsets, cursor, perm, shift partials (one per 256 sorted positions
-    # and per finalize block), rounded centroids, norms, counts, shift
-    parts = -(-75600 // 256) + min(-(-1000 // 64), 64)
+    # sums, offsets, cursor, perm, run starts (one per 256 sorted positions),
+    # shift partials (one per finalize block of 1024 centroid elements),
+    # rounded centroids, norms, counts, shift
+    runs = -(-75600 // 256)
+    fb = -(-1000 * 128 // 1024)
     need = 32 * 1000 * 128 * 4 + 32 * 1001 * 4 + 32 * 1000 * 4 + 32 * 75600 * 4 + \
-        32 * parts * 4 + 32 * 1000 * 128 * 2 + 32 * 1000 * 4 * 2 + 32 * 4
-    assert need <= big <= need + 9 * 256
+        32 * runs * 4 + 32 * fb * 4 + 32 * 1000 * 128 * 2 + 32 * 1000 * 4 * 2 + 32 * 4
+    assert need <= big <= need + 10 * 256
     assert ws(1, 32, 75600, 128, 1000) < ws(0, 32, 75600, 128, 1000)   # fp32 copy is larger
     for bad in [(7, 1, 10, 4, 2), (1, -1, 10, 4, 2), (1, 1, -1, 4, 2), (1, 1, 10, 0, 2),
                 (1, 1, 10, 4, 0), (1, 1, 1 << 31, 4, 2), (1, 1, 10, 4, 1 << 31)]:
