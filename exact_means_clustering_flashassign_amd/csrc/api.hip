@@ -184,7 +184,9 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
     if (e == hipErrorNotSupported || e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
     if (e != hipSuccess) return FK_ERR_HIP;
     if (tr && hipEventRecord(trace_event(slot, 2), stream) != hipSuccess) return FK_ERR_HIP;
-    e = fk::launch_update(x, ids, dt, B, N, d, K, centers, w.counts, w.shift, w.upd, stream);
+    // the shift is only read for the tol test
+    e = fk::launch_update(x, ids, dt, B, N, d, K, centers, w.counts, tol > 0.f ? w.shift : nullptr,
+                          w.upd, stream);
     if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
     if (e != hipSuccess) return FK_ERR_HIP;
     if (tr) {

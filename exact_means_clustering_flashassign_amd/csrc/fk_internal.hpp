@@ -111,9 +111,11 @@ struct UpdateWs {
   int32_t* perm;        // (B,N) point index per sorted position
   int32_t* run_first;   // (B,runs) cluster holding each run's first position
   float* part;          // (B, finalize blocks) partial squared moves
+  int32_t* hist;        // (B, G, K) per-chunk counts of the split sort
 };
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K);
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K);
+// shift may be null: the new centroids are written and no shift is computed.
 hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, int64_t N,
                          int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
                          const UpdateWs& ws, hipStream_t s);

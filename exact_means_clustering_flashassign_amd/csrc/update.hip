@@ -17,12 +17,11 @@
 // Steps:
 //   sort      counts, offsets (exclusive prefix sum of counts), perm
 //             (perm[offsets[id] + rank] = n) and, per run, the cluster that
-//             holds its first position. Long clusters get zeroed sums rows.
-//             Up to kSortOneBlockN points per problem: one 1024-thread block
-//             per problem does it all in LDS. Larger problems: hist (per-block
-//             LDS histograms + one global atomic per non-empty bin), scan,
-//             prep (run starts, zeroed rows) and scatter (LDS ranks + one
-//             cursor atomic per non-empty bin).
+//             holds its first position; long clusters get zeroed sums rows.
+//             Split sort (K <= 32768): per-chunk LDS histograms into a count
+//             matrix, column prefixes and offsets, then LDS-ranked scatter;
+//             no global atomics. Larger K: per-range LDS histograms with one
+//             global atomic per non-empty bin, scan, prep, scatter.
 //   segreduce one wave per (run, column slice). A short segment is summed
 //             whole by the wave whose run holds its first position (it may
 //             read up to kSegRun - 1 positions past its run) and finished in
@@ -45,8 +44,8 @@ constexpr int kThreads = 256;
 constexpr int kMaxLdsBins = 32768;            // 128 KB of LDS bins per block
 constexpr int kSegRun = 256;                  // sorted positions per segreduce run
 constexpr int kSortThreads = 1024;
-constexpr int kSortUnroll = 16;               // ids in flight per thread in the one-block sort
-constexpr int64_t kSortOneBlockN = 1 << 18;   // one sort block per problem up to this N
+constexpr int kSortUnroll = 16;               // ids in flight per thread in the sort kernels
+constexpr int64_t kFusedOffsetsMax = 1 << 16; // G*K up to this: one offsets block per problem
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -94,80 +93,155 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wtot, int& t
 }
 
 // ---------------------------------------------------------------------------
-// sort, one block per problem: LDS histogram, LDS scan, run starts, zeroed
-// rows of long clusters, then the inverse permutation with LDS ranks.
-__global__ __launch_bounds__(kSortThreads) void sort_kernel(
-    const int32_t* __restrict__ ids, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ run_first, float* __restrict__ sums, int N,
-    int K, int d, int runs) {
-  extern __shared__ int32_t bins[];            // K + 1
-  __shared__ int32_t wtot[kSortThreads / 64];
-  const int b = blockIdx.x, t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
-  const int32_t* ib = ids + (int64_t)b * N;
-  for (int i = t; i <= K; i += kSortThreads) bins[i] = 0;
+// Split sort (K <= kMaxLdsBins): each problem's ids are cut into G chunks, one
+// block each.
+//   hist2    block (b, g): LDS histogram of its chunk, stored as row g of the
+//            problem's (G, K) count matrix H (no global atomics);
+//   offsets  per problem: H's columns become exclusive prefix sums over g,
+//            their totals are the counts, whose exclusive prefix sum gives
+//            the segment offsets; also the run starts and zeroed sums rows of
+//            long clusters (one block per problem when G*K is small;
+//            colscan + scan + prep otherwise);
+//   scatter2 block (b, g): LDS cursors offsets[k] + H[g][k], LDS ranks,
+//            perm[cursor] = n.
+__global__ __launch_bounds__(kSortThreads) void hist2_kernel(const int32_t* __restrict__ ids,
+                                                             int32_t* __restrict__ H, int N, int K,
+                                                             int G, int chunk) {
+  extern __shared__ int32_t bins[];
+  const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
+  for (int i = t; i < K; i += kSortThreads) bins[i] = 0;
   __syncthreads();
-  // kSortUnroll ids per thread in flight per step
-  for (int n0 = 0; n0 < N; n0 += kSortThreads * kSortUnroll) {
+  const int32_t* ib = ids + (int64_t)b * N;
+  const int n0 = g * chunk, n1 = min(n0 + chunk, N);
+  for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
     int kk[kSortUnroll];
 #pragma unroll
     for (int q = 0; q < kSortUnroll; ++q) {
-      const int n = n0 + q * kSortThreads + t;
-      kk[q] = n < N ? ib[n] : -1;
+      const int n = m + q * kSortThreads + t;
+      kk[q] = n < n1 ? ib[n] : -1;
     }
 #pragma unroll
     for (int q = 0; q < kSortUnroll; ++q)
       if ((unsigned)kk[q] < (unsigned)K) atomicAdd(&bins[kk[q]], 1);
   }
   __syncthreads();
+  int32_t* hr = H + ((int64_t)b * G + g) * K;
+  for (int i = t; i < K; i += kSortThreads) hr[i] = bins[i];
+}
+
+// Column k of a problem's H: exclusive prefix over g in place; returns the total.
+__device__ __forceinline__ int column_prefix(int32_t* hb, int64_t K, int G, int k) {
+  int run = 0;
+  int g = 0;
+  for (; g + 8 <= G; g += 8) {
+    int v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = hb[(g + q) * K + k];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      hb[(g + q) * K + k] = run;
+      run += v[q];
+    }
+  }
+  for (; g < G; ++g) {
+    const int v = hb[g * K + k];
+    hb[g * K + k] = run;
+    run += v;
+  }
+  return run;
+}
+
+// offsets: G > 0: column prefixes of H and counts first, then offsets, run
+// starts and zeroed long rows; G == 0: counts given, offsets only.
+__global__ __launch_bounds__(kSortThreads) void offsets_kernel(
+    int32_t* __restrict__ H, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ run_first, float* __restrict__ sums, int K, int d, int G, int runs) {
+  extern __shared__ int32_t cnt[];              // K + 1
+  __shared__ int32_t wtot[kSortThreads / 64];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  int32_t* hb = H + (int64_t)b * G * K;
+  int32_t* cb = counts + (int64_t)b * K;
+  if (G > 0) {
+    for (int k = t; k < K; k += kSortThreads) cnt[k] = column_prefix(hb, K, G, k);
+  } else {
+    for (int k0 = t; k0 < K; k0 += kSortThreads * 8) {   // 8 loads in flight per thread
+      int v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = k0 + q * kSortThreads < K ? cb[k0 + q * kSortThreads] : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (k0 + q * kSortThreads < K) cnt[k0 + q * kSortThreads] = v[q];
+    }
+  }
+  __syncthreads();
   const int per = (K + kSortThreads - 1) / kSortThreads;
   const int lo = min(t * per, K), hi = min(lo + per, K);
   int s = 0;
-  for (int i = lo; i < hi; ++i) s += bins[i];
+  for (int i = lo; i < hi; ++i) s += cnt[i];
   int total;
   int run = block_exclusive_scan(s, wtot, total);
-  int32_t* cb = counts + (int64_t)b * K;
   int32_t* ob = offsets + (int64_t)b * (K + 1);
   int32_t* rf = run_first + (int64_t)b * runs;
   for (int i = lo; i < hi; ++i) {
-    const int c = bins[i];
-    cb[i] = c;
-    ob[i] = run;
-    bins[i] = run;
-    if (c > 0) mark_runs(rf, i, run, run + c);
+    const int c = cnt[i];
+    if (G > 0) cb[i] = c;
+    cnt[i] = run;
+    if (G > 0 && c > 0) mark_runs(rf, i, run, run + c);
     run += c;
   }
-  if (t == 0) {
-    ob[K] = total;
-    bins[K] = total;
-  }
+  if (t == 0) cnt[K] = total;
+  __syncthreads();
+  for (int k = t; k <= K; k += kSortThreads) ob[k] = cnt[k];   // coalesced
+  if (G == 0) return;                            // run starts and rows: prep_kernel
   for (int64_t r = (total + (int64_t)kSegRun - 1) / kSegRun + t; r < runs; r += kSortThreads)
     rf[r] = K;                                   // runs past the last valid position
-  __syncthreads();
   float* sb = sums + (int64_t)b * K * d;
   for (int k = w; k < K; k += kSortThreads / 64) {
-    if (!is_long(bins[k], bins[k + 1])) continue;
+    if (!is_long(cnt[k], cnt[k + 1])) continue;
     float* row = sb + (int64_t)k * d;
     for (int j = lane; j < d; j += 64) row[j] = 0.f;
   }
+}
+
+// Large G*K: column prefixes on a grid, one thread per (problem, cluster).
+__global__ __launch_bounds__(kThreads) void colscan_kernel(int32_t* __restrict__ H,
+                                                           int32_t* __restrict__ counts, int K,
+                                                           int G, int kblocks) {
+  const int b = blockIdx.x / kblocks;
+  const int k = (blockIdx.x % kblocks) * kThreads + threadIdx.x;
+  if (k >= K) return;
+  counts[(int64_t)b * K + k] = column_prefix(H + (int64_t)b * G * K, K, G, k);
+}
+
+__global__ __launch_bounds__(kSortThreads) void scatter2_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ H,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int N, int K, int G,
+    int chunk) {
+  extern __shared__ int32_t bins[];
+  const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
+  const int32_t* hr = H + ((int64_t)b * G + g) * K;
+  const int32_t* ob = offsets + (int64_t)b * (K + 1);
+  for (int i = t; i < K; i += kSortThreads) bins[i] = ob[i] + hr[i];
   __syncthreads();
+  const int32_t* ib = ids + (int64_t)b * N;
   int32_t* pb = perm + (int64_t)b * N;
-  for (int n0 = 0; n0 < N; n0 += kSortThreads * kSortUnroll) {
+  const int n0 = g * chunk, n1 = min(n0 + chunk, N);
+  for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
     int kk[kSortUnroll];
 #pragma unroll
     for (int q = 0; q < kSortUnroll; ++q) {
-      const int n = n0 + q * kSortThreads + t;
-      kk[q] = n < N ? ib[n] : -1;
+      const int n = m + q * kSortThreads + t;
+      kk[q] = n < n1 ? ib[n] : -1;
     }
 #pragma unroll
     for (int q = 0; q < kSortUnroll; ++q)
-      if ((unsigned)kk[q] < (unsigned)K)
-        pb[atomicAdd(&bins[kk[q]], 1)] = n0 + q * kSortThreads + t;
+      if ((unsigned)kk[q] < (unsigned)K) pb[atomicAdd(&bins[kk[q]], 1)] = m + q * kSortThreads + t;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Multi-block sort for large problems.
+// Sort for K > kMaxLdsBins (bins in several LDS ranges).
 // hist: block (chunk, bin range, b). Bins of this range live in dynamic LDS.
 template <int IPT>
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ ids,
@@ -533,6 +607,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
 // Empty clusters keep their centroid.
 constexpr int kFinVec = 4;
 
+template <bool SHIFT>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(
     const float* __restrict__ sums, const int32_t* __restrict__ offsets, float* __restrict__ c,
     float* __restrict__ part, int d, int K, int blocks_per_batch, bool vec) {
@@ -552,19 +627,21 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
       const int lo = ob[k], hi = ob[k + 1];
       if (hi > lo) {
         const float4 sv = *reinterpret_cast<const float4*>(sb + e0);
-        float4 cv = *reinterpret_cast<const float4*>(cb + e0);
         const float cnt = (float)(hi - lo);
         const bool lng = is_long(lo, hi);
         float nw[4] = {sv.x, sv.y, sv.z, sv.w};
-        const float od[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          nw[i] = lng ? nw[i] / cnt : nw[i];
-          const float dl = nw[i] - od[i];
-          moved = fmaf(dl, dl, moved);
+        for (int i = 0; i < 4; ++i) nw[i] = lng ? nw[i] / cnt : nw[i];
+        if constexpr (SHIFT) {
+          const float4 cv = *reinterpret_cast<const float4*>(cb + e0);
+          const float od[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float dl = nw[i] - od[i];
+            moved = fmaf(dl, dl, moved);
+          }
         }
-        cv = make_float4(nw[0], nw[1], nw[2], nw[3]);
-        *reinterpret_cast<float4*>(cb + e0) = cv;
+        *reinterpret_cast<float4*>(cb + e0) = make_float4(nw[0], nw[1], nw[2], nw[3]);
       }
     } else {
       for (int64_t e = e0; e < e0 + kFinVec && e < per; ++e) {
@@ -573,20 +650,24 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
         if (hi <= lo) continue;
         const float sv = sb[e];
         const float nw = is_long(lo, hi) ? sv / (float)(hi - lo) : sv;
-        const float dl = nw - cb[e];
+        if constexpr (SHIFT) {
+          const float dl = nw - cb[e];
+          moved = fmaf(dl, dl, moved);
+        }
         cb[e] = nw;
-        moved = fmaf(dl, dl, moved);
       }
     }
   }
-  moved = wave_sum(moved);
-  if (lane == 0) wsum[wv] = moved;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float t = 0.f;
+  if constexpr (SHIFT) {
+    moved = wave_sum(moved);
+    if (lane == 0) wsum[wv] = moved;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
-    part[(int64_t)b * blocks_per_batch + j] = t;
+      for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
+      part[(int64_t)b * blocks_per_batch + j] = t;
+    }
   }
 }
 
@@ -707,6 +788,20 @@ hipError_t segreduce_dt(const void* x, const UpdateWs& ws, int64_t B, int64_t N,
 
 }  // namespace
 
+// Chunks per problem for the split sort: about 512 blocks in all, at least
+// 4096 ids per chunk, at most 256 chunks and 2^24 count-matrix entries;
+// 0 when K needs more than one LDS range of bins.
+int split_groups(int64_t B, int64_t N, int64_t K) {
+  if (K > kMaxLdsBins || B <= 0 || N <= 0) return 0;
+  int64_t g = (512 + B - 1) / B;
+  const int64_t by_n = (N + 4095) / 4096;
+  g = g < by_n ? g : by_n;
+  g = g < 256 ? g : 256;
+  const int64_t by_mem = ((int64_t)1 << 24) / (B * K);
+  g = g < by_mem ? g : by_mem;
+  return (int)(g < 1 ? 1 : g);
+}
+
 // finalize blocks per problem: one thread per kFinVec centroid elements
 int64_t fin_blocks(int64_t K, int64_t d) {
   return (K * d + (int64_t)kThreads * kFinVec - 1) / ((int64_t)kThreads * kFinVec);
@@ -716,7 +811,8 @@ size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K) {
   const int64_t runs = (N + kSegRun - 1) / kSegRun;
   return align256((size_t)B * K * d * 4) + align256((size_t)B * (K + 1) * 4) +
          align256((size_t)B * K * 4) + align256((size_t)B * N * 4) +
-         align256((size_t)B * runs * 4) + align256((size_t)B * fin_blocks(K, d) * 4);
+         align256((size_t)B * runs * 4) + align256((size_t)B * fin_blocks(K, d) * 4) +
+         align256((size_t)B * split_groups(B, N, K) * K * 4);
 }
 
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K) {
@@ -734,6 +830,8 @@ UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K)
   w.run_first = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)B * runs * 4);
   w.part = reinterpret_cast<float*>(p);
+  p += align256((size_t)B * fin_blocks(K, d) * 4);
+  w.hist = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
@@ -747,44 +845,64 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
     g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
     zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
     FK_CHECK(hipGetLastError());
-    fill_f32_kernel<<<1, kThreads, 0, s>>>(shift, 0.f, B);
+    if (shift) fill_f32_kernel<<<1, kThreads, 0, s>>>(shift, 0.f, B);
     return hipGetLastError();
   }
   const int runs = (int)((N + kSegRun - 1) / kSegRun);
   const int64_t fb = fin_blocks(K, d);
-  if (N <= kSortOneBlockN && K <= kMaxLdsBins - 1) {
-    const size_t lds = (size_t)(K + 1) * sizeof(int32_t);
+  const int G = split_groups(B, N, K);
+  if (G > 0) {
+    const int chunk = (int)((N + G - 1) / G);
+    const size_t lds = (size_t)K * sizeof(int32_t);            // bins
+    const size_t lds1 = (size_t)(K + 1) * sizeof(int32_t);     // offsets + total
     static bool attr = false;
-    if (!attr && lds > 65536) {
-      (void)hipFuncSetAttribute((const void*)sort_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kMaxLdsBins * sizeof(int32_t));
+    if (!attr && lds1 > 65536) {
+      for (const void* f : {(const void*)hist2_kernel, (const void*)offsets_kernel,
+                            (const void*)scatter2_kernel})
+        (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (kMaxLdsBins + 64) * sizeof(int32_t));
       (void)hipGetLastError();
       attr = true;
     }
-    sort_kernel<<<(unsigned)B, kSortThreads, lds, s>>>(ids, counts, ws.offsets, ws.perm,
-                                                       ws.run_first, ws.sums, (int)N,
-                                                       (int)K, (int)d, runs);
+    hist2_kernel<<<(unsigned)(B * G), kSortThreads, lds, s>>>(ids, ws.hist, (int)N, (int)K, G,
+                                                             chunk);
+    FK_CHECK(hipGetLastError());
+    if ((int64_t)G * K <= kFusedOffsetsMax) {
+      offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
+                                                            ws.run_first, ws.sums, (int)K, (int)d,
+                                                            G, runs);
+      FK_CHECK(hipGetLastError());
+    } else {
+      const int kblocks = (int)((K + kThreads - 1) / kThreads);
+      colscan_kernel<<<(unsigned)(B * kblocks), kThreads, 0, s>>>(ws.hist, counts, (int)K, G,
+                                                                  kblocks);
+      FK_CHECK(hipGetLastError());
+      offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
+                                                             ws.run_first, ws.sums, (int)K,
+                                                             (int)d, 0, runs);
+      FK_CHECK(hipGetLastError());
+      const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);
+      prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.sums,
+                                                           (int)K, (int)d, runs, pb);
+      FK_CHECK(hipGetLastError());
+    }
+    scatter2_kernel<<<(unsigned)(B * G), kSortThreads, lds, s>>>(ids, ws.hist, ws.offsets,
+                                                                ws.perm, (int)N, (int)K, G,
+                                                                chunk);
     FK_CHECK(hipGetLastError());
   } else {
     int64_t g = (B * K + kThreads - 1) / kThreads;
     g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
     zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
     FK_CHECK(hipGetLastError());
-    if (K <= 4096)
-      FK_CHECK(run_hist_scatter<16>(ids, counts, nullptr, nullptr, B, N, K, false, s));
-    else
-      FK_CHECK(run_hist_scatter<64>(ids, counts, nullptr, nullptr, B, N, K, false, s));
+    FK_CHECK(run_hist_scatter<64>(ids, counts, nullptr, nullptr, B, N, K, false, s));
     scan_kernel<<<(unsigned)B, kSortThreads, 0, s>>>(counts, ws.offsets, ws.cursor, (int)K);
     FK_CHECK(hipGetLastError());
     const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);   // blocks per problem
     prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.sums,
                                                          (int)K, (int)d, runs, pb);
     FK_CHECK(hipGetLastError());
-    if (K <= 4096)
-      FK_CHECK(run_hist_scatter<16>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
-    else
-      FK_CHECK(run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
+    FK_CHECK(run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
   }
   if (dt == FK_F16)
     FK_CHECK(segreduce_dt<FK_F16>(x, ws, B, N, d, K, s));
@@ -795,8 +913,13 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
   const int64_t grid = B * fb;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const bool fvec = d % kFinVec == 0 && ((uintptr_t)c % 16) == 0;
-  finalize_kernel<<<(unsigned)grid, kThreads, 0, s>>>(ws.sums, ws.offsets, c, ws.part, (int)d,
-                                                      (int)K, (int)fb, fvec);
+  if (!shift) {                                  // the caller does not need the shift
+    finalize_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(ws.sums, ws.offsets, c, ws.part,
+                                                               (int)d, (int)K, (int)fb, fvec);
+    return hipGetLastError();
+  }
+  finalize_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(ws.sums, ws.offsets, c, ws.part,
+                                                            (int)d, (int)K, (int)fb, fvec);
   FK_CHECK(hipGetLastError());
   shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, (int)fb);
   return hipGetLastError();
