@@ -11,7 +11,7 @@
 // distance matrix never exists"; itinai.com summary, second paragraph;
 // "Flash-KMeans: Implementação Exata de K-Means…", section "FlashAssign").
 //
-// Small-D path (d <= 512): a block owns 4 waves x NF x 32 points whose
+// Small-D path (d <= 512): a block owns WAVES waves x NF x 32 points whose
 // fragments are loaded once into VGPRs; centroid tiles of TK rows are
 // double-buffered through LDS. v_mfma_f32_32x32x16_{f16,bf16}: A = 32
 // centroid rows from LDS, B = 32 points from registers, C-input = -||c||^2/2
@@ -81,7 +81,7 @@ __device__ __forceinline__ int merge_halves(float best, int bidx, int half) {
 // ===========================================================================
 // Running argmax, per point fragment f, over the 16 scores a lane holds for
 // one 32-row subtile (rows 8*(r/4) + 4*half + r%4 of the subtile, r = 0..15):
-//   m     = max of the 16 scores                      (v_max3 tree, 8 ops)
+//   m     = max of the 16 scores                      (two v_max3 chains, 8 ops)
 //   if m > best: best = m, btile = subtile, saved = the 16 scores
 // Strict '>' keeps the first subtile that reaches the maximum; the row is
 // located once at the end as the first slot of `saved` equal to best, so the
@@ -96,23 +96,23 @@ struct Argmax {
 // The work is split so it can be spread over the k-steps of the next
 // subtile: parts 0-3 build the max tree, part 4 compares, parts 4-7 save.
 __device__ __forceinline__ void drain_part(const floatx16_t& acc, int part, int g, Argmax& st,
-                                           float (&m)[6], bool& gt) {
+                                           float (&m)[2], bool& gt) {
   switch (part) {
     case 0:
       m[0] = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
       m[1] = fmaxf(fmaxf(acc[3], acc[4]), acc[5]);
       break;
     case 1:
-      m[2] = fmaxf(fmaxf(acc[6], acc[7]), acc[8]);
-      m[3] = fmaxf(fmaxf(acc[9], acc[10]), acc[11]);
+      m[0] = fmaxf(fmaxf(m[0], acc[6]), acc[7]);
+      m[1] = fmaxf(fmaxf(m[1], acc[8]), acc[9]);
       break;
     case 2:
-      m[4] = fmaxf(fmaxf(acc[12], acc[13]), acc[14]);
-      m[5] = fmaxf(fmaxf(m[0], m[1]), m[2]);
+      m[0] = fmaxf(fmaxf(m[0], acc[10]), acc[11]);
+      m[1] = fmaxf(fmaxf(m[1], acc[12]), acc[13]);
       break;
     case 3:
-      m[0] = fmaxf(fmaxf(m[3], m[4]), acc[15]);
-      m[0] = fmaxf(m[5], m[0]);
+      m[0] = fmaxf(fmaxf(m[0], m[1]), acc[14]);
+      m[0] = fmaxf(m[0], acc[15]);
       break;
     case 4:
       gt = m[0] > st.best;
@@ -139,23 +139,24 @@ __device__ __forceinline__ int argmax_row(const Argmax& st, int half) {
 
 // FULL: d == 16*KS, so every column of a row is real and loads need no
 // column guard; otherwise columns >= d read as zero.
-template <int DT, int KS, int NF, int TK, bool VEC, bool FULL>
-__global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
+template <int DT, int KS, int NF, int TK, int WAVES, bool VEC, bool FULL>
+__global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ c,
     const float* __restrict__ cnorm, int32_t* __restrict__ ids, int N, int d, int K,
     int blocks_per_batch, int grid) {
+  constexpr int NT = WAVES * 64;         // threads per block
   constexpr int DP = KS * 16;            // padded dimension
   constexpr int PITCH = DP + 8;          // LDS row pitch (elements): +16 B against bank conflicts
   constexpr int NSUB = TK / 32;          // MFMA row blocks per tile
-  constexpr int BN = kWaves * NF * 32;   // points per block
+  constexpr int BN = WAVES * NF * 32;    // points per block
   constexpr int VPR = DP / 8;            // 16-byte vectors per centroid row
-  constexpr int NV = (TK * VPR + kThreads - 1) / kThreads;   // vectors per thread per tile
+  constexpr int NV = (TK * VPR + NT - 1) / NT;   // vectors per thread per tile
   constexpr int NE = 16 * NF;            // accumulator elements per lane per subtile
   constexpr int EPS = (NE + KS - 1) / KS;   // epilogue elements per k-step
   static_assert(NSUB % 2 == 0, "accumulator sets alternate by subtile");
-  static_assert(TK <= kThreads, "one norm per thread");
+  static_assert(TK <= NT, "one norm per thread");
   __shared__ __align__(16) uint16_t lds_c[2][TK * PITCH];
-  __shared__ __align__(16) float lds_h[2][kThreads];
+  __shared__ __align__(16) float lds_h[2][NT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, r32 = lane & 31;
@@ -189,8 +190,8 @@ __global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
   auto fetch = [&](int t) {
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
-      const int v = tid + kThreads * q;
-      if (TK * VPR % kThreads == 0 || v < TK * VPR) {
+      const int v = tid + NT * q;
+      if (TK * VPR % NT == 0 || v < TK * VPR) {
         const int row = v / VPR, col = (v % VPR) * 8;
         const int k = min(t * TK + row, K - 1);
         pre[q] = FULL ? *reinterpret_cast<const uint4*>(cb + (int64_t)k * d + col)
@@ -202,8 +203,8 @@ __global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
   auto stash = [&](int t, int buf) {
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
-      const int v = tid + kThreads * q;
-      if (TK * VPR % kThreads == 0 || v < TK * VPR) {
+      const int v = tid + NT * q;
+      if (TK * VPR % NT == 0 || v < TK * VPR) {
         const int row = v / VPR, col = (v % VPR) * 8;
         *reinterpret_cast<uint4*>(&lds_c[buf][row * PITCH + col]) = pre[q];
       }
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
     ar[0] = read_a(buf, 0);
     ar[1] = read_a(buf, 1 % STEPS);
     read_c(buf, 1 % NSUB, ci[1]);
-    float m[NF][6];
+    float m[NF][2];
     bool gt[NF];
 #pragma unroll
     for (int q = 0; q < STEPS; ++q) {
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void assign_smalld_kernel(
   }
   {
     const int g = ntiles * NSUB - 1;       // the last subtile, still in acc[1]
-    float m[NF][6];
+    float m[NF][2];
     bool gt[NF];
 #pragma unroll
     for (int p = 0; p < 8 * NF; ++p)
@@ -499,35 +500,39 @@ bool vec_ok(const void* x, const void* c, int64_t d) {
   return d % 8 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)c % 16) == 0;
 }
 
-template <int DT, int KS, int NF, int TK>
+template <int DT, int KS, int NF, int TK, int WAVES>
 hipError_t run_smalld(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
                       int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
-  constexpr int BN = kWaves * NF * 32;
+  constexpr int BN = WAVES * NF * 32;
   const int bpb = (int)((N + BN - 1) / BN);
   const int64_t grid = B * bpb;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const uint16_t* xp = (const uint16_t*)x;
   const uint16_t* cp = (const uint16_t*)c;
   if (vec_ok(x, c, d) && d == 16 * KS)
-    assign_smalld_kernel<DT, KS, NF, TK, true, true><<<(unsigned)grid, kThreads, 0, s>>>(
+    assign_smalld_kernel<DT, KS, NF, TK, WAVES, true, true><<<(unsigned)grid, WAVES * 64, 0, s>>>(
         xp, cp, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
   else if (vec_ok(x, c, d))
-    assign_smalld_kernel<DT, KS, NF, TK, true, false><<<(unsigned)grid, kThreads, 0, s>>>(
+    assign_smalld_kernel<DT, KS, NF, TK, WAVES, true, false><<<(unsigned)grid, WAVES * 64, 0, s>>>(
         xp, cp, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
   else
-    assign_smalld_kernel<DT, KS, NF, TK, false, false><<<(unsigned)grid, kThreads, 0, s>>>(
+    assign_smalld_kernel<DT, KS, NF, TK, WAVES, false, false><<<(unsigned)grid, WAVES * 64, 0, s>>>(
         xp, cp, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
   return hipGetLastError();
 }
 
+// Shapes per d: k-steps KS (16 elements each), point fragments NF per wave,
+// tile rows TK, waves per block. d <= 128 uses 8-wave blocks with 128-row
+// tiles: each staged tile feeds 512 points, half the staging work per MFMA
+// of 4-wave blocks with 64-row tiles.
 template <int DT>
 hipError_t smalld_dt(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
                      int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
-  if (d <= 32) return run_smalld<DT, 2, 2, 64>(x, c, cn, B, N, d, K, ids, s);
-  if (d <= 64) return run_smalld<DT, 4, 2, 64>(x, c, cn, B, N, d, K, ids, s);
-  if (d <= 128) return run_smalld<DT, 8, 2, 64>(x, c, cn, B, N, d, K, ids, s);
-  if (d <= 256) return run_smalld<DT, 16, 2, 64>(x, c, cn, B, N, d, K, ids, s);
-  if (d <= 512) return run_smalld<DT, 32, 1, 64>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 32) return run_smalld<DT, 2, 2, 64, 4>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 64) return run_smalld<DT, 4, 2, 64, 4>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 128) return run_smalld<DT, 8, 2, 128, 8>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 256) return run_smalld<DT, 16, 2, 64, 4>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 512) return run_smalld<DT, 32, 1, 64, 4>(x, c, cn, B, N, d, K, ids, s);
   return hipErrorNotSupported;
 }
 
