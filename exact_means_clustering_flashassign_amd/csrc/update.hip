@@ -542,10 +542,18 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     if (g == 0 && colok) {
       float* row = sb + (int64_t)jk * d + col;
       if (jcnt > 0) {
-        const float cnt = (float)jcnt;
+        const float inv = 1.0f / (float)jcnt;
+        if constexpr (VEC) {
+          // whole 16-byte vectors: col is a multiple of EV and d of EV
 #pragma unroll
-        for (int i = 0; i < EV; ++i)
-          if (col + i < d) row[i] = acc[i] / cnt;
+          for (int i = 0; i < EV; i += 4)
+            *reinterpret_cast<float4*>(row + i) =
+                make_float4(acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv);
+        } else {
+#pragma unroll
+          for (int i = 0; i < EV; ++i)
+            if (col + i < d) row[i] = acc[i] * inv;
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < EV; ++i)
