@@ -406,6 +406,39 @@ __device__ __forceinline__ void widen16(const uint4 v, float* out) {
   }
 }
 
+// Lane swaps of gfx950 (VALU, no LDS): v_permlane16_swap exchanges the odd
+// 16-lane rows of a with the even rows of b; v_permlane32_swap exchanges the
+// upper half of a with the lower half of b. Written as instructions with two
+// in-out operands (the compiler's own lowering of these swaps here reads the
+// first result twice); the s_nop gives the wait states a VALU write needs
+// before a permlane reads the register.
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Sum of v over the lanes that share lane % LPR (LPR = 4, 8 or 16), left in
+// every lane: rotations by 8 and 4 inside each 16-lane row (DPP), then the
+// row pairs and the two halves added through the lane swaps above.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16, "lanes per row");
+  if constexpr (LPR <= 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128,
+                                                            0xF, 0xF, false));   // row_ror:8
+  if constexpr (LPR <= 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124,
+                                                            0xF, 0xF, false));   // row_ror:4
+  float a = v, b = v;
+  permlane16_swap(a, b);                         // a: rows 0,0,2,2   b: rows 1,1,3,3
+  a += b;
+  b = a;
+  permlane32_swap(a, b);                         // a: lower half twice, b: upper half twice
+  return a + b;
+}
+
 template <int DT, int LPR, bool VEC>
 __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     const void* __restrict__ x, const int32_t* __restrict__ perm,
@@ -536,9 +569,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   };
   auto flush = [&]() {
 #pragma unroll
-    for (int sh = LPR; sh < 64; sh <<= 1)
-#pragma unroll
-      for (int i = 0; i < EV; ++i) acc[i] += __shfl_xor(acc[i], sh, 64);
+    for (int i = 0; i < EV; ++i) acc[i] = group_sum<LPR>(acc[i]);
     if (g == 0 && colok) {
       float* row = sb + (int64_t)jk * d + col;
       if (jcnt > 0) {
