@@ -15,18 +15,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfkmeans.so")
-SOURCES = ["norms.hip", "assign.hip", "update.hip", "api.hip"]
+SOURCES = ["norms.hip", "assign.hip", "assign_splitd.hip", "update.hip", "api.hip"]
 # Per-file flags. assign.hip: inputs are finite by contract, so fmaxf needs no
-# NaN canonicalisation and the argmax max-tree lowers to plain v_max3_f32.
-FILE_FLAGS = {"assign.hip": ["-fno-honor-nans"]}
+# NaN canonicalisation and the argmax max-tree lowers to plain v_max3_f32; its
+# MFMA accumulators live in VGPRs, which the argmax reads without AGPR copies.
+# assign_splitd.hip keeps the default (accumulators in AGPRs): its 256
+# accumulator registers per lane would not fit the VGPR file.
+FILE_FLAGS = {"assign.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPRs: the argmax reads them directly, no AGPR copies
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
 

@@ -19,10 +19,7 @@
 // centroid scores for one point; the running max stays in-lane across all
 // tiles and one lane swap at the end merges the two lanes that share a point.
 //
-// Split-D path (d > 512): the same tiles with the d loop innermost: a block
-// keeps a (256 points x 128 centroids) score block in registers across the d
-// loop (outer K loop, inner D loop), staging each centroid d-chunk in LDS and
-// reading point d-chunks straight into registers.
+// The split-D path (d > 512) lives in assign_splitd.hip.
 //
 // fp32 inputs use a VALU kernel (exact fp32 products, fp32 fma chain).
 #include <math.h>
@@ -32,49 +29,7 @@
 namespace fk {
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves
-constexpr int kWaves = 4;
-
-// ---- 16-byte loads of 8 stored elements, zero outside [0,limit) -----------
-template <bool VEC>
-__device__ __forceinline__ uint4 load8(const uint16_t* row, int col, int limit) {
-  if (VEC) {
-    if (col < limit) return *reinterpret_cast<const uint4*>(row + col);
-    return make_uint4(0, 0, 0, 0);
-  } else {
-    uint16_t e[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = (col + i < limit) ? row[col + i] : (uint16_t)0;
-    uint4 v;
-    v.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
-    v.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
-    v.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
-    v.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
-    return v;
-  }
-}
-
-// Running argmax over one 32x32 accumulator: lane holds rows
-// 8*(r/4) + 4*half + r%4 of the tile; the 4*half term is added at the merge.
-__device__ __forceinline__ void argmax_update(const floatx16_t& acc, int base, float& best,
-                                              int& bidx) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float v = acc[r];
-    const bool gt = v > best;
-    best = gt ? v : best;
-    bidx = gt ? base + 8 * (r >> 2) + (r & 3) : bidx;
-  }
-}
-
-// Merge the two lanes (half 0 and half 1) that hold the same point.
-__device__ __forceinline__ int merge_halves(float best, int bidx, int half) {
-  int idx = bidx + 4 * half;
-  const float ob = __shfl_xor(best, 32, 64);
-  const int oi = __shfl_xor(idx, 32, 64);
-  if (ob > best || (ob == best && oi < idx)) idx = oi;
-  return idx;
-}
+constexpr int kThreads = 256;   // fp32 kernel block
 
 // ===========================================================================
 // small-D
@@ -307,138 +262,6 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
 }
 
 // ===========================================================================
-// split-D
-// ===========================================================================
-constexpr int kSplitDC = 64;     // d-chunk (4 MFMA k-steps)
-constexpr int kSplitTK = 128;    // centroids per outer tile (4 row blocks)
-constexpr int kSplitNF = 2;      // point fragments per wave
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void assign_splitd_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ c,
-    const float* __restrict__ cnorm, int32_t* __restrict__ ids, int N, int d, int K,
-    int blocks_per_batch, int grid) {
-  constexpr int KSC = kSplitDC / 16;
-  constexpr int PITCH = kSplitDC + 8;
-  constexpr int NSUB = kSplitTK / 32;
-  constexpr int NF = kSplitNF;
-  constexpr int BN = kWaves * NF * 32;
-  constexpr int VPR = kSplitDC / 8;
-  constexpr int NV = kSplitTK * VPR / kThreads;
-  static_assert(kSplitTK * VPR % kThreads == 0, "tile split");
-  __shared__ __align__(16) uint16_t lds_c[2][kSplitTK * PITCH];
-  __shared__ __align__(16) float lds_h[kSplitTK];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, r32 = lane & 31;
-  const int64_t logical = xcd_remap(blockIdx.x, grid);
-  const int b = (int)(logical / blocks_per_batch);
-  const int nblk = (int)(logical % blocks_per_batch) * BN + wave * NF * 32;
-  const uint16_t* xb = x + (int64_t)b * N * d;
-  const uint16_t* cb = c + (int64_t)b * K * d;
-  const float* cnb = cnorm + (int64_t)b * K;
-
-  const uint16_t* xrow[NF];
-  bool xval[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int n = nblk + f * 32 + r32;
-    xval[f] = n < N;
-    xrow[f] = xb + (int64_t)(n < N ? n : 0) * d;
-  }
-
-  const int nchunks = (d + kSplitDC - 1) / kSplitDC;
-  const int ktiles = (K + kSplitTK - 1) / kSplitTK;
-  float best[NF];
-  int bidx[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    best[f] = -INFINITY;
-    bidx[f] = 0;
-  }
-
-  uint4 pre[NV];
-  auto fetch = [&](int kt, int ch) {
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const int v = tid + kThreads * q;
-      const int row = v / VPR, col = ch * kSplitDC + (v % VPR) * 8;
-      const int k = kt * kSplitTK + row;
-      pre[q] = (k < K) ? load8<VEC>(cb + (int64_t)k * d, col, d) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const int v = tid + kThreads * q;
-      const int row = v / VPR, col = (v % VPR) * 8;
-      *reinterpret_cast<uint4*>(&lds_c[buf][row * PITCH + col]) = pre[q];
-    }
-  };
-
-  for (int kt = 0; kt < ktiles; ++kt) {
-    if (tid < kSplitTK) {
-      const int k = kt * kSplitTK + tid;
-      lds_h[tid] = k < K ? -0.5f * cnb[k] : -INFINITY;
-    }
-    fetch(kt, 0);
-    stash(0);
-    __syncthreads();
-    floatx16_t acc[NSUB][NF];
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub) {
-      floatx16_t cinit;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 hv = *reinterpret_cast<const float4*>(&lds_h[sub * 32 + 8 * i + 4 * half]);
-        cinit[4 * i + 0] = hv.x;
-        cinit[4 * i + 1] = hv.y;
-        cinit[4 * i + 2] = hv.z;
-        cinit[4 * i + 3] = hv.w;
-      }
-#pragma unroll
-      for (int f = 0; f < NF; ++f) acc[sub][f] = cinit;
-    }
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const int buf = ch & 1;
-      uint4 xf[NF][KSC];
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int s = 0; s < KSC; ++s)
-          xf[f][s] = xval[f] ? load8<VEC>(xrow[f], ch * kSplitDC + s * 16 + half * 8, d)
-                             : make_uint4(0, 0, 0, 0);
-      if (ch + 1 < nchunks) fetch(kt, ch + 1);
-#pragma unroll
-      for (int sub = 0; sub < NSUB; ++sub) {
-        const uint16_t* arow = &lds_c[buf][(sub * 32 + r32) * PITCH + half * 8];
-#pragma unroll
-        for (int s = 0; s < KSC; ++s) {
-          const uint4 a = *reinterpret_cast<const uint4*>(arow + s * 16);
-#pragma unroll
-          for (int f = 0; f < NF; ++f) acc[sub][f] = Mfma<DT>::run(a, xf[f][s], acc[sub][f]);
-        }
-      }
-      if (ch + 1 < nchunks) stash(buf ^ 1);
-      __syncthreads();
-    }
-#pragma unroll
-    for (int sub = 0; sub < NSUB; ++sub)
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        argmax_update(acc[sub][f], kt * kSplitTK + sub * 32, best[f], bidx[f]);
-  }
-
-  int32_t* ib = ids + (int64_t)b * N;
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int idx = merge_halves(best[f], bidx[f], half);
-    const int n = nblk + f * 32 + r32;
-    if (half == 0 && n < N) ib[n] = idx;
-  }
-}
-
-// ===========================================================================
 // fp32 (VALU)
 // ===========================================================================
 constexpr int kF32TK = 32;   // centroids per tile
@@ -536,22 +359,6 @@ hipError_t smalld_dt(const void* x, const void* c, const float* cn, int64_t B, i
   return hipErrorNotSupported;
 }
 
-template <int DT>
-hipError_t splitd_dt(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
-                     int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
-  constexpr int BN = kWaves * kSplitNF * 32;
-  const int bpb = (int)((N + BN - 1) / BN);
-  const int64_t grid = B * bpb;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (vec_ok(x, c, d))
-    assign_splitd_kernel<DT, true><<<(unsigned)grid, kThreads, 0, s>>>(
-        (const uint16_t*)x, (const uint16_t*)c, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
-  else
-    assign_splitd_kernel<DT, false><<<(unsigned)grid, kThreads, 0, s>>>(
-        (const uint16_t*)x, (const uint16_t*)c, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 // The small-D tiles fit LDS for every d <= 512 (largest: 2 x 32 x 520 x 2 B).
@@ -563,15 +370,6 @@ hipError_t launch_assign_smalld(const void* x, const void* c_lp, const float* cn
   if (B == 0 || N == 0) return hipSuccess;
   if (dt == FK_F16) return smalld_dt<FK_F16>(x, c_lp, cnorm, B, N, d, K, ids, s);
   if (dt == FK_BF16) return smalld_dt<FK_BF16>(x, c_lp, cnorm, B, N, d, K, ids, s);
-  return hipErrorNotSupported;
-}
-
-hipError_t launch_assign_splitd(const void* x, const void* c_lp, const float* cnorm, int dt,
-                                int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,
-                                hipStream_t s) {
-  if (B == 0 || N == 0) return hipSuccess;
-  if (dt == FK_F16) return splitd_dt<FK_F16>(x, c_lp, cnorm, B, N, d, K, ids, s);
-  if (dt == FK_BF16) return splitd_dt<FK_BF16>(x, c_lp, cnorm, B, N, d, K, ids, s);
   return hipErrorNotSupported;
 }
 

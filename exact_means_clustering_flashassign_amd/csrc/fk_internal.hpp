@@ -68,6 +68,41 @@ template <> struct Mfma<FK_BF16> {
 };
 
 // ---------------------------------------------------------------------------
+// MFMA tile helpers (v_mfma_f32_32x32x16: lane = point column r32 + 32*half,
+// holding k-elements half*8 .. half*8+7 of each 16-wide k-step)
+// ---------------------------------------------------------------------------
+// 16-byte load of 8 stored elements starting at col; elements at or past
+// limit read as zero. VEC: the row base is 16-byte aligned and limit % 8 == 0.
+template <bool VEC>
+__device__ __forceinline__ uint4 load8(const uint16_t* row, int col, int limit) {
+  if (VEC) {
+    if (col < limit) return *reinterpret_cast<const uint4*>(row + col);
+    return make_uint4(0, 0, 0, 0);
+  } else {
+    uint16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = (col + i < limit) ? row[col + i] : (uint16_t)0;
+    uint4 v;
+    v.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+    v.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+    v.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
+    v.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
+    return v;
+  }
+}
+
+// The two lanes (half 0 and half 1) that hold the same point each carry the
+// best score and row over their 16 rows of every 32-row block; half 1's rows
+// sit 4 above half 0's. Returns the winning row, lowest row on equal scores.
+__device__ __forceinline__ int merge_halves(float best, int bidx, int half) {
+  int idx = bidx + 4 * half;
+  const float ob = __shfl_xor(best, 32, 64);
+  const int oi = __shfl_xor(idx, 32, 64);
+  if (ob > best || (ob == best && oi < idx)) idx = oi;
+  return idx;
+}
+
+// ---------------------------------------------------------------------------
 // wave helpers (wave64)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {

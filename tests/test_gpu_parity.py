@@ -99,6 +99,7 @@ ASSIGN_CASES = [
     ("bf16", 2, 1000, 1024, 256, False),
     ("f16", 1, 200, 1000, 150, False),
     ("bf16", 1, 150, 2048, 60, False),
+    ("f16", 1, 400, 640, 300, False),       # two 256-row K tiles over five d-chunks
     ("f16", 2, 1000, 128, 300, True),       # split-D forced at small d
     ("bf16", 1, 500, 60, 130, True),
     ("f32", 1, 2048, 32, 16, False),
