@@ -92,13 +92,20 @@ __device__ __forceinline__ int argmax_row(const Argmax& st, int half) {
   return st.btile * 32 + 8 * (slot >> 2) + 4 * half + (slot & 3);
 }
 
+// Persistent: a block walks point blocks v = blockIdx.x, + nblocks, ... of the
+// virtual grid of `total` point blocks (each mapped through xcd_remap, and
+// nblocks is a multiple of 8, so every point block a block takes shares its
+// XCD's L2 with the ones it would have had as a plain launch). During the
+// last centroid tile of one point block the block already stages tile 0 of
+// the next, and the next block's point fragments load while the last argmax
+// drains, so consecutive point blocks run back to back.
 // FULL: d == 16*KS, so every column of a row is real and loads need no
 // column guard; otherwise columns >= d read as zero.
 template <int DT, int KS, int NF, int TK, int WAVES, bool VEC, bool FULL>
 __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ c,
     const float* __restrict__ cnorm, int32_t* __restrict__ ids, int N, int d, int K,
-    int blocks_per_batch, int grid) {
+    int blocks_per_batch, int total, int nblocks) {
   constexpr int NT = WAVES * 64;         // threads per block
   constexpr int DP = KS * 16;            // padded dimension
   constexpr int PITCH = DP + 8;          // LDS row pitch (elements): +16 B against bank conflicts
@@ -106,8 +113,6 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   constexpr int BN = WAVES * NF * 32;    // points per block
   constexpr int VPR = DP / 8;            // 16-byte vectors per centroid row
   constexpr int NV = (TK * VPR + NT - 1) / NT;   // vectors per thread per tile
-  constexpr int NE = 16 * NF;            // accumulator elements per lane per subtile
-  constexpr int EPS = (NE + KS - 1) / KS;   // epilogue elements per k-step
   static_assert(NSUB % 2 == 0, "accumulator sets alternate by subtile");
   static_assert(TK <= NT, "one norm per thread");
   __shared__ __align__(16) uint16_t lds_c[2][TK * PITCH];
@@ -115,34 +120,32 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, r32 = lane & 31;
-  const int64_t logical = xcd_remap(blockIdx.x, grid);
-  const int b = (int)(logical / blocks_per_batch);
-  const int nblk = (int)(logical % blocks_per_batch) * BN + wave * NF * 32;
-  const uint16_t* xb = x + (int64_t)b * N * d;
-  const uint16_t* cb = c + (int64_t)b * K * d;
-  const float* cnb = cnorm + (int64_t)b * K;
+  const int ntiles = (K + TK - 1) / TK;
 
-  // point fragments, resident for the whole kernel; rows past N repeat row
-  // N-1 (their results are never stored)
-  uint4 xf[NF][KS];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int n = min(nblk + f * 32 + r32, N - 1);
-    const uint16_t* row = xb + (int64_t)n * d;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      xf[f][s] = FULL ? *reinterpret_cast<const uint4*>(row + s * 16 + half * 8)
-                      : load8<VEC>(row, s * 16 + half * 8, d);
-  }
+  // point block v -> problem and this wave's first row
+  auto locate = [&](int64_t v, int& pb, int& row0) {
+    const int64_t logical = xcd_remap(v, total);
+    pb = (int)(logical / blocks_per_batch);
+    row0 = (int)(logical % blocks_per_batch) * BN + wave * NF * 32;
+  };
+  // the lane's point row of fragment f; rows past N repeat row N-1 (their
+  // results are never stored)
+  auto point_row = [&](int pb, int row0, int f) -> const uint16_t* {
+    return x + ((int64_t)pb * N + min(row0 + f * 32 + r32, N - 1)) * d;
+  };
+  auto load_frag = [&](const uint16_t* row, int s) -> uint4 {
+    return FULL ? *reinterpret_cast<const uint4*>(row + s * 16 + half * 8)
+                : load8<VEC>(row, s * 16 + half * 8, d);
+  };
 
   // Tile loads: rows past K repeat row K-1 and get -inf norms, so they never
   // win. Loads and stores are unconditional (tile indices clamp, every
   // thread owns an lds_h slot) so one tile iteration is a single basic block
   // the scheduler can interleave.
-  const int ntiles = (K + TK - 1) / TK;
   uint4 pre[NV];
   float pre_n = 0.f;
-  auto fetch = [&](int t) {
+  auto fetch = [&](int pb, int t) {
+    const uint16_t* cb = c + (int64_t)pb * K * d;
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
       const int v = tid + NT * q;
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
                       : load8<VEC>(cb + (int64_t)k * d, col, d);
       }
     }
-    pre_n = cnb[min(t * TK + (tid % TK), K - 1)];
+    pre_n = cnorm[(int64_t)pb * K + min(t * TK + (tid % TK), K - 1)];
   };
   auto stash = [&](int t, int buf) {
 #pragma unroll
@@ -166,25 +169,6 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
     }
     lds_h[buf][tid] = (t * TK + tid < K) ? -0.5f * pre_n : -INFINITY;
   };
-
-  Argmax st[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    st[f].best = -INFINITY;
-    st[f].btile = 0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st[f].saved[r] = -INFINITY;
-  }
-
-  // Two accumulator sets alternate by subtile: while the MFMAs of subtile g
-  // fill one set, the argmax of subtile g-1 drains the other, spread over the
-  // k-steps, so VALU work issues in the shadow of the matrix core. The first
-  // drain is of an all -inf set standing for subtile -1.
-  floatx16_t acc[2][NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[1][f][r] = -INFINITY;
 
   // LDS operands of a step, read ahead of use: A fragments two k-steps ahead
   // (ring of three), C inputs (-||c||^2/2 of the lane's rows) one subtile
@@ -209,12 +193,16 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
     }
   };
 
-  fetch(0);
-  stash(0, 0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    fetch(t + 1 < ntiles ? t + 1 : t);     // the last fetch is a harmless repeat
+  uint4 xf[NF][KS];
+  Argmax st[NF];
+  // Two accumulator sets alternate by subtile: while the MFMAs of subtile g
+  // fill one set, the argmax of subtile g-1 drains the other, spread over the
+  // k-steps, so VALU work issues in the shadow of the matrix core. The first
+  // drain of a point block is of an all -inf set standing for subtile -1.
+  floatx16_t acc[2][NF];
+
+  // One centroid tile from LDS buffer buf.
+  auto tile = [&](int buf, int t) {
     floatx16_t ci[2];
     uint4 ar[3];
     read_c(buf, 0, ci[0]);
@@ -226,7 +214,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
 #pragma unroll
     for (int q = 0; q < STEPS; ++q) {
       const int sub = q / KS, kk = q % KS;
-      const int g = t * NSUB + sub;          // global subtile index
+      const int g = t * NSUB + sub;          // subtile index within the point block
       floatx16_t (&cur)[NF] = acc[sub & 1];
       const floatx16_t (&prev)[NF] = acc[(sub + 1) & 1];
       if (q + 2 < STEPS) ar[(q + 2) % 3] = read_a(buf, q + 2);
@@ -240,24 +228,80 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
       // keep program order across steps: the reads above stay ahead of use
       __builtin_amdgcn_sched_barrier(0);
     }
-    stash(t + 1, buf ^ 1);                 // never read after the last tile
-    __syncthreads();
-  }
-  {
-    const int g = ntiles * NSUB - 1;       // the last subtile, still in acc[1]
-    float m[NF][2];
-    bool gt[NF];
-#pragma unroll
-    for (int p = 0; p < 8 * NF; ++p)
-      drain_part(acc[1][p % NF], p / NF, g, st[p % NF], m[p % NF], gt[p % NF]);
-  }
+  };
 
-  int32_t* ib = ids + (int64_t)b * N;
+  auto reset = [&]() {
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int idx = merge_halves(st[f].best, argmax_row(st[f], half) - 4 * half, half);
-    const int n = nblk + f * 32 + r32;
-    if (half == 0 && n < N) ib[n] = min(max(idx, 0), K - 1);
+    for (int f = 0; f < NF; ++f) {
+      st[f].best = -INFINITY;
+      st[f].btile = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[f].saved[r] = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[1][f][r] = -INFINITY;
+    }
+  };
+  auto load_block = [&](int pb, int row0) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint16_t* row = point_row(pb, row0, f);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) xf[f][s] = load_frag(row, s);
+    }
+  };
+
+  int64_t v = blockIdx.x;
+  int pb, row0;
+  locate(v, pb, row0);
+  // the next point block, or this one again past the end (its loads and
+  // tile-0 stage are then harmless repeats that nothing reads)
+  int64_t vn = v + nblocks;
+  int npb = pb, nrow0 = row0;
+  if (vn < total) locate(vn, npb, nrow0);
+  load_block(pb, row0);
+  fetch(pb, 0);
+  stash(0, 0);
+  reset();
+  __syncthreads();
+  int buf = 0, t = 0;
+  for (;;) {
+    // one centroid tile; the tile staged meanwhile is the next one of this
+    // point block or, during the last, tile 0 of the next point block
+    const bool last = t == ntiles - 1;
+    const int ft = last ? 0 : t + 1;
+    fetch(last ? npb : pb, ft);
+    tile(buf, t);
+    stash(ft, buf ^ 1);
+    if (last) {
+      const int g = ntiles * NSUB - 1;       // the last subtile, still in acc[1]
+      float m[NF][2];
+      bool gt[NF];
+#pragma unroll
+      for (int p = 0; p < 8 * NF; ++p)
+        drain_part(acc[1][p % NF], p / NF, g, st[p % NF], m[p % NF], gt[p % NF]);
+      int32_t* ib = ids + (int64_t)pb * N;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int idx = merge_halves(st[f].best, argmax_row(st[f], half) - 4 * half, half);
+        const int n = row0 + f * 32 + r32;
+        if (half == 0 && n < N) ib[n] = min(max(idx, 0), K - 1);
+      }
+      load_block(npb, nrow0);
+      reset();
+    }
+    __syncthreads();
+    buf ^= 1;
+    if (!last) {
+      ++t;
+      continue;
+    }
+    if (vn >= total) break;
+    v = vn;
+    pb = npb;
+    row0 = nrow0;
+    vn = v + nblocks;
+    if (vn < total) locate(vn, npb, nrow0);
+    t = 0;
   }
 }
 
@@ -323,25 +367,52 @@ bool vec_ok(const void* x, const void* c, int64_t d) {
   return d % 8 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)c % 16) == 0;
 }
 
+// Blocks of kernel `kern` that fit on the current device at once (resident
+// blocks per CU times the CU count), cached per device in `cache` (one cache
+// per kernel instance; 0 = not yet queried).
+template <typename Kern>
+int resident_blocks(Kern kern, int threads, int (&cache)[64]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev] = per_cu * cus;
+  }
+  return cache[dev];
+}
+
+template <int DT, int KS, int NF, int TK, int WAVES, bool VEC, bool FULL>
+hipError_t launch_smalld(const uint16_t* x, const uint16_t* c, const float* cn, int64_t total,
+                         int bpb, int64_t N, int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
+  static int cache[64];
+  auto kern = assign_smalld_kernel<DT, KS, NF, TK, WAVES, VEC, FULL>;
+  const int resident = resident_blocks(kern, WAVES * 64, cache);
+  if (resident <= 0) return hipErrorInvalidConfiguration;
+  // a multiple of 8 so each block's point blocks stay on its XCD
+  int64_t nblocks = resident >= 8 ? resident / 8 * 8 : resident;
+  if (nblocks > total) nblocks = total;
+  kern<<<(unsigned)nblocks, WAVES * 64, 0, s>>>(x, c, cn, ids, (int)N, (int)d, (int)K, bpb,
+                                                (int)total, (int)nblocks);
+  return hipGetLastError();
+}
+
 template <int DT, int KS, int NF, int TK, int WAVES>
 hipError_t run_smalld(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
                       int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
   constexpr int BN = WAVES * NF * 32;
   const int bpb = (int)((N + BN - 1) / BN);
-  const int64_t grid = B * bpb;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const int64_t total = B * bpb;
+  if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const uint16_t* xp = (const uint16_t*)x;
   const uint16_t* cp = (const uint16_t*)c;
   if (vec_ok(x, c, d) && d == 16 * KS)
-    assign_smalld_kernel<DT, KS, NF, TK, WAVES, true, true><<<(unsigned)grid, WAVES * 64, 0, s>>>(
-        xp, cp, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
-  else if (vec_ok(x, c, d))
-    assign_smalld_kernel<DT, KS, NF, TK, WAVES, true, false><<<(unsigned)grid, WAVES * 64, 0, s>>>(
-        xp, cp, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
-  else
-    assign_smalld_kernel<DT, KS, NF, TK, WAVES, false, false><<<(unsigned)grid, WAVES * 64, 0, s>>>(
-        xp, cp, cn, ids, (int)N, (int)d, (int)K, bpb, (int)grid);
-  return hipGetLastError();
+    return launch_smalld<DT, KS, NF, TK, WAVES, true, true>(xp, cp, cn, total, bpb, N, d, K, ids, s);
+  if (vec_ok(x, c, d))
+    return launch_smalld<DT, KS, NF, TK, WAVES, true, false>(xp, cp, cn, total, bpb, N, d, K, ids, s);
+  return launch_smalld<DT, KS, NF, TK, WAVES, false, false>(xp, cp, cn, total, bpb, N, d, K, ids, s);
 }
 
 // Shapes per d: k-steps KS (16 elements each), point fragments NF per wave,
@@ -368,6 +439,7 @@ hipError_t launch_assign_smalld(const void* x, const void* c_lp, const float* cn
                                 int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,
                                 hipStream_t s) {
   if (B == 0 || N == 0) return hipSuccess;
+  if (K < 1) return hipErrorInvalidValue;    // the point-block loop needs a tile
   if (dt == FK_F16) return smalld_dt<FK_F16>(x, c_lp, cnorm, B, N, d, K, ids, s);
   if (dt == FK_BF16) return smalld_dt<FK_BF16>(x, c_lp, cnorm, B, N, d, K, ids, s);
   return hipErrorNotSupported;
