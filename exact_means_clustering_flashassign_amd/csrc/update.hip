@@ -24,15 +24,17 @@
 //             global atomic per non-empty bin, scan, prep, scatter.
 //   segreduce one wave per (run, column slice). A short segment is summed
 //             whole by the wave whose run holds its first position (it may
-//             read up to kSegRun - 1 positions past its run) and finished in
-//             place: c = sum / count, squared move into the wave's partial.
-//             A long segment is summed piecewise, one piece per run it
-//             touches, into fp32 sums with one atomic per element: at most
-//             (number of long clusters + number of runs) * d atomics per
-//             problem, none at all when every cluster is short.
-//   finalize  long clusters: c = sums / count; squared moves into the
-//             block's partial; the last block of a problem to finish sums
-//             that problem's partials in a fixed order into shift[b].
+//             read up to kSegRun - 1 positions past its run) and its mean
+//             (sum / count) is written to its sums row. A long segment is
+//             summed piecewise, one piece per run it touches, into its zeroed
+//             sums row with one fp32 atomic per element: at most (number of
+//             long clusters + number of runs) * d atomics per problem, none
+//             at all when every cluster is short.
+//   finalize  elementwise over (cluster, column) of non-empty clusters:
+//             c = sums row (short: already the mean; long: divided by the
+//             count); with a shift buffer, each block's squared moves go to a
+//             partial, and shift_reduce sums a problem's partials in a fixed
+//             order into shift[b].
 // Empty clusters are never touched, so they keep their centroid. Ids outside
 // [0, K) are skipped: they count nowhere and add to no cluster.
 #include "fk_internal.hpp"

@@ -44,7 +44,7 @@ COPY_TAG = "neg_kernel"
 
 # Kernel sources whose text decides a kernel's counter readings.
 PHASE_SOURCES = {
-    "assign": ("assign.hip", "fk_internal.hpp"),
+    "assign": ("assign.hip", "assign_splitd.hip", "fk_internal.hpp"),
     "update": ("update.hip", "fk_internal.hpp"),
 }
 
