@@ -25,16 +25,17 @@
 //   segreduce one wave per (run, column slice). A short segment is summed
 //             whole by the wave whose run holds its first position (it may
 //             read up to kSegRun - 1 positions past its run) and its mean
-//             (sum / count) is written to its sums row. A long segment is
-//             summed piecewise, one piece per run it touches, into its zeroed
-//             sums row with one fp32 atomic per element: at most (number of
-//             long clusters + number of runs) * d atomics per problem, none
-//             at all when every cluster is short.
-//   finalize  elementwise over (cluster, column) of non-empty clusters:
-//             c = sums row (short: already the mean; long: divided by the
-//             count); with a shift buffer, each block's squared moves go to a
-//             partial, and shift_reduce sums a problem's partials in a fixed
-//             order into shift[b].
+//             (sum / count) is written straight into c, the squared move into
+//             the wave's shift partial. A long segment is summed piecewise,
+//             one piece per run it touches, into its zeroed sums row with one
+//             fp32 atomic per element: at most (number of long clusters +
+//             number of runs) * d atomics per problem, none at all when every
+//             cluster is short.
+//   finalize  elementwise over (cluster, column) of long clusters:
+//             c = sums / count, squared moves into the block's partial; with
+//             a shift buffer, shift_reduce sums a problem's partials (its
+//             segreduce waves', then its finalize blocks') in a fixed order
+//             into shift[b].
 // Empty clusters are never touched, so they keep their centroid. Ids outside
 // [0, K) are skipped: they count nowhere and add to no cluster.
 #include "fk_internal.hpp"
@@ -388,9 +389,9 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
 // read as 16-byte vectors: LPR lanes cover the slice's SPAN columns of a row,
 // so one wave instruction reads R = 64/LPR rows. Inside a batch each
 // segment's rows are added under a 0/1 position weight; when a segment ends,
-// the R row groups are summed with lane shuffles and the sum goes to the
-// cluster's sums row: divided by the count for a short segment (the finished
-// mean), added with atomics for a piece of a long one.
+// the R row groups are summed across lanes and the sum goes out: divided by
+// the count into the cluster's row of c for a short segment (the finished
+// mean), added with atomics to its sums row for a piece of a long one.
 template <int DT>
 __device__ __forceinline__ void widen16(const uint4 v, float* out) {
   if constexpr (DT == FK_F32) {
@@ -445,7 +446,8 @@ template <int DT, int LPR, bool VEC>
 __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     const void* __restrict__ x, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ run_first,
-    float* __restrict__ sums, int N, int d, int K, int runs, int slices, int64_t total_waves) {
+    float* __restrict__ sums, float* __restrict__ c, float* __restrict__ part, int part_stride,
+    int N, int d, int K, int runs, int slices, int64_t total_waves) {
   constexpr int R = 64 / LPR;                    // rows per wave instruction
   constexpr int EB = DT == FK_F32 ? 4 : 2;
   constexpr int EV = 16 / EB;                    // elements per 16-byte vector
@@ -470,6 +472,9 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   const int32_t* ob = offsets + (int64_t)b * (K + 1);
   const char* xb = reinterpret_cast<const char*>(x) + (int64_t)b * N * d * EB;
   float* sb = sums + (int64_t)b * K * d;
+  float* cb = c + (int64_t)b * K * d;
+  float moved = 0.f;                             // squared moves of this wave's short clusters
+  [&]() {
 
   int k = run_first[(int64_t)b * runs + run];
   k = k < 0 ? K : k;
@@ -573,21 +578,40 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
 #pragma unroll
     for (int i = 0; i < EV; ++i) acc[i] = group_sum<LPR>(acc[i]);
     if (g == 0 && colok) {
-      float* row = sb + (int64_t)jk * d + col;
-      if (jcnt > 0) {
+      if (jcnt > 0) {                            // short: the finished mean, straight into c
+        float* row = cb + (int64_t)jk * d + col;
         const float inv = 1.0f / (float)jcnt;
+        float nw[EV];
+#pragma unroll
+        for (int i = 0; i < EV; ++i) nw[i] = acc[i] * inv;
         if constexpr (VEC) {
           // whole 16-byte vectors: col is a multiple of EV and d of EV
+          if (part) {
+#pragma unroll
+            for (int i = 0; i < EV; i += 4) {
+              const float4 o = *reinterpret_cast<const float4*>(row + i);
+              const float dl[4] = {nw[i] - o.x, nw[i + 1] - o.y, nw[i + 2] - o.z, nw[i + 3] - o.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) moved = fmaf(dl[e], dl[e], moved);
+            }
+          }
 #pragma unroll
           for (int i = 0; i < EV; i += 4)
-            *reinterpret_cast<float4*>(row + i) =
-                make_float4(acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv);
+            *reinterpret_cast<float4*>(row + i) = make_float4(nw[i], nw[i + 1], nw[i + 2], nw[i + 3]);
         } else {
 #pragma unroll
-          for (int i = 0; i < EV; ++i)
-            if (col + i < d) row[i] = acc[i] * inv;
+          for (int i = 0; i < EV; ++i) {
+            if (col + i < d) {
+              if (part) {
+                const float dl = nw[i] - row[i];
+                moved = fmaf(dl, dl, moved);
+              }
+              row[i] = nw[i];
+            }
+          }
         }
-      } else {
+      } else {                                   // a piece of a long segment
+        float* row = sb + (int64_t)jk * d + col;
 #pragma unroll
         for (int i = 0; i < EV; ++i)
           if (col + i < d) unsafeAtomicAdd(row + i, acc[i]);
@@ -638,6 +662,11 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     __builtin_amdgcn_sched_barrier(0);
     if (base + BR < E) consume(base + BR, vb);
   }
+  }();
+  if (part) {                                    // every wave writes its slot, zero included
+    moved = wave_sum(moved);
+    if (lane == 0) part[(int64_t)b * part_stride + rem] = moved;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -651,7 +680,7 @@ constexpr int kFinVec = 4;
 template <bool SHIFT>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(
     const float* __restrict__ sums, const int32_t* __restrict__ offsets, float* __restrict__ c,
-    float* __restrict__ part, int d, int K, int blocks_per_batch, bool vec) {
+    float* __restrict__ part, int part_stride, int d, int K, int blocks_per_batch, bool vec) {
   __shared__ float wsum[kThreads / 64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -666,13 +695,12 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     if (vec && e0 + kFinVec <= per) {         // vec: d % kFinVec == 0, c 16-byte aligned
       const int k = (int)(e0 / d);               // the kFinVec elements share a row
       const int lo = ob[k], hi = ob[k + 1];
-      if (hi > lo) {
+      if (is_long(lo, hi)) {
         const float4 sv = *reinterpret_cast<const float4*>(sb + e0);
         const float cnt = (float)(hi - lo);
-        const bool lng = is_long(lo, hi);
         float nw[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) nw[i] = lng ? nw[i] / cnt : nw[i];
+        for (int i = 0; i < 4; ++i) nw[i] = nw[i] / cnt;
         if constexpr (SHIFT) {
           const float4 cv = *reinterpret_cast<const float4*>(cb + e0);
           const float od[4] = {cv.x, cv.y, cv.z, cv.w};
@@ -688,9 +716,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
       for (int64_t e = e0; e < e0 + kFinVec && e < per; ++e) {
         const int k = (int)(e / d);
         const int lo = ob[k], hi = ob[k + 1];
-        if (hi <= lo) continue;
-        const float sv = sb[e];
-        const float nw = is_long(lo, hi) ? sv / (float)(hi - lo) : sv;
+        if (!is_long(lo, hi)) continue;
+        const float nw = sb[e] / (float)(hi - lo);
         if constexpr (SHIFT) {
           const float dl = nw - cb[e];
           moved = fmaf(dl, dl, moved);
@@ -707,7 +734,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
       float t = 0.f;
 #pragma unroll
       for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
-      part[(int64_t)b * blocks_per_batch + j] = t;
+      part[(int64_t)b * part_stride + j] = t;
     }
   }
 }
@@ -798,33 +825,44 @@ int seg_slices_dt(int64_t d) {
 
 template <int DT, int LPR>
 hipError_t run_segreduce(const void* x, const UpdateWs& ws, int64_t B, int64_t N, int64_t d,
-                         int64_t K, hipStream_t s) {
+                         int64_t K, float* c, float* part, int part_stride, hipStream_t s) {
   constexpr int EB = DT == FK_F32 ? 4 : 2;
   const int runs = (int)((N + kSegRun - 1) / kSegRun);
   const int slices = seg_slices_dt<DT>(d);
   const int64_t total = B * runs * slices;
   const int64_t grid = (total + 3) / 4;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const bool vec = (d * EB) % 16 == 0 && ((uintptr_t)x % 16) == 0;
+  // vector path: 16-byte x rows and 16-byte-aligned rows of c
+  const bool vec = (d * EB) % 16 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)c % 16) == 0;
   if (vec)
     segreduce_kernel<DT, LPR, true><<<(unsigned)grid, kThreads, 0, s>>>(
-        x, ws.perm, ws.offsets, ws.run_first, ws.sums, (int)N, (int)d, (int)K, runs, slices,
-        total);
+        x, ws.perm, ws.offsets, ws.run_first, ws.sums, c, part, part_stride, (int)N, (int)d,
+        (int)K, runs, slices, total);
   else
     segreduce_kernel<DT, LPR, false><<<(unsigned)grid, kThreads, 0, s>>>(
-        x, ws.perm, ws.offsets, ws.run_first, ws.sums, (int)N, (int)d, (int)K, runs, slices,
-        total);
+        x, ws.perm, ws.offsets, ws.run_first, ws.sums, c, part, part_stride, (int)N, (int)d,
+        (int)K, runs, slices, total);
   return hipGetLastError();
 }
 
+// part: per-wave squared moves of short clusters (null: no shift), wave w of
+// problem b at part[b * part_stride + w].
 template <int DT>
 hipError_t segreduce_dt(const void* x, const UpdateWs& ws, int64_t B, int64_t N, int64_t d,
-                        int64_t K, hipStream_t s) {
+                        int64_t K, float* c, float* part, int part_stride, hipStream_t s) {
   switch (seg_lanes<DT>(d)) {
-    case 4: return run_segreduce<DT, 4>(x, ws, B, N, d, K, s);
-    case 8: return run_segreduce<DT, 8>(x, ws, B, N, d, K, s);
-    default: return run_segreduce<DT, 16>(x, ws, B, N, d, K, s);
+    case 4: return run_segreduce<DT, 4>(x, ws, B, N, d, K, c, part, part_stride, s);
+    case 8: return run_segreduce<DT, 8>(x, ws, B, N, d, K, c, part, part_stride, s);
+    default: return run_segreduce<DT, 16>(x, ws, B, N, d, K, c, part, part_stride, s);
   }
+}
+
+// segreduce waves per problem (one per run and column slice)
+int64_t seg_waves(int dt, int64_t N, int64_t d) {
+  const int64_t runs = (N + kSegRun - 1) / kSegRun;
+  if (dt == FK_F16) return runs * seg_slices_dt<FK_F16>(d);
+  if (dt == FK_BF16) return runs * seg_slices_dt<FK_BF16>(d);
+  return runs * seg_slices_dt<FK_F32>(d);
 }
 
 }  // namespace
@@ -852,7 +890,8 @@ size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K) {
   const int64_t runs = (N + kSegRun - 1) / kSegRun;
   return align256((size_t)B * K * d * 4) + align256((size_t)B * (K + 1) * 4) +
          align256((size_t)B * K * 4) + align256((size_t)B * N * 4) +
-         align256((size_t)B * runs * 4) + align256((size_t)B * fin_blocks(K, d) * 4) +
+         align256((size_t)B * runs * 4) +
+         align256((size_t)B * (seg_waves(FK_F32, N, d) + fin_blocks(K, d)) * 4) +
          align256((size_t)B * split_groups(B, N, K) * K * 4);
 }
 
@@ -871,7 +910,7 @@ UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K)
   w.run_first = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)B * runs * 4);
   w.part = reinterpret_cast<float*>(p);
-  p += align256((size_t)B * fin_blocks(K, d) * 4);
+  p += align256((size_t)B * (seg_waves(FK_F32, N, d) + fin_blocks(K, d)) * 4);
   w.hist = reinterpret_cast<int32_t*>(p);
   return w;
 }
@@ -945,24 +984,29 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
     FK_CHECK(hipGetLastError());
     FK_CHECK(run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
   }
+  // shift partials of a problem: its segreduce waves, then its finalize blocks
+  const int64_t sw = seg_waves(dt, N, d);
+  const int64_t pstride = sw + fb;
+  if (pstride > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  float* spart = shift ? ws.part : nullptr;
   if (dt == FK_F16)
-    FK_CHECK(segreduce_dt<FK_F16>(x, ws, B, N, d, K, s));
+    FK_CHECK(segreduce_dt<FK_F16>(x, ws, B, N, d, K, c, spart, (int)pstride, s));
   else if (dt == FK_BF16)
-    FK_CHECK(segreduce_dt<FK_BF16>(x, ws, B, N, d, K, s));
+    FK_CHECK(segreduce_dt<FK_BF16>(x, ws, B, N, d, K, c, spart, (int)pstride, s));
   else
-    FK_CHECK(segreduce_dt<FK_F32>(x, ws, B, N, d, K, s));
+    FK_CHECK(segreduce_dt<FK_F32>(x, ws, B, N, d, K, c, spart, (int)pstride, s));
   const int64_t grid = B * fb;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const bool fvec = d % kFinVec == 0 && ((uintptr_t)c % 16) == 0;
   if (!shift) {                                  // the caller does not need the shift
-    finalize_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(ws.sums, ws.offsets, c, ws.part,
-                                                               (int)d, (int)K, (int)fb, fvec);
+    finalize_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(
+        ws.sums, ws.offsets, c, ws.part, 0, (int)d, (int)K, (int)fb, fvec);
     return hipGetLastError();
   }
-  finalize_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(ws.sums, ws.offsets, c, ws.part,
-                                                            (int)d, (int)K, (int)fb, fvec);
+  finalize_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(
+      ws.sums, ws.offsets, c, ws.part + sw, (int)pstride, (int)d, (int)K, (int)fb, fvec);
   FK_CHECK(hipGetLastError());
-  shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, (int)fb);
+  shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, (int)pstride);
   return hipGetLastError();
 }
 

@@ -56,14 +56,16 @@ def test_workspace_size(lib):
     ws = lib.fk_workspace_size
     big = ws(1, 32, 75600, 128, 1000)
     # sums, offsets, cursor, perm, run starts (one per 256 sorted positions),
-    # shift partials (one per finalize block of 1024 centroid elements), the
-    # split sort's count matrix (16 chunks per problem here), rounded
-    # centroids, norms, counts, shift
+    # shift partials (one per segment-reduce wave -- a run and a column slice,
+    # sized for fp32 rows, 64 columns per slice -- and one per finalize block
+    # of 1024 centroid elements), the split sort's count matrix (16 chunks per
+    # problem here), rounded centroids, norms, counts, shift
     runs = -(-75600 // 256)
+    slices = -(-128 // 64)
     fb = -(-1000 * 128 // 1024)
     G = 16
     need = 32 * 1000 * 128 * 4 + 32 * 1001 * 4 + 32 * 1000 * 4 + 32 * 75600 * 4 + \
-        32 * runs * 4 + 32 * fb * 4 + 32 * G * 1000 * 4 + \
+        32 * runs * 4 + 32 * (runs * slices + fb) * 4 + 32 * G * 1000 * 4 + \
         32 * 1000 * 128 * 2 + 32 * 1000 * 4 * 2 + 32 * 4
     assert need <= big <= need + 11 * 256
     assert ws(1, 32, 75600, 128, 1000) < ws(0, 32, 75600, 128, 1000)   # fp32 copy is larger
