@@ -47,6 +47,15 @@ struct Argmax {
   float saved[16];
 };
 
+// v_max3_f32 of three finite scores. The compiler turns a two-operand fmaxf
+// of MFMA results into canonicalising maxes; this keeps the tree at one
+// instruction per two new scores.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Part `part` (0..7) of draining accumulator `acc` of subtile g into st.
 // The work is split so it can be spread over the k-steps of the next
 // subtile: parts 0-3 build the max tree, part 4 compares, parts 4-7 save.
@@ -54,20 +63,20 @@ __device__ __forceinline__ void drain_part(const floatx16_t& acc, int part, int 
                                            float (&m)[2], bool& gt) {
   switch (part) {
     case 0:
-      m[0] = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
-      m[1] = fmaxf(fmaxf(acc[3], acc[4]), acc[5]);
+      m[0] = vmax3(acc[0], acc[1], acc[2]);
+      m[1] = vmax3(acc[3], acc[4], acc[5]);
       break;
     case 1:
-      m[0] = fmaxf(fmaxf(m[0], acc[6]), acc[7]);
-      m[1] = fmaxf(fmaxf(m[1], acc[8]), acc[9]);
+      m[0] = vmax3(m[0], acc[6], acc[7]);
+      m[1] = vmax3(m[1], acc[8], acc[9]);
       break;
     case 2:
-      m[0] = fmaxf(fmaxf(m[0], acc[10]), acc[11]);
-      m[1] = fmaxf(fmaxf(m[1], acc[12]), acc[13]);
+      m[0] = vmax3(m[0], acc[10], acc[11]);
+      m[1] = vmax3(m[1], acc[12], acc[13]);
       break;
     case 3:
-      m[0] = fmaxf(fmaxf(m[0], m[1]), acc[14]);
-      m[0] = fmaxf(m[0], acc[15]);
+      m[0] = vmax3(m[0], m[1], acc[14]);
+      m[0] = vmax3(m[0], acc[15], acc[15]);
       break;
     case 4:
       gt = m[0] > st.best;

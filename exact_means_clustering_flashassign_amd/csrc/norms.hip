@@ -1,9 +1,10 @@
 // Centroid precompute and small element-wise kernels.
 //
-// norms: one wave per centroid row. Each lane rounds its share of the fp32
-// master row to the element type (nearest-even), stores the rounded copy that
-// the assignment reads, and accumulates the square of the *rounded* value in
-// fp32; a wave reduction gives ||c_lp||^2. The assignment then measures the
+// norms: a group of lanes per centroid row (16-byte loads when d % 4 == 0,
+// else one wave per row). Each lane rounds its share of the fp32 master row
+// to the element type (nearest-even), stores the rounded copy that the
+// assignment reads, and accumulates the square of the *rounded* value in
+// fp32; a reduction over the group gives ||c_lp||^2. The assignment then measures the
 // true distance to the centroid it actually uses. The ||c||^2 term is the
 // only centroid-side quantity the fused distance needs besides x.c
 // ("Flash-KMeans：IO感知的精确K-Means…", section "它攻克的两大瓶颈").
@@ -33,6 +34,62 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ c,
   }
   acc = wave_sum(acc);
   if (lane == 0) cnorm[row] = acc;
+}
+
+// Vector form (d % 4 == 0, 16-byte aligned c, 8-byte aligned c_lp): LPR lanes
+// per row, 4 elements per lane per step, so one wave covers 64/LPR rows; the
+// row's squares are summed over its lane group.
+template <int DT, int LPR>
+__global__ __launch_bounds__(256) void norms_vec_kernel(const float* __restrict__ c,
+                                                        uint16_t* __restrict__ c_lp,
+                                                        float* __restrict__ cnorm, int64_t rows,
+                                                        int d) {
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63, li = lane % LPR;
+  const int64_t row = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const bool ok = row < rows;
+  float acc = 0.f;
+  if (ok) {
+    const float* src = c + row * d;
+    uint16_t* dst = c_lp + row * d;
+    for (int j = li * 4; j < d; j += LPR * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + j);
+      const uint16_t h[4] = {Elem<DT>::narrow(v.x), Elem<DT>::narrow(v.y), Elem<DT>::narrow(v.z),
+                             Elem<DT>::narrow(v.w)};
+      *reinterpret_cast<uint2*>(dst + j) =
+          make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float r = Elem<DT>::widen(h[i]);
+        acc = fmaf(r, r, acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (ok && li == 0) cnorm[row] = acc;
+}
+
+template <int DT, int LPR>
+hipError_t run_norms_vec(const float* c, uint16_t* c_lp, float* cnorm, int64_t rows, int64_t d,
+                         hipStream_t s) {
+  constexpr int RPB = kWaves * (64 / LPR);       // rows per block
+  const int64_t grid = (rows + RPB - 1) / RPB;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  norms_vec_kernel<DT, LPR><<<(unsigned)grid, 256, 0, s>>>(c, c_lp, cnorm, rows, (int)d);
+  return hipGetLastError();
+}
+
+// lanes per row: the vectors of a row, rounded up to a power of two in [4, 64]
+template <int DT>
+hipError_t norms_vec_dt(const float* c, uint16_t* c_lp, float* cnorm, int64_t rows, int64_t d,
+                        hipStream_t s) {
+  const int64_t nv = d / 4;
+  if (nv <= 4) return run_norms_vec<DT, 4>(c, c_lp, cnorm, rows, d, s);
+  if (nv <= 8) return run_norms_vec<DT, 8>(c, c_lp, cnorm, rows, d, s);
+  if (nv <= 16) return run_norms_vec<DT, 16>(c, c_lp, cnorm, rows, d, s);
+  if (nv <= 32) return run_norms_vec<DT, 32>(c, c_lp, cnorm, rows, d, s);
+  return run_norms_vec<DT, 64>(c, c_lp, cnorm, rows, d, s);
 }
 
 __global__ __launch_bounds__(256) void norms_f32_kernel(const float* __restrict__ c,
@@ -87,6 +144,10 @@ unsigned grid_for(int64_t count) {
 hipError_t launch_norms(const float* c, void* c_lp, float* cnorm, int dt, int64_t rows,
                         int64_t d, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  const bool vec = d % 4 == 0 && d <= 0x7FFFFFFF && ((uintptr_t)c % 16) == 0 &&
+                   ((uintptr_t)c_lp % 8) == 0;
+  if (vec && dt == FK_F16) return norms_vec_dt<FK_F16>(c, (uint16_t*)c_lp, cnorm, rows, d, s);
+  if (vec && dt == FK_BF16) return norms_vec_dt<FK_BF16>(c, (uint16_t*)c_lp, cnorm, rows, d, s);
   const unsigned grid = (unsigned)((rows + kWaves - 1) / kWaves);
   if (dt == FK_F16)
     norms_kernel<FK_F16><<<grid, 256, 0, s>>>(c, (uint16_t*)c_lp, cnorm, rows, d);

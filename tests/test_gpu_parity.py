@@ -56,11 +56,12 @@ def make_centroids(x64, K, dtype, seed, jitter=0.25, dup=True):
 # ---------------------------------------------------------------------------
 # fk_norms
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
-def test_norms_rounding_and_sqnorms(fk, dtype):
+@pytest.mark.parametrize("dtype,d", [("f16", 100), ("bf16", 100), ("f32", 100), ("f16", 99),
+                                     ("bf16", 1024), ("f16", 4), ("bf16", 30)])
+def test_norms_rounding_and_sqnorms(fk, dtype, d):
     torch = _torch()
-    rng = np.random.default_rng(100)
-    B, K, d = 3, 77, 100
+    rng = np.random.default_rng(100 + d)
+    B, K = 3, 77
     c = (rng.standard_normal((B, K, d)) * 10.0 ** rng.integers(-3, 3, (B, K, 1))).astype(np.float32)
     if dtype != "f32":
         # exact halfway points between neighbours, and values next to them
