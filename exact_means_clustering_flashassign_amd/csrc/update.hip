@@ -59,6 +59,16 @@ __device__ __forceinline__ void mark_runs(int32_t* rf, int k, int lo, int hi) {
   for (int64_t r = (lo + (int64_t)kSegRun - 1) / kSegRun; r * kSegRun < hi; ++r) rf[r] = k;
 }
 
+// A long cluster's sums row, zeroed by one thread before its pieces are added
+// (rows start 16-byte aligned when d % 4 == 0: the buffer is 256-byte aligned).
+__device__ __forceinline__ void zero_row(float* row, int d) {
+  if (d % 4 == 0) {
+    for (int j = 0; j < d; j += 4) *reinterpret_cast<float4*>(row + j) = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    for (int j = 0; j < d; ++j) row[j] = 0.f;
+  }
+}
+
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void zero_kernel(int32_t* __restrict__ p, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -162,7 +172,6 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   extern __shared__ int32_t cnt[];              // K + 1
   __shared__ int32_t wtot[kSortThreads / 64];
   const int b = blockIdx.x, t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
   int32_t* hb = H + (int64_t)b * G * K;
   int32_t* cb = counts + (int64_t)b * K;
   if (G > 0) {
@@ -186,11 +195,13 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   int run = block_exclusive_scan(s, wtot, total);
   int32_t* ob = offsets + (int64_t)b * (K + 1);
   int32_t* rf = run_first + (int64_t)b * runs;
+  float* sb = sums + (int64_t)b * K * d;
   for (int i = lo; i < hi; ++i) {
     const int c = cnt[i];
     if (G > 0) cb[i] = c;
     cnt[i] = run;
     if (G > 0 && c > 0) mark_runs(rf, i, run, run + c);
+    if (G > 0 && is_long(run, run + c)) zero_row(sb + (int64_t)i * d, d);
     run += c;
   }
   if (t == 0) cnt[K] = total;
@@ -199,12 +210,6 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   if (G == 0) return;                            // run starts and rows: prep_kernel
   for (int64_t r = (total + (int64_t)kSegRun - 1) / kSegRun + t; r < runs; r += kSortThreads)
     rf[r] = K;                                   // runs past the last valid position
-  float* sb = sums + (int64_t)b * K * d;
-  for (int k = w; k < K; k += kSortThreads / 64) {
-    if (!is_long(cnt[k], cnt[k + 1])) continue;
-    float* row = sb + (int64_t)k * d;
-    for (int j = lane; j < d; j += 64) row[j] = 0.f;
-  }
 }
 
 // Large G*K: column prefixes on a grid, one thread per (problem, cluster).
