@@ -49,6 +49,7 @@ constexpr int kSegRun = 256;                  // sorted positions per segreduce 
 constexpr int kSortThreads = 1024;
 constexpr int kSortUnroll = 16;               // ids in flight per thread in the sort kernels
 constexpr int64_t kFusedOffsetsMax = 1 << 16; // G*K up to this: one offsets block per problem
+constexpr size_t kSortedScatterLds = 96 * 1024;  // LDS budget of the sorted scatter
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -246,6 +247,76 @@ __global__ __launch_bounds__(kSortThreads) void scatter2_kernel(
     for (int q = 0; q < kSortUnroll; ++q)
       if ((unsigned)kk[q] < (unsigned)K) pb[atomicAdd(&bins[kk[q]], 1)] = m + q * kSortThreads + t;
   }
+}
+
+// scatter2, sorted form (when 2K + 2*chunk ints fit LDS): the chunk is
+// counting-sorted in LDS first, so the perm stores of one cluster's piece go
+// out as consecutive addresses instead of one scattered 4-byte store per
+// point.
+//   cur[k]  local cursor, from the chunk's exclusive prefix of cluster sizes
+//   gof[k]  global position of the chunk's piece of cluster k minus its local
+//           start: perm[gof[k] + p] = sidx[p] for local sorted position p
+__global__ __launch_bounds__(kSortThreads) void scatter2s_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ H,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int N, int K, int G,
+    int chunk) {
+  extern __shared__ int32_t sm[];
+  int32_t* cur = sm;
+  int32_t* gof = sm + K;
+  int32_t* skey = sm + 2 * K;
+  int32_t* sidx = skey + chunk;
+  __shared__ int32_t wtot[kSortThreads / 64];
+  const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
+  const int32_t* hr = H + ((int64_t)b * G + g) * K;
+  const int32_t* ob = offsets + (int64_t)b * (K + 1);
+  const int32_t* ib = ids + (int64_t)b * N;
+  const int n0 = g * chunk, n1 = min(n0 + chunk, N);
+  for (int i = t; i < K; i += kSortThreads) cur[i] = 0;
+  __syncthreads();
+  for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
+    int kk[kSortUnroll];
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q) {
+      const int n = m + q * kSortThreads + t;
+      kk[q] = n < n1 ? ib[n] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q)
+      if ((unsigned)kk[q] < (unsigned)K) atomicAdd(&cur[kk[q]], 1);
+  }
+  __syncthreads();
+  const int per = (K + kSortThreads - 1) / kSortThreads;
+  const int lo = min(t * per, K), hi = min(lo + per, K);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += cur[i];
+  int total;
+  int run = block_exclusive_scan(sum, wtot, total);
+  for (int i = lo; i < hi; ++i) {
+    const int c = cur[i];
+    cur[i] = run;
+    gof[i] = ob[i] + hr[i] - run;
+    run += c;
+  }
+  __syncthreads();
+  for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
+    int kk[kSortUnroll];
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q) {
+      const int n = m + q * kSortThreads + t;
+      kk[q] = n < n1 ? ib[n] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q) {
+      if ((unsigned)kk[q] < (unsigned)K) {
+        const int p = atomicAdd(&cur[kk[q]], 1);
+        skey[p] = kk[q];
+        sidx[p] = m + q * kSortThreads + t;
+      }
+    }
+  }
+  __syncthreads();
+  int32_t* pb = perm + (int64_t)b * N;
+  for (int p = t; p < total; p += kSortThreads) pb[gof[skey[p]] + p] = sidx[p];
 }
 
 // ---------------------------------------------------------------------------
@@ -971,9 +1042,21 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
                                                            (int)K, (int)d, runs, pb);
       FK_CHECK(hipGetLastError());
     }
-    scatter2_kernel<<<(unsigned)(B * G), kSortThreads, lds, s>>>(ids, ws.hist, ws.offsets,
-                                                                ws.perm, (int)N, (int)K, G,
-                                                                chunk);
+    const size_t lds_sorted = (size_t)(2 * K + 2 * (int64_t)chunk) * sizeof(int32_t);
+    if (lds_sorted <= kSortedScatterLds) {
+      static bool sattr = false;
+      if (!sattr && lds_sorted > 65536) {
+        (void)hipFuncSetAttribute((const void*)scatter2s_kernel,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kSortedScatterLds);
+        (void)hipGetLastError();
+        sattr = true;
+      }
+      scatter2s_kernel<<<(unsigned)(B * G), kSortThreads, lds_sorted, s>>>(
+          ids, ws.hist, ws.offsets, ws.perm, (int)N, (int)K, G, chunk);
+    } else {
+      scatter2_kernel<<<(unsigned)(B * G), kSortThreads, lds, s>>>(
+          ids, ws.hist, ws.offsets, ws.perm, (int)N, (int)K, G, chunk);
+    }
     FK_CHECK(hipGetLastError());
   } else {
     int64_t g = (B * K + kThreads - 1) / kThreads;
