@@ -50,6 +50,7 @@ constexpr int kSortThreads = 1024;
 constexpr int kSortUnroll = 16;               // ids in flight per thread in the sort kernels
 constexpr int64_t kFusedOffsetsMax = 1 << 16; // G*K up to this: one offsets block per problem
 constexpr size_t kSortedScatterLds = 96 * 1024;  // LDS budget of the sorted scatter
+constexpr int kLongList = 1024;               // long clusters listed per problem by offsets
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -172,7 +173,10 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
     int32_t* __restrict__ run_first, float* __restrict__ sums, int K, int d, int G, int runs) {
   extern __shared__ int32_t cnt[];              // K + 1
   __shared__ int32_t wtot[kSortThreads / 64];
+  __shared__ int32_t longs[kLongList];           // long clusters, zeroed by the whole block
+  __shared__ int32_t nlong;
   const int b = blockIdx.x, t = threadIdx.x;
+  if (t == 0) nlong = 0;
   int32_t* hb = H + (int64_t)b * G * K;
   int32_t* cb = counts + (int64_t)b * K;
   if (G > 0) {
@@ -202,7 +206,11 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
     if (G > 0) cb[i] = c;
     cnt[i] = run;
     if (G > 0 && c > 0) mark_runs(rf, i, run, run + c);
-    if (G > 0 && is_long(run, run + c)) zero_row(sb + (int64_t)i * d, d);
+    if (G > 0 && is_long(run, run + c)) {
+      const int q = atomicAdd(&nlong, 1);
+      if (q < kLongList) longs[q] = i;
+      else zero_row(sb + (int64_t)i * d, d);     // past the list: this thread alone
+    }
     run += c;
   }
   if (t == 0) cnt[K] = total;
@@ -211,6 +219,17 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   if (G == 0) return;                            // run starts and rows: prep_kernel
   for (int64_t r = (total + (int64_t)kSegRun - 1) / kSegRun + t; r < runs; r += kSortThreads)
     rf[r] = K;                                   // runs past the last valid position
+  // the listed long clusters' sums rows, spread over the block
+  const int nl = min(nlong, kLongList);
+  if (d % 4 == 0) {
+    const int nv = d / 4;
+    for (int64_t e = t; e < (int64_t)nl * nv; e += kSortThreads) {
+      const int k = longs[e / nv];
+      *reinterpret_cast<float4*>(sb + (int64_t)k * d + (e % nv) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  } else {
+    for (int64_t e = t; e < (int64_t)nl * d; e += kSortThreads) sb[(int64_t)longs[e / d] * d + e % d] = 0.f;
+  }
 }
 
 // Large G*K: column prefixes on a grid, one thread per (problem, cluster).
@@ -1042,8 +1061,10 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
                                                            (int)K, (int)d, runs, pb);
       FK_CHECK(hipGetLastError());
     }
+    // the sorted form pays off with enough chunks to fill the chip; with few,
+    // its extra passes cost more than the scattered stores
     const size_t lds_sorted = (size_t)(2 * K + 2 * (int64_t)chunk) * sizeof(int32_t);
-    if (lds_sorted <= kSortedScatterLds) {
+    if (lds_sorted <= kSortedScatterLds && B * G >= 256) {
       static bool sattr = false;
       if (!sattr && lds_sorted > 65536) {
         (void)hipFuncSetAttribute((const void*)scatter2s_kernel,
