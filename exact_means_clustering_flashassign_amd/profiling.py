@@ -61,7 +61,7 @@ def phase_of(kernel: str) -> str:
     k = kernel.replace("(anonymous namespace)", "").split("(")[0]
     if "assign_" in k:
         return "assign"
-    if "norms_kernel" in k:
+    if "norms_" in k and "_kernel" in k:
         return "norms"
     if COPY_TAG in k:
         return "copy"

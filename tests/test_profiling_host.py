@@ -19,6 +19,7 @@ def test_phase_classification():
     assert P.phase_of("void fk::(anonymous namespace)::assign_smalld_kernel<1, 8>(int)") == "assign"
     assert P.phase_of("void fk::(anonymous namespace)::segreduce_kernel<1>(void const*)") == "update"
     assert P.phase_of("fk::(anonymous namespace)::norms_kernel<1>(float const*)") == "norms"
+    assert P.phase_of("void fk::(anonymous namespace)::norms_vec_kernel<1, 32>(float const*)") == "norms"
     assert P.phase_of("void fk::(anonymous namespace)::widen_kernel<1>(unsigned short const*)") == "setup"
     assert P.phase_of("void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda>") == "copy"
     assert P.phase_of("void at::native::distribution_elementwise_grid_stride_kernel<float>") == "other"
