@@ -900,14 +900,15 @@ hipError_t run_hist_scatter(const int32_t* ids, int32_t* counts, int32_t* cursor
   } while (0)
 
 // Lanes per row slice: enough 16-byte vectors for the row, as a power of two,
-// at most 16 (a 256-byte slice); wider rows are cut into column slices, each
-// its own wave, so a problem with few points still fills the machine.
+// from 4 to 8 (a 128-byte slice, one cache line); wider rows are cut into
+// column slices, each its own wave, so a problem with few points still fills
+// the machine. 8 lanes beat 16 (more waves in flight, one line per row read).
 template <int DT>
 int seg_lanes(int64_t d) {
   constexpr int EV = DT == FK_F32 ? 4 : 8;
   const int64_t nvec = (d + EV - 1) / EV;
   int l = 4;
-  while (l < 16 && l < nvec) l <<= 1;
+  while (l < 8 && l < nvec) l <<= 1;
   return l;
 }
 

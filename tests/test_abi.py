@@ -57,11 +57,11 @@ def test_workspace_size(lib):
     big = ws(1, 32, 75600, 128, 1000)
     # sums, offsets, cursor, perm, run starts (one per 256 sorted positions),
     # shift partials (one per segment-reduce wave -- a run and a column slice,
-    # sized for fp32 rows, 64 columns per slice -- and one per finalize block
+    # sized for fp32 rows, 32 columns per slice -- and one per finalize block
     # of 1024 centroid elements), the split sort's count matrix (16 chunks per
     # problem here), rounded centroids, norms, counts, shift
     runs = -(-75600 // 256)
-    slices = -(-128 // 64)
+    slices = -(-128 // 32)
     fb = -(-1000 * 128 // 1024)
     G = 16
     need = 32 * 1000 * 128 * 4 + 32 * 1001 * 4 + 32 * 1000 * 4 + 32 * 75600 * 4 + \
