@@ -147,6 +147,7 @@ struct UpdateWs {
   int32_t* run_first;   // (B,runs) cluster holding each run's first position
   float* part;          // (B, finalize blocks) partial squared moves
   int32_t* hist;        // (B, G, K) per-chunk counts of the split sort
+  int32_t* has_long;    // (B) nonzero when the problem has a long cluster
 };
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K);
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K);

@@ -170,7 +170,8 @@ __device__ __forceinline__ int column_prefix(int32_t* hb, int64_t K, int G, int 
 // starts and zeroed long rows; G == 0: counts given, offsets only.
 __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
     int32_t* __restrict__ H, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ run_first, float* __restrict__ sums, int K, int d, int G, int runs) {
+    int32_t* __restrict__ run_first, float* __restrict__ sums, int32_t* __restrict__ has_long,
+    int K, int d, int G, int runs) {
   extern __shared__ int32_t cnt[];              // K + 1
   __shared__ int32_t wtot[kSortThreads / 64];
   __shared__ int32_t longs[kLongList];           // long clusters, zeroed by the whole block
@@ -216,7 +217,8 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   if (t == 0) cnt[K] = total;
   __syncthreads();
   for (int k = t; k <= K; k += kSortThreads) ob[k] = cnt[k];   // coalesced
-  if (G == 0) return;                            // run starts and rows: prep_kernel
+  if (G == 0) return;                            // run starts, rows, flag: prep_kernel
+  if (t == 0) has_long[b] = nlong;
   for (int64_t r = (total + (int64_t)kSegRun - 1) / kSegRun + t; r < runs; r += kSortThreads)
     rf[r] = K;                                   // runs past the last valid position
   // the listed long clusters' sums rows, spread over the block
@@ -401,11 +403,13 @@ __global__ __launch_bounds__(kSortThreads) void scan_kernel(const int32_t* __res
 // the sums row of a long cluster; runs past the last position get K.
 __global__ __launch_bounds__(kThreads) void prep_kernel(const int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ run_first,
-                                                        float* __restrict__ sums, int K, int d,
-                                                        int runs, int blocks_per_batch) {
+                                                        float* __restrict__ sums,
+                                                        int32_t* __restrict__ has_long, int K,
+                                                        int d, int runs, int blocks_per_batch) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int b = blockIdx.x / blocks_per_batch;
   const int j = blockIdx.x % blocks_per_batch;
+  if (j == 0 && threadIdx.x == 0) has_long[b] = 1;   // not counted here: finalize checks all
   const int32_t* ob = offsets + (int64_t)b * (K + 1);
   int32_t* rf = run_first + (int64_t)b * runs;
   const int total = ob[K];
@@ -775,11 +779,16 @@ constexpr int kFinVec = 4;
 template <bool SHIFT>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(
     const float* __restrict__ sums, const int32_t* __restrict__ offsets, float* __restrict__ c,
-    float* __restrict__ part, int part_stride, int d, int K, int blocks_per_batch, bool vec) {
+    float* __restrict__ part, int part_stride, const int32_t* __restrict__ has_long, int d, int K,
+    int blocks_per_batch, bool vec) {
   __shared__ float wsum[kThreads / 64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x / blocks_per_batch, j = blockIdx.x % blocks_per_batch;
+  if (!has_long[b]) {                            // nothing to finish in this problem
+    if (SHIFT && threadIdx.x == 0) part[(int64_t)b * part_stride + j] = 0.f;
+    return;
+  }
   const int64_t per = (int64_t)K * d;
   const int64_t e0 = ((int64_t)j * kThreads + threadIdx.x) * kFinVec;
   const int32_t* ob = offsets + (int64_t)b * (K + 1);
@@ -988,7 +997,7 @@ size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K) {
          align256((size_t)B * K * 4) + align256((size_t)B * N * 4) +
          align256((size_t)B * runs * 4) +
          align256((size_t)B * (seg_waves(FK_F32, N, d) + fin_blocks(K, d)) * 4) +
-         align256((size_t)B * split_groups(B, N, K) * K * 4);
+         align256((size_t)B * split_groups(B, N, K) * K * 4) + align256((size_t)B * 4);
 }
 
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K) {
@@ -1008,6 +1017,8 @@ UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K)
   w.part = reinterpret_cast<float*>(p);
   p += align256((size_t)B * (seg_waves(FK_F32, N, d) + fin_blocks(K, d)) * 4);
   w.hist = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)B * split_groups(B, N, K) * K * 4);
+  w.has_long = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
@@ -1045,8 +1056,8 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
     FK_CHECK(hipGetLastError());
     if ((int64_t)G * K <= kFusedOffsetsMax) {
       offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
-                                                            ws.run_first, ws.sums, (int)K, (int)d,
-                                                            G, runs);
+                                                            ws.run_first, ws.sums, ws.has_long,
+                                                            (int)K, (int)d, G, runs);
       FK_CHECK(hipGetLastError());
     } else {
       const int kblocks = (int)((K + kThreads - 1) / kThreads);
@@ -1054,12 +1065,12 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
                                                                   kblocks);
       FK_CHECK(hipGetLastError());
       offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
-                                                             ws.run_first, ws.sums, (int)K,
-                                                             (int)d, 0, runs);
+                                                             ws.run_first, ws.sums, ws.has_long,
+                                                             (int)K, (int)d, 0, runs);
       FK_CHECK(hipGetLastError());
       const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);
       prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.sums,
-                                                           (int)K, (int)d, runs, pb);
+                                                           ws.has_long, (int)K, (int)d, runs, pb);
       FK_CHECK(hipGetLastError());
     }
     // the sorted form pays off with enough chunks to fill the chip; with few,
@@ -1090,7 +1101,7 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
     FK_CHECK(hipGetLastError());
     const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);   // blocks per problem
     prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.sums,
-                                                         (int)K, (int)d, runs, pb);
+                                                         ws.has_long, (int)K, (int)d, runs, pb);
     FK_CHECK(hipGetLastError());
     FK_CHECK(run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
   }
@@ -1110,11 +1121,12 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
   const bool fvec = d % kFinVec == 0 && ((uintptr_t)c % 16) == 0;
   if (!shift) {                                  // the caller does not need the shift
     finalize_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(
-        ws.sums, ws.offsets, c, ws.part, 0, (int)d, (int)K, (int)fb, fvec);
+        ws.sums, ws.offsets, c, ws.part, 0, ws.has_long, (int)d, (int)K, (int)fb, fvec);
     return hipGetLastError();
   }
   finalize_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(
-      ws.sums, ws.offsets, c, ws.part + sw, (int)pstride, (int)d, (int)K, (int)fb, fvec);
+      ws.sums, ws.offsets, c, ws.part + sw, (int)pstride, ws.has_long, (int)d, (int)K, (int)fb,
+      fvec);
   FK_CHECK(hipGetLastError());
   shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, (int)pstride);
   return hipGetLastError();

@@ -59,15 +59,16 @@ def test_workspace_size(lib):
     # shift partials (one per segment-reduce wave -- a run and a column slice,
     # sized for fp32 rows, 32 columns per slice -- and one per finalize block
     # of 1024 centroid elements), the split sort's count matrix (16 chunks per
-    # problem here), rounded centroids, norms, counts, shift
+    # problem here), a long-cluster flag per problem, rounded centroids, norms,
+    # counts, shift
     runs = -(-75600 // 256)
     slices = -(-128 // 32)
     fb = -(-1000 * 128 // 1024)
     G = 16
     need = 32 * 1000 * 128 * 4 + 32 * 1001 * 4 + 32 * 1000 * 4 + 32 * 75600 * 4 + \
-        32 * runs * 4 + 32 * (runs * slices + fb) * 4 + 32 * G * 1000 * 4 + \
+        32 * runs * 4 + 32 * (runs * slices + fb) * 4 + 32 * G * 1000 * 4 + 32 * 4 + \
         32 * 1000 * 128 * 2 + 32 * 1000 * 4 * 2 + 32 * 4
-    assert need <= big <= need + 11 * 256
+    assert need <= big <= need + 12 * 256
     assert ws(1, 32, 75600, 128, 1000) < ws(0, 32, 75600, 128, 1000)   # fp32 copy is larger
     for bad in [(7, 1, 10, 4, 2), (1, -1, 10, 4, 2), (1, 1, -1, 4, 2), (1, 1, 10, 0, 2),
                 (1, 1, 10, 4, 0), (1, 1, 1 << 31, 4, 2), (1, 1, 10, 4, 1 << 31)]:
