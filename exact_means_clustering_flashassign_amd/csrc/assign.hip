@@ -18,6 +18,8 @@
 // of those rows, so the accumulator is the score itself. Each lane holds 16
 // centroid scores for one point; the running max stays in-lane across all
 // tiles and one lane swap at the end merges the two lanes that share a point.
+// The running max works on scores whose 4 low mantissa bits carry the row
+// slot, so one v_max3 tree gives the maximum and where it is.
 //
 // The split-D path (d > 512) lives in assign_splitd.hip.
 //
@@ -31,21 +33,43 @@ namespace {
 
 constexpr int kThreads = 256;   // fp32 kernel block
 
+// Word 3 of a raw (unformatted, stride 0) buffer resource.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// A pointer the caller knows to be the same in every lane, moved to scalar
+// registers (a buffer resource must be scalar).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ===========================================================================
 // small-D
 // ===========================================================================
 // Running argmax, per point fragment f, over the 16 scores a lane holds for
-// one 32-row subtile (rows 8*(r/4) + 4*half + r%4 of the subtile, r = 0..15):
-//   m     = max of the 16 scores                      (two v_max3 chains, 8 ops)
-//   if m > best: best = m, btile = subtile, saved = the 16 scores
-// Strict '>' keeps the first subtile that reaches the maximum; the row is
-// located once at the end as the first slot of `saved` equal to best, so the
-// lowest index among equal scores wins, exactly as a sequential scan would.
+// one 32-row subtile (slot r = 0..15 holds row 8*(r/4) + 4*half + r%4 of the
+// subtile). Each score's 4 low mantissa bits are replaced by 15 - r (one
+// v_and_or_b32), so a single v_max3 tree yields the maximum and its slot:
+//   m = max of the 16 coded scores;  if m > best: best = m, btile = subtile
+// The code moves a score by less than 2^-19 of its magnitude, the size of
+// the rounding of the fp32 accumulation over d products, so it only orders
+// scores that agree to that precision; among those it prefers the lower row
+// for positive scores and the higher row for negative ones. Across subtiles
+// the strict '>' keeps the earlier subtile, and the two lane halves merge on
+// (coded score, lowest row). Scores that must never win are -FLT_MAX (a
+// finite value, so the code cannot turn it into a NaN).
 struct Argmax {
   float best;
   int btile;
-  float saved[16];
 };
+
+constexpr float kNeverWins = -3.40282346638528859812e+38f;   // -FLT_MAX
+
+__device__ __forceinline__ float code_slot(float score, int r) {
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, score) & ~0xFu) | (uint32_t)(15 - r));
+}
 
 // v_max3_f32 of three finite scores. The compiler turns a two-operand fmaxf
 // of MFMA results into canonicalising maxes; this keeps the tree at one
@@ -58,46 +82,42 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
 
 // Part `part` (0..7) of draining accumulator `acc` of subtile g into st.
 // The work is split so it can be spread over the k-steps of the next
-// subtile: parts 0-3 build the max tree, part 4 compares, parts 4-7 save.
+// subtile: parts 0-3 code the scores and build the max tree, part 4
+// compares, parts 5-7 are empty.
 __device__ __forceinline__ void drain_part(const floatx16_t& acc, int part, int g, Argmax& st,
                                            float (&m)[2], bool& gt) {
   switch (part) {
     case 0:
-      m[0] = vmax3(acc[0], acc[1], acc[2]);
-      m[1] = vmax3(acc[3], acc[4], acc[5]);
+      m[0] = vmax3(code_slot(acc[0], 0), code_slot(acc[1], 1), code_slot(acc[2], 2));
+      m[1] = vmax3(code_slot(acc[3], 3), code_slot(acc[4], 4), code_slot(acc[5], 5));
       break;
     case 1:
-      m[0] = vmax3(m[0], acc[6], acc[7]);
-      m[1] = vmax3(m[1], acc[8], acc[9]);
+      m[0] = vmax3(m[0], code_slot(acc[6], 6), code_slot(acc[7], 7));
+      m[1] = vmax3(m[1], code_slot(acc[8], 8), code_slot(acc[9], 9));
       break;
     case 2:
-      m[0] = vmax3(m[0], acc[10], acc[11]);
-      m[1] = vmax3(m[1], acc[12], acc[13]);
+      m[0] = vmax3(m[0], code_slot(acc[10], 10), code_slot(acc[11], 11));
+      m[1] = vmax3(m[1], code_slot(acc[12], 12), code_slot(acc[13], 13));
       break;
-    case 3:
-      m[0] = vmax3(m[0], m[1], acc[14]);
-      m[0] = vmax3(m[0], acc[15], acc[15]);
+    case 3: {
+      const float c15 = code_slot(acc[15], 15);
+      m[0] = vmax3(m[0], m[1], code_slot(acc[14], 14));
+      m[0] = vmax3(m[0], c15, c15);
       break;
+    }
     case 4:
       gt = m[0] > st.best;
       st.best = gt ? m[0] : st.best;
       st.btile = gt ? g : st.btile;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st.saved[r] = gt ? acc[r] : st.saved[r];
       break;
-    default: {
-      const int r0 = 4 * (part - 4);
-#pragma unroll
-      for (int r = r0; r < r0 + 4; ++r) st.saved[r] = gt ? acc[r] : st.saved[r];
-    }
+    default:
+      break;
   }
 }
 
 // Row of the maximum, relative to the kernel's first row, for half `half`.
 __device__ __forceinline__ int argmax_row(const Argmax& st, int half) {
-  int slot = 15;
-#pragma unroll
-  for (int r = 15; r >= 0; --r) slot = st.saved[r] == st.best ? r : slot;
+  const int slot = 15 - (int)(__builtin_bit_cast(uint32_t, st.best) & 0xFu);
   return st.btile * 32 + 8 * (slot >> 2) + 4 * half + (slot & 3);
 }
 
@@ -106,8 +126,9 @@ __device__ __forceinline__ int argmax_row(const Argmax& st, int half) {
 // nblocks is a multiple of 8, so every point block a block takes shares its
 // XCD's L2 with the ones it would have had as a plain launch). During the
 // last centroid tile of one point block the block already stages tile 0 of
-// the next, and the next block's point fragments load while the last argmax
-// drains, so consecutive point blocks run back to back.
+// the next and (8-wave blocks) loads the first half of the next block's
+// point fragments into spare registers; the other half loads while the last
+// argmax drains, so consecutive point blocks run back to back.
 // FULL: d == 16*KS, so every column of a row is real and loads need no
 // column guard; otherwise columns >= d read as zero.
 template <int DT, int KS, int NF, int TK, int WAVES, bool VEC, bool FULL>
@@ -124,18 +145,22 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   constexpr int NV = (TK * VPR + NT - 1) / NT;   // vectors per thread per tile
   static_assert(NSUB % 2 == 0, "accumulator sets alternate by subtile");
   static_assert(TK <= NT, "one norm per thread");
+  // k-steps of the next point block prefetched into registers during a
+  // point block's last tile (8-wave blocks with whole rows only)
+  constexpr int XP = (FULL && WAVES == 8) ? KS / 2 : 0;
   __shared__ __align__(16) uint16_t lds_c[2][TK * PITCH];
   __shared__ __align__(16) float lds_h[2][NT];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int half = lane >> 5, r32 = lane & 31;
   const int ntiles = (K + TK - 1) / TK;
 
   // point block v -> problem and this wave's first row
-  auto locate = [&](int64_t v, int& pb, int& row0) {
+  auto locate = [&](uint32_t v, int& pb, int& row0) {
     const int64_t logical = xcd_remap(v, total);
-    pb = (int)(logical / blocks_per_batch);
-    row0 = (int)(logical % blocks_per_batch) * BN + wave * NF * 32;
+    pb = __builtin_amdgcn_readfirstlane((int)(logical / blocks_per_batch));
+    row0 = __builtin_amdgcn_readfirstlane((int)(logical % blocks_per_batch) * BN + wave * NF * 32);
   };
   // the lane's point row of fragment f; rows past N repeat row N-1 (their
   // results are never stored)
@@ -151,18 +176,38 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   // win. Loads and stores are unconditional (tile indices clamp, every
   // thread owns an lds_h slot) so one tile iteration is a single basic block
   // the scheduler can interleave.
+  // Buffer resources over (at most) 32 whole rows from base: rows at or past
+  // the end of the data read as zero (a raw buffer's range check) instead of
+  // being clamped, and the per-lane offsets are constants of the kernel, so
+  // the loads cost no per-load 64-bit address registers.
+  auto rows_rsrc = [&](const void* base, int rows_left, int row_bytes) {
+    const int n = min(max(rows_left, 0), 32) * row_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), 0,
+                                             __builtin_amdgcn_readfirstlane(n), kRawBufferWord3);
+  };
   uint4 pre[NV];
   float pre_n = 0.f;
   auto fetch = [&](int pb, int t) {
     const uint16_t* cb = c + (int64_t)pb * K * d;
+    if constexpr (FULL && TK * VPR % NT == 0 && NT % VPR == 0) {
+      const uint32_t cvo = (uint32_t)((tid / VPR) * d + (tid % VPR) * 8) * 2;
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const int v = tid + NT * q;
-      if (TK * VPR % NT == 0 || v < TK * VPR) {
-        const int row = v / VPR, col = (v % VPR) * 8;
-        const int k = min(t * TK + row, K - 1);
-        pre[q] = FULL ? *reinterpret_cast<const uint4*>(cb + (int64_t)k * d + col)
-                      : load8<VEC>(cb + (int64_t)k * d, col, d);
+      for (int q = 0; q < NV; ++q) {
+        const int r0 = t * TK + q * (NT / VPR);
+        pre[q] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rows_rsrc(cb + (int64_t)r0 * d, K - r0, d * 2), cvo, 0, 0));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        const int v = tid + NT * q;
+        if (TK * VPR % NT == 0 || v < TK * VPR) {
+          const int row = v / VPR, col = (v % VPR) * 8;
+          const int k = min(t * TK + row, K - 1);
+          pre[q] = FULL ? *reinterpret_cast<const uint4*>(cb + (int64_t)k * d + col)
+                        : load8<VEC>(cb + (int64_t)k * d, col, d);
+        }
       }
     }
     pre_n = cnorm[(int64_t)pb * K + min(t * TK + (tid % TK), K - 1)];
@@ -176,7 +221,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
         *reinterpret_cast<uint4*>(&lds_c[buf][row * PITCH + col]) = pre[q];
       }
     }
-    lds_h[buf][tid] = (t * TK + tid < K) ? -0.5f * pre_n : -INFINITY;
+    lds_h[buf][tid] = (t * TK + tid < K) ? -0.5f * pre_n : kNeverWins;
   };
 
   // LDS operands of a step, read ahead of use: A fragments two k-steps ahead
@@ -210,14 +255,33 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   // drain of a point block is of an all -inf set standing for subtile -1.
   floatx16_t acc[2][NF];
 
+  // The switch to the next point block: its first XP k-steps are loaded
+  // into spare registers at the start of the current block's last tile, a
+  // whole tile ahead of use, so at the switch only the remaining k-steps
+  // come from HBM, and those are first needed XP k-steps into the new
+  // block's first subtile.
+  const uint32_t xvo = (uint32_t)(r32 * d + half * 8) * 2;   // lane's bytes within a fragment
+  auto frag_rsrc = [&](int pb, int row0, int f) {
+    return rows_rsrc(x + ((int64_t)pb * N + row0 + f * 32) * d, N - (row0 + f * 32), d * 2);
+  };
+  uint4 xn[NF][XP > 0 ? XP : 1];
+  auto prefetch_x = [&](int pb, int row0) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const auto rs = frag_rsrc(pb, row0, f);
+#pragma unroll
+      for (int s = 0; s < XP; ++s)
+        xn[f][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, xvo + s * 32, 0, 0));
+    }
+  };
+
   // One centroid tile from LDS buffer buf.
   auto tile = [&](int buf, int t) {
-    floatx16_t ci[2];
+    floatx16_t ci;
     uint4 ar[3];
-    read_c(buf, 0, ci[0]);
+    read_c(buf, 0, ci);
     ar[0] = read_a(buf, 0);
     ar[1] = read_a(buf, 1 % STEPS);
-    read_c(buf, 1 % NSUB, ci[1]);
     float m[NF][2];
     bool gt[NF];
 #pragma unroll
@@ -227,10 +291,10 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
       floatx16_t (&cur)[NF] = acc[sub & 1];
       const floatx16_t (&prev)[NF] = acc[(sub + 1) & 1];
       if (q + 2 < STEPS) ar[(q + 2) % 3] = read_a(buf, q + 2);
-      if (kk == 1 && sub + 2 < NSUB) read_c(buf, sub + 2, ci[sub & 1]);
 #pragma unroll
       for (int f = 0; f < NF; ++f)
-        cur[f] = Mfma<DT>::run(ar[q % 3], xf[f][kk], kk == 0 ? ci[sub & 1] : cur[f]);
+        cur[f] = Mfma<DT>::run(ar[q % 3], xf[f][kk], kk == 0 ? ci : cur[f]);
+      if (kk == 0 && sub + 1 < NSUB) read_c(buf, sub + 1, ci);
 #pragma unroll
       for (int p = kk * PPS; p < (kk + 1) * PPS && p < PARTS; ++p)
         drain_part(prev[p % NF], p / NF, g - 1, st[p % NF], m[p % NF], gt[p % NF]);
@@ -245,9 +309,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
       st[f].best = -INFINITY;
       st[f].btile = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[f].saved[r] = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[1][f][r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) acc[1][f][r] = kNeverWins;
     }
   };
   auto load_block = [&](int pb, int row0) {
@@ -258,15 +320,31 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
       for (int s = 0; s < KS; ++s) xf[f][s] = load_frag(row, s);
     }
   };
+  auto load_block_next = [&](int pb, int row0) {
+    if constexpr (XP > 0) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const auto rs = frag_rsrc(pb, row0, f);
+#pragma unroll
+        for (int s = XP; s < KS; ++s)
+          xf[f][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, xvo + s * 32, 0, 0));
+#pragma unroll
+        for (int s = 0; s < XP; ++s) xf[f][s] = xn[f][s];
+      }
+    } else {
+      load_block(pb, row0);
+    }
+  };
 
-  int64_t v = blockIdx.x;
+  // item indices stay below 2 * total < 2^32
+  uint32_t v = blockIdx.x;
   int pb, row0;
   locate(v, pb, row0);
   // the next point block, or this one again past the end (its loads and
   // tile-0 stage are then harmless repeats that nothing reads)
-  int64_t vn = v + nblocks;
+  uint32_t vn = v + (uint32_t)nblocks;
   int npb = pb, nrow0 = row0;
-  if (vn < total) locate(vn, npb, nrow0);
+  if (vn < (uint32_t)total) locate(vn, npb, nrow0);
   load_block(pb, row0);
   fetch(pb, 0);
   stash(0, 0);
@@ -279,23 +357,26 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
     const bool last = t == ntiles - 1;
     const int ft = last ? 0 : t + 1;
     fetch(last ? npb : pb, ft);
+    if (XP > 0 && last) prefetch_x(npb, nrow0);
     tile(buf, t);
     stash(ft, buf ^ 1);
     if (last) {
+      // the next point block's fragments first (the rest of its k-steps
+      // load while this one's final subtile drains), then this one's ids
+      int32_t* ib = ids + (int64_t)pb * N;
       const int g = ntiles * NSUB - 1;       // the last subtile, still in acc[1]
       float m[NF][2];
       bool gt[NF];
+      load_block_next(npb, nrow0);
 #pragma unroll
       for (int p = 0; p < 8 * NF; ++p)
         drain_part(acc[1][p % NF], p / NF, g, st[p % NF], m[p % NF], gt[p % NF]);
-      int32_t* ib = ids + (int64_t)pb * N;
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const int idx = merge_halves(st[f].best, argmax_row(st[f], half) - 4 * half, half);
         const int n = row0 + f * 32 + r32;
         if (half == 0 && n < N) ib[n] = min(max(idx, 0), K - 1);
       }
-      load_block(npb, nrow0);
       reset();
     }
     __syncthreads();
@@ -304,12 +385,12 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
       ++t;
       continue;
     }
-    if (vn >= total) break;
+    if (vn >= (uint32_t)total) break;
     v = vn;
     pb = npb;
     row0 = nrow0;
-    vn = v + nblocks;
-    if (vn < total) locate(vn, npb, nrow0);
+    vn = v + (uint32_t)nblocks;
+    if (vn < (uint32_t)total) locate(vn, npb, nrow0);
     t = 0;
   }
 }
