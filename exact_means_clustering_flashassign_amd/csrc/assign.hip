@@ -65,21 +65,6 @@ struct Argmax {
   int btile;
 };
 
-constexpr float kNeverWins = -3.40282346638528859812e+38f;   // -FLT_MAX
-
-__device__ __forceinline__ float code_slot(float score, int r) {
-  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, score) & ~0xFu) | (uint32_t)(15 - r));
-}
-
-// v_max3_f32 of three finite scores. The compiler turns a two-operand fmaxf
-// of MFMA results into canonicalising maxes; this keeps the tree at one
-// instruction per two new scores.
-__device__ __forceinline__ float vmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 // Part `part` (0..7) of draining accumulator `acc` of subtile g into st.
 // The work is split so it can be spread over the k-steps of the next
 // subtile: parts 0-3 code the scores and build the max tree, part 4
@@ -117,8 +102,7 @@ __device__ __forceinline__ void drain_part(const floatx16_t& acc, int part, int 
 
 // Row of the maximum, relative to the kernel's first row, for half `half`.
 __device__ __forceinline__ int argmax_row(const Argmax& st, int half) {
-  const int slot = 15 - (int)(__builtin_bit_cast(uint32_t, st.best) & 0xFu);
-  return st.btile * 32 + 8 * (slot >> 2) + 4 * half + (slot & 3);
+  return st.btile * 32 + slot_row(slot_of(st.best)) + 4 * half;
 }
 
 // Persistent: a block walks point blocks v = blockIdx.x, + nblocks, ... of the
@@ -156,9 +140,26 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   const int half = lane >> 5, r32 = lane & 31;
   const int ntiles = (K + TK - 1) / TK;
 
-  // point block v -> problem and this wave's first row
-  auto locate = [&](uint32_t v, int& pb, int& row0) {
-    const int64_t logical = xcd_remap(v, total);
+  // Tail: when the last round of point blocks would leave at least half of
+  // the blocks idle (r = total % nblocks, 0 < 2r <= nblocks), its r point
+  // blocks become 2r half blocks: in each, the waves of one half do the
+  // MFMA work for their rows and the other waves only help stage tiles, so
+  // that round takes about half as long.
+  const uint32_t rtail = (uint32_t)(total % nblocks);
+  const bool split = WAVES == 8 && rtail > 0 && 2 * rtail <= (uint32_t)nblocks;
+  const uint32_t nfull = split ? (uint32_t)total - rtail : (uint32_t)total;
+  const uint32_t nitems = split ? (uint32_t)total + rtail : (uint32_t)total;
+  // item v -> problem, this wave's first row, and whether the wave works on it
+  auto locate = [&](uint32_t v, int& pb, int& row0, bool& act) {
+    int64_t logical = 0;
+    act = true;
+    if (v < nfull) {
+      logical = xcd_remap(v, nfull);
+    } else {
+      const int64_t hr = xcd_remap(v - nfull, 2 * rtail);
+      logical = nfull + hr / 2;
+      act = wave / (WAVES / 2) == (int)(hr % 2);
+    }
     pb = __builtin_amdgcn_readfirstlane((int)(logical / blocks_per_batch));
     row0 = __builtin_amdgcn_readfirstlane((int)(logical % blocks_per_batch) * BN + wave * NF * 32);
   };
@@ -339,12 +340,14 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   // item indices stay below 2 * total < 2^32
   uint32_t v = blockIdx.x;
   int pb, row0;
-  locate(v, pb, row0);
+  bool act;
+  locate(v, pb, row0, act);
   // the next point block, or this one again past the end (its loads and
   // tile-0 stage are then harmless repeats that nothing reads)
   uint32_t vn = v + (uint32_t)nblocks;
   int npb = pb, nrow0 = row0;
-  if (vn < (uint32_t)total) locate(vn, npb, nrow0);
+  bool nact = act;
+  if (vn < nitems) locate(vn, npb, nrow0, nact);
   load_block(pb, row0);
   fetch(pb, 0);
   stash(0, 0);
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
     const int ft = last ? 0 : t + 1;
     fetch(last ? npb : pb, ft);
     if (XP > 0 && last) prefetch_x(npb, nrow0);
-    tile(buf, t);
+    if (act) tile(buf, t);
     stash(ft, buf ^ 1);
     if (last) {
       // the next point block's fragments first (the rest of its k-steps
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
       for (int f = 0; f < NF; ++f) {
         const int idx = merge_halves(st[f].best, argmax_row(st[f], half) - 4 * half, half);
         const int n = row0 + f * 32 + r32;
-        if (half == 0 && n < N) ib[n] = min(max(idx, 0), K - 1);
+        if (act && half == 0 && n < N) ib[n] = min(max(idx, 0), K - 1);
       }
       reset();
     }
@@ -385,12 +388,13 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
       ++t;
       continue;
     }
-    if (vn >= (uint32_t)total) break;
+    if (vn >= nitems) break;
     v = vn;
     pb = npb;
     row0 = nrow0;
+    act = nact;
     vn = v + (uint32_t)nblocks;
-    if (vn < (uint32_t)total) locate(vn, npb, nrow0);
+    if (vn < nitems) locate(vn, npb, nrow0, nact);
     t = 0;
   }
 }

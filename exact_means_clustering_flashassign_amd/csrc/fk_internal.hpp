@@ -91,6 +91,35 @@ __device__ __forceinline__ uint4 load8(const uint16_t* row, int col, int limit) 
   }
 }
 
+// Slot-coded scores for a running argmax over the 16 scores a lane holds of
+// one 32-row MFMA output (slot r = 0..15 is row 8*(r/4) + 4*half + r%4): the
+// 4 low mantissa bits of each score are replaced by 15 - r, so a max over
+// coded scores also says where the maximum is. The code changes a score by
+// less than 2^-19 of its size; scores that agree to that precision are
+// ordered by it (lower row first when positive, higher row when negative).
+// Scores that must never win are kNeverWins, a finite value (a code on -inf
+// would make a NaN).
+constexpr float kNeverWins = -3.40282346638528859812e+38f;   // -FLT_MAX
+
+__device__ __forceinline__ float code_slot(float score, int r) {
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, score) & ~0xFu) | (uint32_t)(15 - r));
+}
+__device__ __forceinline__ int slot_of(float coded) {
+  return 15 - (int)(__builtin_bit_cast(uint32_t, coded) & 0xFu);
+}
+// Row (within the 32-row block, without the 4*half term) of slot r.
+__device__ __forceinline__ int slot_row(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// v_max3_f32 of three finite scores. The compiler turns a two-operand fmaxf
+// of MFMA results into canonicalising maxes; this keeps the tree at one
+// instruction per two new scores (the kernels that use it build with
+// -fno-honor-nans; inputs are finite by contract).
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // The two lanes (half 0 and half 1) that hold the same point each carry the
 // best score and row over their 16 rows of every 32-row block; half 1's rows
 // sit 4 above half 0's. Returns the winning row, lowest row on equal scores.

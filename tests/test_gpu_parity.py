@@ -85,6 +85,8 @@ def test_norms_rounding_and_sqnorms(fk, dtype, d):
 ASSIGN_CASES = [
     # dtype, B, N, d, K, force split-D
     ("f16", 2, 3000, 128, 1000, False),     # reduced headline shape, ragged N and K
+    ("f16", 4, 40000, 128, 150, False),     # more point blocks than resident blocks:
+    ("bf16", 3, 50000, 128, 100, False),    # blocks move on to a second point block
     ("f16", 1, 777, 1, 5, False),
     ("f16", 1, 500, 3, 40, False),
     ("f16", 1, 600, 8, 70, False),
