@@ -23,3 +23,4 @@ from ._binding import (  # noqa: F401
     torch_dtype,
     workspace,
 )
+from .api import FlashKMeans, batch_kmeans_Euclid, random_init  # noqa: F401,E402
