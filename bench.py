@@ -102,6 +102,54 @@ def cpu_baseline(w, name: str, min_seconds: float = 10.0):
                       f"{reps} run(s) in {total:.1f} s, scaled by problems and rows to the whole batch"}
 
 
+def gpu_baselines(fk, torch, x, ids, centers, ws, dtype: str, reps: int = 3):
+    """The standard formulations the method replaces, timed on the same inputs.
+
+    Materialised-distance assign (rocBLAS GEMM into a (B,N,K) fp32 matrix,
+    then an argmin pass) against fk_assign, and the scatter-atomic update
+    against fk_update, each called on its own (HIP events on torch's current
+    stream, where both libraries enqueue). Skipped when the distance matrix
+    would take more than 48 GiB."""
+    B, N, d = x.shape
+    K = centers.shape[1]
+    if B * N * K * 4 > 48 * 2**30:
+        return {"skipped": f"the (B,N,K) fp32 distance matrix would take "
+                           f"{B * N * K * 4 / 2**30:.0f} GiB"}
+    fk.load_baseline()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    c_lp, cn = fk.fk_norms(centers, x.dtype)
+    dist = torch.empty((B, N, K), dtype=torch.float32, device=x.device)
+    ids_b = torch.empty_like(ids)
+    mat_ms = timed(lambda: fk.fkb_assign_materialized(x, c_lp, cn, dist=dist, ids=ids_b))
+    flash_ms = timed(lambda: fk.fk_assign(x, c_lp, cn, ids=ids_b))
+    del dist
+    torch.cuda.empty_cache()
+    c_tmp = centers.clone()
+    counts = torch.empty((B, K), dtype=torch.int32, device=x.device)
+    sums = torch.empty((B, K, d), dtype=torch.float32, device=x.device)
+    shift = torch.empty((B,), dtype=torch.float32, device=x.device)
+    atomic_ms = timed(lambda: fk.fkb_update_atomic(x, ids, c_tmp, counts=counts, sums=sums))
+    sort_ms = timed(lambda: fk.fk_update(x, ids, c_tmp, counts=counts, shift=shift, ws=ws))
+    x_bytes = B * N * d * elem_bytes(dtype)
+    return {"assign_materialized_ms": mat_ms, "assign_flash_ms": flash_ms,
+            "assign_speedup": mat_ms / flash_ms,
+            "update_scatter_atomic_ms": atomic_ms, "update_sort_inverse_ms": sort_ms,
+            "update_speedup": atomic_ms / sort_ms,
+            "scatter_atomic_effective_GBps": x_bytes / (atomic_ms * 1e-3) / 1e9,
+            "note": "each call on its own, same inputs; fk_update here also computes the shift"}
+
+
 def copy_calibration(mib: int, dev):
     """A plain elementwise kernel over a buffer of known size, for scaling
     the HBM byte counters (reads and writes mib MiB each)."""
@@ -124,6 +172,9 @@ def main():
                     help="1 = time the oracle on its bounded sample, 0 = skip")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="after the timed region, run a copy kernel of this size (counter scaling)")
+    ap.add_argument("--baselines", type=int, default=1,
+                    help="1 = after the timed region, time the materialised-distance assign and "
+                         "the scatter-atomic update on the same inputs, 0 = skip")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -206,6 +257,8 @@ def main():
                             "frac": u_bytes / (u_ms * 1e-3) / 1e9 / PEAK_HBM,
                             "traffic": u_traffic},
     }
+    out["gpu_baselines"] = (gpu_baselines(fk, torch, x, ids, centers, ws, w.dtype)
+                            if args.baselines > 0 else None)
     out["cpu_baseline"] = cpu_baseline(w, args.workload) if args.cpu_batches > 0 else None
     print(json.dumps(out))
 

@@ -4,6 +4,7 @@ All computation runs in the hand-written HIP kernels of ``libfkmeans.so``
 (C ABI in ``include/fkmeans.h``); this package only marshals arguments.
 """
 from ._binding import (  # noqa: F401
+    BASELINE_LIB_PATH,
     FK_BF16,
     FK_F16,
     FK_F32,
@@ -19,7 +20,10 @@ from ._binding import (  # noqa: F401
     fk_update,
     fk_version,
     fk_workspace_size,
+    fkb_assign_materialized,
+    fkb_update_atomic,
     load,
+    load_baseline,
     torch_dtype,
     workspace,
 )

@@ -213,3 +213,67 @@ def fk_trace_end() -> dict:
     _check(load().fk_trace_end(ctypes.byref(out)), "fk_trace_end")
     return {"iterations": out.iterations, "norms_ms": out.norms_ms,
             "assign_ms": out.assign_ms, "update_ms": out.update_ms}
+
+
+# ---------------------------------------------------------------------------
+# libfkbaseline: the materialised-distance assign and the scatter-atomic
+# update (include/fkmeans_baselines.h), for contrast measurements only.
+# ---------------------------------------------------------------------------
+BASELINE_LIB_PATH = os.path.join(HERE, "libfkbaseline.so")
+_blib = None
+
+
+def load_baseline(path: Optional[str] = None):
+    """Load libfkbaseline.so (once) and declare its signatures."""
+    global _blib
+    if _blib is not None:
+        return _blib
+    path = path or BASELINE_LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first "
+                           "(python -m exact_means_clustering_flashassign_amd.build)")
+    lib = ctypes.CDLL(path)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.fkb_assign_materialized.restype = ctypes.c_int
+    lib.fkb_assign_materialized.argtypes = [P, P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P]
+    lib.fkb_update_atomic.restype = ctypes.c_int
+    lib.fkb_update_atomic.argtypes = [P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, P]
+    _blib = lib
+    return lib
+
+
+def fkb_assign_materialized(x, c_lp, cnorm, dist=None, ids=None):
+    """Standard assign: the (B,N,K) fp32 matrix -2 x.c (rocBLAS), then argmin."""
+    torch = _torch()
+    code = dtype_code(x.dtype)
+    B, N, d = x.shape
+    K = c_lp.shape[1]
+    if dist is None:
+        dist = torch.empty((B, N, K), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty((B, N), dtype=torch.int32, device=x.device)
+    st = load_baseline().fkb_assign_materialized(
+        _dev(x, "x"), _dev(c_lp, "c_lp", x.dtype, (B, K, d)),
+        _dev(cnorm, "cnorm", torch.float32, (B, K)), code, B, N, d, K,
+        _dev(dist, "dist", torch.float32, (B, N, K)), _dev(ids, "ids", torch.int32, (B, N)),
+        _stream(x))
+    _check(st, "fkb_assign_materialized")
+    return ids
+
+
+def fkb_update_atomic(x, ids, c, counts=None, sums=None):
+    """Standard update: scatter atomics into sums, then divide; c updated in place."""
+    torch = _torch()
+    code = dtype_code(x.dtype)
+    B, N, d = x.shape
+    K = c.shape[1]
+    if counts is None:
+        counts = torch.empty((B, K), dtype=torch.int32, device=x.device)
+    if sums is None:
+        sums = torch.empty((B, K, d), dtype=torch.float32, device=x.device)
+    st = load_baseline().fkb_update_atomic(
+        _dev(x, "x"), _dev(ids, "ids", torch.int32, (B, N)), code, B, N, d, K,
+        _dev(c, "c", torch.float32, (B, K, d)), _dev(counts, "counts", torch.int32, (B, K)),
+        _dev(sums, "sums", torch.float32, (B, K, d)), _stream(x))
+    _check(st, "fkb_update_atomic")
+    return c, counts

@@ -16,6 +16,12 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfkmeans.so")
 SOURCES = ["norms.hip", "assign.hip", "assign_splitd.hip", "update.hip", "api.hip"]
+# The contrast baselines (materialised-distance assign, scatter-atomic
+# update) are a library of their own, linked against rocBLAS for the GEMM,
+# so the Lloyd library itself depends on nothing but the HIP runtime.
+BASELINE_LIB = os.path.join(HERE, "libfkbaseline.so")
+BASELINE_SOURCES = ["baseline.hip"]
+ROCM_LIB = "/opt/rocm/lib"
 # Per-file flags. assign.hip: inputs are finite by contract, so fmaxf needs no
 # NaN canonicalisation and the argmax max-tree lowers to plain v_max3_f32; its
 # MFMA accumulators live in VGPRs, which the argmax reads without AGPR copies.
@@ -49,19 +55,27 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+def _link(objs, out, libs=()) -> None:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *libs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile and link libfkmeans.so and libfkbaseline.so; returns the former's path."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = SOURCES + BASELINE_SOURCES
+    jobs = min(len(srcs), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra_flags)), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in BASELINE_SOURCES], BASELINE_LIB,
+          [f"-L{ROCM_LIB}", f"-Wl,-rpath,{ROCM_LIB}", "-lrocblas"])
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {BASELINE_LIB}")
     return LIB
 
 

@@ -1,0 +1,165 @@
+// libfkbaseline: the standard assign (materialised distance matrix + argmin)
+// and the standard update (scatter atomics), for contrast with FlashAssign
+// and the sort-inverse update. The pages describe both as the formulations
+// the method replaces (itinai.com summary, the paragraphs on the first and
+// second bottleneck; "Flash-KMeans: Implementação Exata ...", section on
+// conventional assignment; "Flash-KMeans：IO感知的精确K-Means ...", update
+// section). The GEMM is rocBLAS, as a library GEMM would be in a standard
+// implementation; the argmin, scatter and divide kernels are plain HIP.
+// Nothing here is shared with libfkmeans.
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+#include <stdint.h>
+
+#include "../../include/fkmeans_baselines.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
+  if (dt == FK_F32) return reinterpret_cast<const float*>(p)[i];
+  const uint16_t h = reinterpret_cast<const uint16_t*>(p)[i];
+  if (dt == FK_F16) return (float)__builtin_bit_cast(_Float16, h);
+  return __builtin_bit_cast(float, (uint32_t)h << 16);   // bf16
+}
+
+// One wave per point row: min over k of cnorm[k] + dist[n,k], lowest k on
+// ties (each lane scans increasing k; the wave keeps the lower index on
+// equal values).
+__global__ __launch_bounds__(kThreads) void argmin_rows_kernel(const float* __restrict__ dist,
+                                                               const float* __restrict__ cnorm,
+                                                               int32_t* __restrict__ ids,
+                                                               int64_t rows, int N, int K) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t b = row / N;
+  const float* dr = dist + row * K;
+  const float* cn = cnorm + b * K;
+  float best = INFINITY;
+  int bidx = 0;
+  for (int k = lane; k < K; k += 64) {
+    const float v = cn[k] + dr[k];
+    if (v < best) {
+      best = v;
+      bidx = k;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(best, off, 64);
+    const int oi = __shfl_xor(bidx, off, 64);
+    if (ov < best || (ov == best && oi < bidx)) {
+      best = ov;
+      bidx = oi;
+    }
+  }
+  if (lane == 0) ids[row] = bidx;
+}
+
+__global__ __launch_bounds__(kThreads) void zero_kernel(float* __restrict__ s, int64_t ns,
+                                                        int32_t* __restrict__ c, int64_t nc) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < ns; i += stride) s[i] = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nc; i += stride) c[i] = 0;
+}
+
+// One thread per element of x: one fp32 atomic add into its cluster's sums
+// (hardware float atomic), and one count per point.
+__global__ __launch_bounds__(kThreads) void scatter_add_kernel(const void* __restrict__ x,
+                                                               const int32_t* __restrict__ ids,
+                                                               float* __restrict__ sums,
+                                                               int32_t* __restrict__ counts,
+                                                               int dt, int64_t total, int N, int d,
+                                                               int K) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+    const int64_t pt = e / d;                  // b * N + n
+    const int j = (int)(e - pt * d);
+    const int64_t b = pt / N;
+    const int k = ids[pt];
+    if ((unsigned)k >= (unsigned)K) continue;  // out of contract: ignored
+    unsafeAtomicAdd(&sums[(b * K + k) * d + j], load_elem(x, e, dt));
+    if (j == 0) atomicAdd(&counts[b * K + k], 1);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void divide_kernel(const float* __restrict__ sums,
+                                                          const int32_t* __restrict__ counts,
+                                                          float* __restrict__ c, int64_t total,
+                                                          int d) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+    const int n = counts[e / d];
+    if (n > 0) c[e] = sums[e] / (float)n;
+  }
+}
+
+unsigned grid_for(int64_t n) {
+  int64_t g = (n + kThreads - 1) / kThreads;
+  return (unsigned)(g < 1 ? 1 : (g > 65536 ? 65536 : g));
+}
+
+rocblas_handle handle_for_device() {
+  static rocblas_handle handles[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success)
+    handles[dev] = nullptr;
+  return handles[dev];
+}
+
+bool sizes_ok(int64_t B, int64_t N, int64_t d, int64_t K) {
+  const int64_t lim = 0x7FFFFFFF;
+  return B > 0 && N > 0 && d > 0 && K > 0 && B < lim && N < lim && d < lim && K < lim;
+}
+
+}  // namespace
+
+extern "C" fk_status_t fkb_assign_materialized(const void* x, const void* c_lp,
+                                               const float* cnorm, fk_dtype_t dt, int64_t B,
+                                               int64_t N, int64_t d, int64_t K, float* dist,
+                                               int32_t* ids, hipStream_t stream) {
+  if (!sizes_ok(B, N, d, K) || !x || !c_lp || !cnorm || !dist || !ids) return FK_ERR_INVALID;
+  rocblas_datatype in_t;
+  if (dt == FK_F32) in_t = rocblas_datatype_f32_r;
+  else if (dt == FK_F16) in_t = rocblas_datatype_f16_r;
+  else if (dt == FK_BF16) in_t = rocblas_datatype_bf16_r;
+  else return FK_ERR_INVALID;
+  rocblas_handle h = handle_for_device();
+  if (!h || rocblas_set_stream(h, stream) != rocblas_status_success) return FK_ERR_HIP;
+  // Row-major dist (N,K) of problem b is the column-major K x N product
+  // c_lp_b (K x d) * x_b^T: A = c_lp as column-major d x K, transposed;
+  // B = x as column-major d x N.
+  const float alpha = -2.f, beta = 0.f;
+  const rocblas_status st = rocblas_gemm_strided_batched_ex(
+      h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)K, (rocblas_int)N,
+      (rocblas_int)d, &alpha, c_lp, in_t, (rocblas_int)d, (rocblas_stride)(K * d), x, in_t,
+      (rocblas_int)d, (rocblas_stride)(N * d), &beta, dist, rocblas_datatype_f32_r,
+      (rocblas_int)K, (rocblas_stride)(N * K), dist, rocblas_datatype_f32_r, (rocblas_int)K,
+      (rocblas_stride)(N * K), (rocblas_int)B, rocblas_datatype_f32_r, rocblas_gemm_algo_standard,
+      0, 0);
+  if (st != rocblas_status_success) return FK_ERR_HIP;
+  const int64_t rows = B * N;
+  const int64_t blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
+  if (blocks > 0x7FFFFFFF) return FK_ERR_INVALID;
+  argmin_rows_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(dist, cnorm, ids, rows, (int)N,
+                                                                 (int)K);
+  return hipGetLastError() == hipSuccess ? FK_OK : FK_ERR_HIP;
+}
+
+extern "C" fk_status_t fkb_update_atomic(const void* x, const int32_t* ids, fk_dtype_t dt,
+                                         int64_t B, int64_t N, int64_t d, int64_t K, float* c,
+                                         int32_t* counts, float* sums, hipStream_t stream) {
+  if (!sizes_ok(B, N, d, K) || !x || !ids || !c || !counts || !sums) return FK_ERR_INVALID;
+  if (dt != FK_F32 && dt != FK_F16 && dt != FK_BF16) return FK_ERR_INVALID;
+  const int64_t kd = B * K * d, total = B * N * d;
+  zero_kernel<<<grid_for(kd), kThreads, 0, stream>>>(sums, kd, counts, B * K);
+  if (hipGetLastError() != hipSuccess) return FK_ERR_HIP;
+  scatter_add_kernel<<<grid_for(total), kThreads, 0, stream>>>(x, ids, sums, counts, (int)dt,
+                                                               total, (int)N, (int)d, (int)K);
+  if (hipGetLastError() != hipSuccess) return FK_ERR_HIP;
+  divide_kernel<<<grid_for(kd), kThreads, 0, stream>>>(sums, counts, c, kd, (int)d);
+  return hipGetLastError() == hipSuccess ? FK_OK : FK_ERR_HIP;
+}

@@ -96,7 +96,7 @@ def _run(cmd, log, limit):
 def _bench_cmd(args):
     return ["python3", os.path.join(ROOT, "bench.py"), "--workload", args.workload,
             "--steps", str(args.steps), "--warmup", str(args.warmup), "--cpu-batches", "0",
-            "--copy-calibration", str(COPY_MIB)]
+            "--baselines", "0", "--copy-calibration", str(COPY_MIB)]
 
 
 def _find(d, suffix):

@@ -108,3 +108,20 @@ def test_validation_rejects_before_launch(lib):
     # trace
     assert lib.fk_trace_begin(0) == INVALID
     assert lib.fk_trace_end(None) == INVALID
+
+
+def test_baseline_library_exports_its_header():
+    """libfkbaseline.so exports every call include/fkmeans_baselines.h declares."""
+    from exact_means_clustering_flashassign_amd import _binding
+
+    text = open(os.path.join(ROOT, "include", "fkmeans_baselines.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(fkb_[a-z_]+)\s*\(", text)))
+    assert names == ["fkb_assign_materialized", "fkb_update_atomic"]
+    if not os.path.exists(_binding.BASELINE_LIB_PATH):
+        pytest.fail("libfkbaseline.so is not built (run __graft_entry__.build())")
+    lib = _binding.load_baseline()
+    for name in names:
+        assert hasattr(lib, name), name
+        assert callable(getattr(_binding, name)), name
+
