@@ -30,7 +30,8 @@ __device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
 __global__ __launch_bounds__(kThreads) void argmin_rows_kernel(const float* __restrict__ dist,
                                                                const float* __restrict__ cnorm,
                                                                int32_t* __restrict__ ids,
-                                                               int64_t rows, int N, int K) {
+                                                               int64_t rows, int N, int K,
+                                                               bool vec) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -39,11 +40,26 @@ __global__ __launch_bounds__(kThreads) void argmin_rows_kernel(const float* __re
   const float* cn = cnorm + b * K;
   float best = INFINITY;
   int bidx = 0;
-  for (int k = lane; k < K; k += 64) {
-    const float v = cn[k] + dr[k];
-    if (v < best) {
-      best = v;
-      bidx = k;
+  if (vec) {                   // K % 4 == 0 and 16-byte aligned bases: 16-byte loads
+    for (int k = 4 * lane; k < K; k += 256) {
+      const float4 dv = *reinterpret_cast<const float4*>(dr + k);
+      const float4 cv = *reinterpret_cast<const float4*>(cn + k);
+      const float v[4] = {cv.x + dv.x, cv.y + dv.y, cv.z + dv.z, cv.w + dv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (v[i] < best) {
+          best = v[i];
+          bidx = k + i;
+        }
+      }
+    }
+  } else {
+    for (int k = lane; k < K; k += 64) {
+      const float v = cn[k] + dr[k];
+      if (v < best) {
+        best = v;
+        bidx = k;
+      }
     }
   }
 #pragma unroll
@@ -144,8 +160,9 @@ extern "C" fk_status_t fkb_assign_materialized(const void* x, const void* c_lp,
   const int64_t rows = B * N;
   const int64_t blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
   if (blocks > 0x7FFFFFFF) return FK_ERR_INVALID;
+  const bool vec = K % 4 == 0 && (uintptr_t)dist % 16 == 0 && (uintptr_t)cnorm % 16 == 0;
   argmin_rows_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(dist, cnorm, ids, rows, (int)N,
-                                                                 (int)K);
+                                                                 (int)K, vec);
   return hipGetLastError() == hipSuccess ? FK_OK : FK_ERR_HIP;
 }
 

@@ -57,8 +57,14 @@ def source_digest(phase: str) -> str:
     return h.hexdigest()[:16]
 
 
+BASELINE_KERNELS = ("argmin_rows_kernel", "scatter_add_kernel", "divide_kernel")
+
+
 def phase_of(kernel: str) -> str:
     k = kernel.replace("(anonymous namespace)", "").split("(")[0]
+    if (any(b in k for b in BASELINE_KERNELS) or k.startswith("Cijk_") or "rocblas" in k
+            or ("zero_kernel" in k and "fk::" not in k)):
+        return "baseline"
     if "assign_" in k:
         return "assign"
     if "norms_" in k and "_kernel" in k:
@@ -73,7 +79,8 @@ def phase_of(kernel: str) -> str:
 
 
 def short_name(kernel: str) -> str:
-    k = kernel.replace("fk::(anonymous namespace)::", "").replace("void ", "")
+    k = (kernel.replace("fk::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+         .replace("void ", ""))
     head = k.split("(")[0]
     if COPY_TAG in k:
         return "torch neg_kernel (copy calibration)"
@@ -153,6 +160,10 @@ def stats_text(cmds, rows, bench):
     for r in sorted(rows, key=lambda r: -r["total_ms"]):
         out.append(f"{short_name(r['kernel']):72s} {phase_of(r['kernel']):7s} {r['calls']:5d} "
                    f"{r['avg_us']:9.1f} {r['min_us']:9.1f} {r['pct']:5.1f}%")
+    if bench and bench.get("gpu_baselines"):
+        gb = bench["gpu_baselines"]
+        out += ["", "same run, contrast baselines (each call on its own, same inputs, HIP events):"]
+        out += [f"  {k}: {v:.4g}" if isinstance(v, float) else f"  {k}: {v}" for k, v in gb.items()]
     if bench:
         ph = bench["phases_ms"]
         out += ["", "same run, HIP events recorded by the library on the launch stream "
@@ -198,6 +209,32 @@ def traffic_text(cmds, per, f_fetch, f_write, nbytes_copy, algo):
     return "\n".join(out) + "\n"
 
 
+def baselines_pass(args) -> int:
+    """Kernel statistics of a short bench run with the contrast baselines."""
+    wl = args.workload
+    raw = os.path.join(args.raw, wl)
+    os.makedirs(raw, exist_ok=True)
+    os.makedirs(args.out, exist_ok=True)
+    bcmd = ["python3", os.path.join(ROOT, "bench.py"), "--workload", wl, "--steps", "2",
+            "--warmup", "1", "--cpu-batches", "0", "--baselines", "1"]
+    cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+           os.path.join(raw, "baselines"), "-o", "run", "--"] + bcmd
+    log = os.path.join(raw, "baselines.log")
+    if not args.summarize_only:
+        rc = _run(cmd, log, args.limit)
+        if rc != 0:
+            return rc
+    top = ("python3 -m exact_means_clustering_flashassign_amd.profiling --baselines --workload "
+           + wl)
+    rows = read_stats(_find(os.path.join(raw, "baselines"), "_kernel_stats.csv"))
+    txt = stats_text([top, "  which runs:", cmd], rows, _bench_json(log))
+    txt = txt.replace(ROOT + "/", "").replace(args.raw, "gpurun_out/rocprof")
+    with open(os.path.join(args.out, f"kernels_baselines_{wl}.txt"), "w") as f:
+        f.write(txt)
+    print(txt, flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--workload", default="api_example")
@@ -210,7 +247,12 @@ def main(argv=None):
     ap.add_argument("--limit", type=int, default=240, help="seconds per pass")
     ap.add_argument("--summarize-only", action="store_true",
                     help="do not run anything; summarise the raw output of an earlier run")
+    ap.add_argument("--baselines", action="store_true",
+                    help="instead: one kernel-statistics pass of a short run that also times "
+                         "the contrast baselines (kernels_baselines_<workload>.txt)")
     args = ap.parse_args(argv)
+    if args.baselines:
+        return baselines_pass(args)
     sys.path.insert(0, ROOT)
     import bench  # algorithmic byte counts; bench imports torch lazily
 
