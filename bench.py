@@ -150,6 +150,50 @@ def gpu_baselines(fk, torch, x, ids, centers, ws, dtype: str, reps: int = 3):
             "note": "each call on its own, same inputs; fk_update here also computes the shift"}
 
 
+PEAK_PCIE = 64.0   # GB/s, PCIe 5.0 x16, one direction
+
+
+def host_stream(fk, torch, synthdata, w, args):
+    """fk_lloyd_host on the workload with x in page-locked host memory: every
+    iteration streams all of x over PCIe, so the bound is the host link."""
+    dev = torch.device("cuda:0")
+    xh = synthdata.to_torch(w.x, w.dtype).contiguous().pin_memory()
+    init = synthdata.to_torch(w.init, w.dtype).to(dev)
+    B, N, d, K = w.B, w.N, w.d, w.K
+    ids = torch.empty((B, N), dtype=torch.int32, device=dev)
+    centers = torch.empty((B, K, d), dtype=torch.float32, device=dev)
+    n = fk.fk_workspace_size_host(xh.dtype, B, args.host_stream, d, K)
+    raw = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + n]
+    if args.warmup > 0:
+        fk.fk_lloyd_host(xh, init, args.warmup, 0.0, args.host_stream, ids, centers, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    _, _, n_iter = fk.fk_lloyd_host(xh, init, args.steps, 0.0, args.host_stream, ids, centers, ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert n_iter == args.steps
+    x_bytes = B * N * d * elem_bytes(w.dtype)
+    gbps = x_bytes * args.steps / elapsed / 1e9
+    out = {
+        "metric": METRIC, "value": args.steps / elapsed, "unit": "iter/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload} host-streamed: B={B} N={N} d={d} K={K} "
+                               f"{w.dtype}, x in page-locked host memory, {args.host_stream} "
+                               f"points per problem per copy, {args.steps} Lloyd iterations, "
+                               "tol=0",
+                   "B": B, "N": N, "d": d, "K": K, "chunk": args.host_stream},
+        "roofline": {"bound": "pcie", "achieved": gbps, "peak": PEAK_PCIE, "unit": "GB/s",
+                     "frac": gbps / PEAK_PCIE, "traffic": None,
+                     "kernel": "host-to-device copies of x (the Lloyd kernels overlap them)"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out))
+
+
 def copy_calibration(mib: int, dev):
     """A plain elementwise kernel over a buffer of known size, for scaling
     the HBM byte counters (reads and writes mib MiB each)."""
@@ -172,6 +216,9 @@ def main():
                     help="1 = time the oracle on its bounded sample, 0 = skip")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="after the timed region, run a copy kernel of this size (counter scaling)")
+    ap.add_argument("--host-stream", type=int, default=0, metavar="CHUNK",
+                    help="keep x in page-locked host memory and run fk_lloyd_host, streaming "
+                         "CHUNK points per problem per copy (0 = the device-resident loop)")
     ap.add_argument("--baselines", type=int, default=1,
                     help="1 = after the timed region, time the materialised-distance assign and "
                          "the scatter-atomic update on the same inputs, 0 = skip")
@@ -191,6 +238,9 @@ def main():
     fk.load()
     dev = torch.device("cuda:0")
     w = synthdata.make_workload(args.workload)
+    if args.host_stream > 0:
+        host_stream(fk, torch, synthdata, w, args)
+        return
     x = synthdata.to_torch(w.x, w.dtype).to(dev)
     init = synthdata.to_torch(w.init, w.dtype).to(dev)
     B, N, d, K = w.B, w.N, w.d, w.K

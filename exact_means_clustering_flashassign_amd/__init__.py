@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     dtype_code,
     fk_assign,
     fk_lloyd,
+    fk_lloyd_host,
     fk_norms,
     fk_status_string,
     fk_trace_begin,
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     fk_update,
     fk_version,
     fk_workspace_size,
+    fk_workspace_size_host,
     fkb_assign_materialized,
     fkb_update_atomic,
     load,

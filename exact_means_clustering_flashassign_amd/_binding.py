@@ -52,6 +52,10 @@ def load(path: Optional[str] = None):
         "fk_update": (ctypes.c_int, [P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, P, SZ, P]),
         "fk_lloyd": (ctypes.c_int, [P, ctypes.c_int, I64, I64, I64, I64, P, I32, ctypes.c_float,
                                     P, P, ctypes.POINTER(I32), P, SZ, P]),
+        "fk_workspace_size_host": (SZ, [ctypes.c_int, I64, I64, I64, I64]),
+        "fk_lloyd_host": (ctypes.c_int, [P, ctypes.c_int, I64, I64, I64, I64, P, I32,
+                                         ctypes.c_float, I64, P, P, ctypes.POINTER(I32), P, SZ,
+                                         P]),
         "fk_trace_begin": (ctypes.c_int, [I32]),
         "fk_trace_end": (ctypes.c_int, [ctypes.POINTER(fk_trace_t)]),
     }
@@ -201,6 +205,47 @@ def fk_lloyd(x, init, max_iter: int, tol: float, ids=None, centers=None, ws=None
                          ctypes.byref(n_iter), _dev(ws, "ws", torch.uint8), ws.numel(),
                          _stream(x))
     _check(st, "fk_lloyd")
+    return ids, centers, int(n_iter.value)
+
+
+def fk_workspace_size_host(dtype, B: int, chunk: int, d: int, K: int) -> int:
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    return int(load().fk_workspace_size_host(code, B, chunk, d, K))
+
+
+def fk_lloyd_host(x_host, init, max_iter: int, tol: float, chunk: int, ids=None, centers=None,
+                  ws=None):
+    """Lloyd's loop over points in host memory, streamed in chunks of `chunk`
+    points per problem -> (ids, centers fp32, n_iter). x_host: a contiguous
+    CPU tensor (B,N,d), best page-locked (pin_memory); init (B,K,d) on the GPU."""
+    torch = _torch()
+    if not isinstance(x_host, torch.Tensor) or x_host.device.type != "cpu":
+        raise ValueError("x_host must be a CPU tensor")
+    if not x_host.is_contiguous() or x_host.dim() != 3:
+        raise ValueError("x_host must be a contiguous (B, N, d) tensor")
+    code = dtype_code(x_host.dtype)
+    B, N, d = x_host.shape
+    K = init.shape[1]
+    dev = init.device
+    if ids is None:
+        ids = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if centers is None:
+        centers = torch.empty((B, K, d), dtype=torch.float32, device=dev)
+    if ws is None:
+        n = fk_workspace_size_host(code, B, chunk, d, K)
+        if n == 0:
+            raise ValueError("invalid problem size or chunk")
+        raw = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        off = (-raw.data_ptr()) % 256
+        ws = raw[off:off + n]
+    n_iter = ctypes.c_int32(0)
+    st = load().fk_lloyd_host(x_host.data_ptr(), code, B, N, d, K,
+                              _dev(init, "init", x_host.dtype, (B, K, d)), int(max_iter),
+                              float(tol), int(chunk), _dev(ids, "ids", torch.int32, (B, N)),
+                              _dev(centers, "centers", torch.float32, (B, K, d)),
+                              ctypes.byref(n_iter), _dev(ws, "ws", torch.uint8), ws.numel(),
+                              _stream(init))
+    _check(st, "fk_lloyd_host")
     return ids, centers, int(n_iter.value)
 
 

@@ -79,6 +79,80 @@ LloydWs carve_lloyd(void* base, int dt, int64_t B, int64_t N, int64_t d, int64_t
   return w;
 }
 
+// Workspace of the host-streamed loop: two chunk buffers, the chunk's ids,
+// the update scratch for one chunk, the running sums and counts, the
+// chunk's counts, rounded centroids, norms, shift and shift partials.
+struct HostWs {
+  void* xbuf[2];
+  int32_t* ids_chunk;
+  UpdateWs upd;
+  float* sums;
+  int32_t* counts;
+  int32_t* counts_chunk;
+  void* c_lp;
+  float* cnorm;
+  float* shift;
+  float* part;
+};
+
+size_t host_ws_bytes(int dt, int64_t B, int64_t chunk, int64_t d, int64_t K) {
+  return 2 * align256((size_t)B * chunk * d * elem_bytes(dt)) + align256((size_t)B * chunk * 4) +
+         fk::update_ws_bytes(B, chunk, d, K) + align256((size_t)B * K * d * 4) +
+         2 * align256((size_t)B * K * 4) + align256((size_t)B * K * d * elem_bytes(dt)) +
+         align256((size_t)B * K * 4) + align256((size_t)B * 4) +
+         align256((size_t)B * fk::sums_fin_blocks(K, d) * 4);
+}
+
+HostWs carve_host(void* base, int dt, int64_t B, int64_t chunk, int64_t d, int64_t K) {
+  HostWs w;
+  char* p = static_cast<char*>(base);
+  for (int i = 0; i < 2; ++i) {
+    w.xbuf[i] = p;
+    p += align256((size_t)B * chunk * d * elem_bytes(dt));
+  }
+  w.ids_chunk = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)B * chunk * 4);
+  w.upd = fk::carve_update_ws(p, B, chunk, d, K);
+  p += fk::update_ws_bytes(B, chunk, d, K);
+  w.sums = reinterpret_cast<float*>(p);
+  p += align256((size_t)B * K * d * 4);
+  w.counts = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)B * K * 4);
+  w.counts_chunk = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)B * K * 4);
+  w.c_lp = p;
+  p += align256((size_t)B * K * d * elem_bytes(dt));
+  w.cnorm = reinterpret_cast<float*>(p);
+  p += align256((size_t)B * K * 4);
+  w.shift = reinterpret_cast<float*>(p);
+  p += align256((size_t)B * 4);
+  w.part = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// The copy stream and events of one host-streamed call, released on every
+// return path.
+struct StreamSet {
+  hipStream_t copy = nullptr;
+  hipEvent_t ready[2] = {nullptr, nullptr};
+  hipEvent_t free_[2] = {nullptr, nullptr};
+  bool ok = false;
+  StreamSet() {
+    ok = hipStreamCreateWithFlags(&copy, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; i < 2 && ok; ++i)
+      ok = hipEventCreateWithFlags(&ready[i], hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&free_[i], hipEventDisableTiming) == hipSuccess;
+  }
+  ~StreamSet() {   // teardown errors have no one to report to
+    if (copy) (void)hipStreamSynchronize(copy);
+    for (int i = 0; i < 2; ++i) {
+      if (ready[i]) (void)hipEventDestroy(ready[i]);
+      if (free_[i]) (void)hipEventDestroy(free_[i]);
+    }
+    if (copy) (void)hipStreamDestroy(copy);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // trace
 struct Trace {
@@ -90,7 +164,7 @@ struct Trace {
 Trace g_trace;
 
 void trace_release() {
-  for (hipEvent_t e : g_trace.ev) hipEventDestroy(e);
+  for (hipEvent_t e : g_trace.ev) (void)hipEventDestroy(e);
   g_trace.ev.clear();
   g_trace.on = false;
   g_trace.capacity = g_trace.used = 0;
@@ -206,6 +280,86 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
   }
   *n_iter = done;
   return FK_OK;
+}
+
+size_t fk_workspace_size_host(fk_dtype_t dt, int64_t B, int64_t chunk, int64_t d, int64_t K) {
+  if (!valid_dt(dt) || chunk < 1 || !valid_sizes(B, chunk, d, K)) return 0;
+  const size_t n = host_ws_bytes(dt, B, chunk, d, K);
+  return n < 256 ? 256 : n;
+}
+
+fk_status_t fk_lloyd_host(const void* x_host, fk_dtype_t dt, int64_t B, int64_t N, int64_t d,
+                          int64_t K, const void* init, int32_t max_iter, float tol,
+                          int64_t chunk, int32_t* ids, float* centers, int32_t* n_iter,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dt(dt) || !valid_sizes(B, N, d, K) || chunk < 1) return FK_ERR_INVALID;
+  if (max_iter < 0 || !(tol >= 0.f) || !n_iter) return FK_ERR_INVALID;
+  if (B > 0 && (!init || !centers)) return FK_ERR_INVALID;
+  if (B * N > 0 && (!x_host || !ids)) return FK_ERR_INVALID;
+  *n_iter = 0;
+  if (B == 0) return FK_OK;
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < fk_workspace_size_host(dt, B, chunk, d, K))
+    return FK_ERR_WORKSPACE;
+  const HostWs w = carve_host(ws, dt, B, chunk, d, K);
+  if (fk::launch_widen(init, centers, dt, B * K * d, stream) != hipSuccess) return FK_ERR_HIP;
+  if (max_iter == 0) {
+    if (fk::launch_fill_i32(ids, 0, B * N, stream) != hipSuccess) return FK_ERR_HIP;
+    return hip_status(hipStreamSynchronize(stream));
+  }
+  StreamSet ss;
+  if (!ss.ok) return FK_ERR_HIP;
+  const size_t es = (size_t)elem_bytes(dt);
+  const int64_t cmax = chunk < N ? chunk : N;
+  const int64_t nchunks = N > 0 ? (N + cmax - 1) / cmax : 0;
+  for (int i = 0; i < 2; ++i)
+    if (hipEventRecord(ss.free_[i], stream) != hipSuccess) return FK_ERR_HIP;
+  std::vector<float> host_shift(tol > 0.f ? (size_t)B : 0);
+  int32_t done = 0;
+  for (int32_t t = 0; t < max_iter; ++t) {
+    if (fk::launch_norms(centers, w.c_lp, w.cnorm, dt, B * K, d, stream) != hipSuccess ||
+        fk::launch_zero_sums(w.sums, w.counts, B, K, d, stream) != hipSuccess)
+      return FK_ERR_HIP;
+    for (int64_t i = 0; i < nchunks; ++i) {
+      const int slot = (int)(i & 1);
+      const int64_t n0 = i * cmax, cn = (N - n0) < cmax ? (N - n0) : cmax;
+      // copy stream: the slot's previous chunk is done, then x[:, n0:n0+cn]
+      if (hipStreamWaitEvent(ss.copy, ss.free_[slot], 0) != hipSuccess ||
+          hipMemcpy2DAsync(w.xbuf[slot], (size_t)cn * d * es,
+                           static_cast<const char*>(x_host) + (size_t)n0 * d * es,
+                           (size_t)N * d * es, (size_t)cn * d * es, (size_t)B,
+                           hipMemcpyHostToDevice, ss.copy) != hipSuccess ||
+          hipEventRecord(ss.ready[slot], ss.copy) != hipSuccess ||
+          hipStreamWaitEvent(stream, ss.ready[slot], 0) != hipSuccess)
+        return FK_ERR_HIP;
+      hipError_t e = run_assign(w.xbuf[slot], w.c_lp, w.cnorm, dt, B, cn, d, K, w.ids_chunk,
+                                stream);
+      if (e == hipErrorNotSupported || e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
+      if (e != hipSuccess) return FK_ERR_HIP;
+      if (hipMemcpy2DAsync(ids + n0, (size_t)N * 4, w.ids_chunk, (size_t)cn * 4, (size_t)cn * 4,
+                           (size_t)B, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+        return FK_ERR_HIP;
+      e = fk::launch_update_accumulate(w.xbuf[slot], w.ids_chunk, dt, B, cn, d, K, w.sums,
+                                       w.counts, w.counts_chunk, w.upd, stream);
+      if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
+      if (e != hipSuccess || hipEventRecord(ss.free_[slot], stream) != hipSuccess)
+        return FK_ERR_HIP;
+    }
+    if (fk::launch_finalize_sums(w.sums, w.counts, centers, tol > 0.f ? w.shift : nullptr,
+                                 w.part, B, K, d, stream) != hipSuccess)
+      return FK_ERR_HIP;
+    done = t + 1;
+    if (tol > 0.f) {
+      if (hipMemcpyAsync(host_shift.data(), w.shift, (size_t)B * sizeof(float),
+                         hipMemcpyDeviceToHost, stream) != hipSuccess ||
+          hipStreamSynchronize(stream) != hipSuccess)
+        return FK_ERR_HIP;
+      float mx = host_shift[0];
+      for (int64_t b = 1; b < B; ++b) mx = host_shift[b] > mx ? host_shift[b] : mx;
+      if (mx < tol) break;
+    }
+  }
+  *n_iter = done;
+  return hip_status(hipStreamSynchronize(stream));
 }
 
 fk_status_t fk_trace_begin(int32_t capacity) {

@@ -185,4 +185,20 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
                          int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
                          const UpdateWs& ws, hipStream_t s);
 
+// Accumulating update for points that arrive in chunks: the sorted segments
+// of one chunk are added into sums_run with atomics and its counts into
+// counts_run (counts_chunk: scratch of B*K ints); ws sized for the chunk.
+hipError_t launch_update_accumulate(const void* x, const int32_t* ids, int dt, int64_t B,
+                                    int64_t N, int64_t d, int64_t K, float* sums_run,
+                                    int32_t* counts_run, int32_t* counts_chunk,
+                                    const UpdateWs& ws, hipStream_t s);
+hipError_t launch_zero_sums(float* sums, int32_t* counts, int64_t B, int64_t K, int64_t d,
+                            hipStream_t s);
+// c = sums / counts for non-empty clusters; shift (nullable) from part, which
+// holds B * sums_fin_blocks(K, d) floats.
+int64_t sums_fin_blocks(int64_t K, int64_t d);
+hipError_t launch_finalize_sums(const float* sums, const int32_t* counts, float* c,
+                                float* shift, float* part, int64_t B, int64_t K, int64_t d,
+                                hipStream_t s);
+
 }  // namespace fk

@@ -201,13 +201,13 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   int run = block_exclusive_scan(s, wtot, total);
   int32_t* ob = offsets + (int64_t)b * (K + 1);
   int32_t* rf = run_first + (int64_t)b * runs;
-  float* sb = sums + (int64_t)b * K * d;
+  float* sb = sums ? sums + (int64_t)b * K * d : nullptr;   // null: no rows to zero
   for (int i = lo; i < hi; ++i) {
     const int c = cnt[i];
     if (G > 0) cb[i] = c;
     cnt[i] = run;
     if (G > 0 && c > 0) mark_runs(rf, i, run, run + c);
-    if (G > 0 && is_long(run, run + c)) {
+    if (G > 0 && sb && is_long(run, run + c)) {
       const int q = atomicAdd(&nlong, 1);
       if (q < kLongList) longs[q] = i;
       else zero_row(sb + (int64_t)i * d, d);     // past the list: this thread alone
@@ -222,6 +222,7 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   for (int64_t r = (total + (int64_t)kSegRun - 1) / kSegRun + t; r < runs; r += kSortThreads)
     rf[r] = K;                                   // runs past the last valid position
   // the listed long clusters' sums rows, spread over the block
+  if (!sb) return;
   const int nl = min(nlong, kLongList);
   if (d % 4 == 0) {
     const int nv = d / 4;
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const int32_t* __restric
     if (hi <= lo) continue;
     for (int64_t r = (lo + (int64_t)kSegRun - 1) / kSegRun + lane; r * kSegRun < hi; r += 64)
       rf[r] = k;
-    if (is_long(lo, hi)) {
+    if (sums && is_long(lo, hi)) {
       float* row = sums + ((int64_t)b * K + k) * d;
       for (int i = lane; i < d; i += 64) row[i] = 0.f;
     }
@@ -546,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     const void* __restrict__ x, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ run_first,
     float* __restrict__ sums, float* __restrict__ c, float* __restrict__ part, int part_stride,
-    int N, int d, int K, int runs, int slices, int64_t total_waves) {
+    int N, int d, int K, int runs, int slices, int64_t total_waves, bool acc_all) {
   constexpr int R = 64 / LPR;                    // rows per wave instruction
   constexpr int EB = DT == FK_F32 ? 4 : 2;
   constexpr int EV = 16 / EB;                    // elements per 16-byte vector
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
 #pragma unroll
     for (int i = 0; i < EV; ++i) acc[i] = group_sum<LPR>(acc[i]);
     if (g == 0 && colok) {
-      if (jcnt > 0) {                            // short: the finished mean, straight into c
+      if (jcnt > 0 && !acc_all) {                // short: the finished mean, straight into c
         float* row = cb + (int64_t)jk * d + col;
         const float inv = 1.0f / (float)jcnt;
         float nw[EV];
@@ -709,8 +710,8 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
             }
           }
         }
-      } else {                                   // a piece of a long segment
-        float* row = sb + (int64_t)jk * d + col;
+      } else {                                   // a piece of a long segment, or any
+        float* row = sb + (int64_t)jk * d + col;   // segment when accumulating
 #pragma unroll
         for (int i = 0; i < EV; ++i)
           if (col + i < d) unsafeAtomicAdd(row + i, acc[i]);
@@ -843,6 +844,55 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
   }
 }
 
+// Accumulating update over chunks of points (the host-streamed Lloyd loop):
+// counts_run += counts of one chunk.
+__global__ __launch_bounds__(kThreads) void add_counts_kernel(int32_t* __restrict__ run,
+                                                              const int32_t* __restrict__ chunk,
+                                                              int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+    run[i] += chunk[i];
+}
+
+// After the last chunk: c = sums / count for non-empty clusters (empty ones
+// keep c), one thread per element, blocks_per_batch blocks per problem
+// striding over its (K, d) block; with SHIFT each block's squared moves go to
+// part[b * blocks_per_batch + j].
+template <bool SHIFT>
+__global__ __launch_bounds__(kThreads) void finalize_sums_kernel(
+    const float* __restrict__ sums, const int32_t* __restrict__ counts, float* __restrict__ c,
+    float* __restrict__ part, int64_t per, int d, int blocks_per_batch) {
+  __shared__ float wsum[kThreads / 64];
+  const int b = blockIdx.x / blocks_per_batch, j = blockIdx.x % blocks_per_batch;
+  const float* sb = sums + (int64_t)b * per;
+  const int32_t* nb = counts + (int64_t)b * (per / d);
+  float* cb = c + (int64_t)b * per;
+  float moved = 0.f;
+  for (int64_t e = (int64_t)j * kThreads + threadIdx.x; e < per;
+       e += (int64_t)blocks_per_batch * kThreads) {
+    const int n = nb[e / d];
+    if (n > 0) {
+      const float nw = sb[e] / (float)n;
+      if constexpr (SHIFT) {
+        const float dl = nw - cb[e];
+        moved = fmaf(dl, dl, moved);
+      }
+      cb[e] = nw;
+    }
+  }
+  if constexpr (SHIFT) {
+    moved = wave_sum(moved);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = moved;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) t += wsum[w];
+      part[(int64_t)b * blocks_per_batch + j] = t;
+    }
+  }
+}
+
 // shift[b] = sum of the problem's finalize partials, in index order.
 __global__ __launch_bounds__(kThreads) void shift_reduce_kernel(const float* __restrict__ part,
                                                                 float* __restrict__ shift,
@@ -930,7 +980,8 @@ int seg_slices_dt(int64_t d) {
 
 template <int DT, int LPR>
 hipError_t run_segreduce(const void* x, const UpdateWs& ws, int64_t B, int64_t N, int64_t d,
-                         int64_t K, float* c, float* part, int part_stride, hipStream_t s) {
+                         int64_t K, float* sums, float* c, float* part, int part_stride,
+                         bool acc_all, hipStream_t s) {
   constexpr int EB = DT == FK_F32 ? 4 : 2;
   const int runs = (int)((N + kSegRun - 1) / kSegRun);
   const int slices = seg_slices_dt<DT>(d);
@@ -941,25 +992,39 @@ hipError_t run_segreduce(const void* x, const UpdateWs& ws, int64_t B, int64_t N
   const bool vec = (d * EB) % 16 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)c % 16) == 0;
   if (vec)
     segreduce_kernel<DT, LPR, true><<<(unsigned)grid, kThreads, 0, s>>>(
-        x, ws.perm, ws.offsets, ws.run_first, ws.sums, c, part, part_stride, (int)N, (int)d,
-        (int)K, runs, slices, total);
+        x, ws.perm, ws.offsets, ws.run_first, sums, c, part, part_stride, (int)N, (int)d,
+        (int)K, runs, slices, total, acc_all);
   else
     segreduce_kernel<DT, LPR, false><<<(unsigned)grid, kThreads, 0, s>>>(
-        x, ws.perm, ws.offsets, ws.run_first, ws.sums, c, part, part_stride, (int)N, (int)d,
-        (int)K, runs, slices, total);
+        x, ws.perm, ws.offsets, ws.run_first, sums, c, part, part_stride, (int)N, (int)d,
+        (int)K, runs, slices, total, acc_all);
   return hipGetLastError();
 }
 
 // part: per-wave squared moves of short clusters (null: no shift), wave w of
 // problem b at part[b * part_stride + w].
+// acc_all: every segment is added with atomics into sums (an accumulating
+// pass over one chunk of points); c and part are not touched.
 template <int DT>
 hipError_t segreduce_dt(const void* x, const UpdateWs& ws, int64_t B, int64_t N, int64_t d,
-                        int64_t K, float* c, float* part, int part_stride, hipStream_t s) {
+                        int64_t K, float* sums, float* c, float* part, int part_stride,
+                        bool acc_all, hipStream_t s) {
   switch (seg_lanes<DT>(d)) {
-    case 4: return run_segreduce<DT, 4>(x, ws, B, N, d, K, c, part, part_stride, s);
-    case 8: return run_segreduce<DT, 8>(x, ws, B, N, d, K, c, part, part_stride, s);
-    default: return run_segreduce<DT, 16>(x, ws, B, N, d, K, c, part, part_stride, s);
+    case 4: return run_segreduce<DT, 4>(x, ws, B, N, d, K, sums, c, part, part_stride, acc_all, s);
+    case 8: return run_segreduce<DT, 8>(x, ws, B, N, d, K, sums, c, part, part_stride, acc_all, s);
+    default:
+      return run_segreduce<DT, 16>(x, ws, B, N, d, K, sums, c, part, part_stride, acc_all, s);
   }
+}
+
+hipError_t segreduce_any(const void* x, int dt, const UpdateWs& ws, int64_t B, int64_t N,
+                         int64_t d, int64_t K, float* sums, float* c, float* part,
+                         int part_stride, bool acc_all, hipStream_t s) {
+  if (dt == FK_F16)
+    return segreduce_dt<FK_F16>(x, ws, B, N, d, K, sums, c, part, part_stride, acc_all, s);
+  if (dt == FK_BF16)
+    return segreduce_dt<FK_BF16>(x, ws, B, N, d, K, sums, c, part, part_stride, acc_all, s);
+  return segreduce_dt<FK_F32>(x, ws, B, N, d, K, sums, c, part, part_stride, acc_all, s);
 }
 
 // segreduce waves per problem (one per run and column slice)
@@ -1022,21 +1087,12 @@ UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K)
   return w;
 }
 
-hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, int64_t N,
-                         int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
-                         const UpdateWs& ws, hipStream_t s) {
-  if (B == 0) return hipSuccess;
-  if (N == 0) {
-    // no point: every cluster is empty and keeps its centroid
-    int64_t g = (B * K + kThreads - 1) / kThreads;
-    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
-    zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
-    FK_CHECK(hipGetLastError());
-    if (shift) fill_f32_kernel<<<1, kThreads, 0, s>>>(shift, 0.f, B);
-    return hipGetLastError();
-  }
+// Counting sort of a batch's ids into per-cluster segments: counts, offsets,
+// run starts, perm. zsums: the sums rows of long clusters are zeroed there
+// (null: left alone).
+hipError_t run_sort(const int32_t* ids, int64_t B, int64_t N, int64_t d, int64_t K,
+                    int32_t* counts, float* zsums, const UpdateWs& ws, hipStream_t s) {
   const int runs = (int)((N + kSegRun - 1) / kSegRun);
-  const int64_t fb = fin_blocks(K, d);
   const int G = split_groups(B, N, K);
   if (G > 0) {
     const int chunk = (int)((N + G - 1) / G);
@@ -1056,7 +1112,7 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
     FK_CHECK(hipGetLastError());
     if ((int64_t)G * K <= kFusedOffsetsMax) {
       offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
-                                                            ws.run_first, ws.sums, ws.has_long,
+                                                            ws.run_first, zsums, ws.has_long,
                                                             (int)K, (int)d, G, runs);
       FK_CHECK(hipGetLastError());
     } else {
@@ -1065,11 +1121,11 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
                                                                   kblocks);
       FK_CHECK(hipGetLastError());
       offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
-                                                             ws.run_first, ws.sums, ws.has_long,
+                                                             ws.run_first, zsums, ws.has_long,
                                                              (int)K, (int)d, 0, runs);
       FK_CHECK(hipGetLastError());
       const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);
-      prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.sums,
+      prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, zsums,
                                                            ws.has_long, (int)K, (int)d, runs, pb);
       FK_CHECK(hipGetLastError());
     }
@@ -1100,22 +1156,35 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
     scan_kernel<<<(unsigned)B, kSortThreads, 0, s>>>(counts, ws.offsets, ws.cursor, (int)K);
     FK_CHECK(hipGetLastError());
     const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);   // blocks per problem
-    prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.sums,
+    prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, zsums,
                                                          ws.has_long, (int)K, (int)d, runs, pb);
     FK_CHECK(hipGetLastError());
     FK_CHECK(run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
   }
+  return hipSuccess;
+}
+
+hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, int64_t N,
+                         int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
+                         const UpdateWs& ws, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  if (N == 0) {
+    // no point: every cluster is empty and keeps its centroid
+    int64_t g = (B * K + kThreads - 1) / kThreads;
+    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+    zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
+    FK_CHECK(hipGetLastError());
+    if (shift) fill_f32_kernel<<<1, kThreads, 0, s>>>(shift, 0.f, B);
+    return hipGetLastError();
+  }
+  const int64_t fb = fin_blocks(K, d);
+  FK_CHECK(run_sort(ids, B, N, d, K, counts, ws.sums, ws, s));
   // shift partials of a problem: its segreduce waves, then its finalize blocks
   const int64_t sw = seg_waves(dt, N, d);
   const int64_t pstride = sw + fb;
   if (pstride > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   float* spart = shift ? ws.part : nullptr;
-  if (dt == FK_F16)
-    FK_CHECK(segreduce_dt<FK_F16>(x, ws, B, N, d, K, c, spart, (int)pstride, s));
-  else if (dt == FK_BF16)
-    FK_CHECK(segreduce_dt<FK_BF16>(x, ws, B, N, d, K, c, spart, (int)pstride, s));
-  else
-    FK_CHECK(segreduce_dt<FK_F32>(x, ws, B, N, d, K, c, spart, (int)pstride, s));
+  FK_CHECK(segreduce_any(x, dt, ws, B, N, d, K, ws.sums, c, spart, (int)pstride, false, s));
   const int64_t grid = B * fb;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const bool fvec = d % kFinVec == 0 && ((uintptr_t)c % 16) == 0;
@@ -1129,6 +1198,54 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
       fvec);
   FK_CHECK(hipGetLastError());
   shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, (int)pstride);
+  return hipGetLastError();
+}
+
+// Finalize blocks per problem of finalize_sums_kernel.
+int64_t sums_fin_blocks(int64_t K, int64_t d) {
+  const int64_t g = (K * d + kThreads - 1) / kThreads;
+  return g < 64 ? (g < 1 ? 1 : g) : 64;
+}
+
+hipError_t launch_update_accumulate(const void* x, const int32_t* ids, int dt, int64_t B,
+                                    int64_t N, int64_t d, int64_t K, float* sums_run,
+                                    int32_t* counts_run, int32_t* counts_chunk,
+                                    const UpdateWs& ws, hipStream_t s) {
+  if (B == 0 || N == 0) return hipSuccess;
+  FK_CHECK(run_sort(ids, B, N, d, K, counts_chunk, nullptr, ws, s));
+  FK_CHECK(segreduce_any(x, dt, ws, B, N, d, K, sums_run, nullptr, nullptr, 0, true, s));
+  int64_t g = (B * K + kThreads - 1) / kThreads;
+  g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+  add_counts_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts_run, counts_chunk, B * K);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_sums(float* sums, int32_t* counts, int64_t B, int64_t K, int64_t d,
+                            hipStream_t s) {
+  int64_t g = (B * K * d + kThreads - 1) / kThreads;
+  g = g < 1 ? 1 : (g > 8192 ? 8192 : g);
+  zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(reinterpret_cast<int32_t*>(sums), B * K * d);
+  FK_CHECK(hipGetLastError());
+  g = (B * K + kThreads - 1) / kThreads;
+  g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+  zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_sums(const float* sums, const int32_t* counts, float* c,
+                                float* shift, float* part, int64_t B, int64_t K, int64_t d,
+                                hipStream_t s) {
+  const int64_t fb = sums_fin_blocks(K, d);
+  if (B * fb > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (!shift) {
+    finalize_sums_kernel<false><<<(unsigned)(B * fb), kThreads, 0, s>>>(sums, counts, c, part,
+                                                                       K * d, (int)d, (int)fb);
+    return hipGetLastError();
+  }
+  finalize_sums_kernel<true><<<(unsigned)(B * fb), kThreads, 0, s>>>(sums, counts, c, part,
+                                                                    K * d, (int)d, (int)fb);
+  FK_CHECK(hipGetLastError());
+  shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(part, shift, (int)fb);
   return hipGetLastError();
 }
 

@@ -13,7 +13,9 @@
  *                indices; the points themselves never move), on-chip segment
  *                reductions with one atomic per segment piece, then the new
  *                centroids and the centre shift;
- *   - fk_lloyd : the loop over those steps with the tol test.
+ *   - fk_lloyd : the loop over those steps with the tol test;
+ *   - fk_lloyd_host: the same loop for points kept in host memory, streamed
+ *                through the device in chunks every iteration.
  *
  * Sources (web pages describing flash-kmeans):
  *   [hysenlabs] "flash-kmeans and the return of exact K-Means on the GPU"
@@ -27,8 +29,8 @@
  *   Layout     : dense row-major. x (B,N,d) and centroid copies (B,K,d) are in
  *                the element type dt; ids (B,N) and counts (B,K) are int32;
  *                master centroids (B,K,d), norms (B,K) and shift (B) are fp32.
- *   Memory     : every pointer except n_iter (host) is device memory owned by
- *                the caller. The library allocates no device memory and keeps
+ *   Memory     : every pointer except n_iter and fk_lloyd_host's x_host
+ *                (host) is device memory owned by the caller. The library allocates no device memory and keeps
  *                no state between calls except the optional timing trace.
  *   Streams    : work is enqueued on `stream` and is asynchronous, except that
  *                fk_lloyd with tol > 0 waits for each iteration's shift.
@@ -144,6 +146,34 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
                      const void* init, int32_t max_iter, float tol,
                      int32_t* ids, float* centers, int32_t* n_iter,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Host-streamed Lloyd's loop, for points that stay in host memory (more
+ * than fits the device, or not worth a resident copy). Every iteration
+ * streams x through two device buffers of `chunk` points per problem: the
+ * copy of one chunk overlaps the assign and the accumulating update of the
+ * previous one, and the next iteration's first chunks overlap the end of
+ * the current one. The update adds each chunk's sorted segments into
+ * running fp32 sums (atomics) and counts, and divides after the last chunk.
+ * [hysenlabs] section on multi-GPU scaling for large N: contiguous blocks of
+ * points, a double-buffered host-to-device and compute pipeline, the next
+ * iteration's first block prefetched during the reduction (one GPU here).
+ *   x_host (B,N,d) dt in host memory; page-locked memory (hipHostMalloc)
+ *   lets the copies overlap, pageable memory still works. init, ids,
+ *   centers, n_iter, max_iter, tol and the stop rule as fk_lloyd.
+ *   chunk >= 1: points per problem per copy (clamped to N).
+ *   ws: fk_workspace_size_host(dt, B, chunk, d, K) bytes, 256-byte aligned.
+ * The call creates one non-blocking copy stream and four events, and
+ * returns after all its work is done (it synchronises `stream`). Centroids
+ * may differ from fk_lloyd's in the last bits (summation order).
+ */
+fk_status_t fk_lloyd_host(const void* x_host, fk_dtype_t dt, int64_t B, int64_t N, int64_t d,
+                          int64_t K, const void* init, int32_t max_iter, float tol,
+                          int64_t chunk, int32_t* ids, float* centers, int32_t* n_iter,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes fk_lloyd_host needs; 0 for invalid arguments. */
+size_t fk_workspace_size_host(fk_dtype_t dt, int64_t B, int64_t chunk, int64_t d, int64_t K);
 
 /*
  * Optional timing trace of fk_lloyd (process-wide, not thread-safe).

@@ -105,6 +105,15 @@ def test_validation_rejects_before_launch(lib):
     n_iter.value = 5
     assert lib.fk_lloyd(null, 1, 0, 16, 8, 4, null, 3, 0.0, null, null, ctypes.byref(n_iter),
                         null, 0, null) == 0 and n_iter.value == 0
+    # host-streamed loop: chunk and workspace checks come before any HIP call
+    host = lambda chunk, ws, nbytes: lib.fk_lloyd_host(dummy, 1, 1, 16, 8, 4, dummy, 3, 0.0,
+                                                      chunk, dummy, dummy, ctypes.byref(n_iter),
+                                                      ws, nbytes, null)
+    assert host(0, dummy, 1 << 20) == INVALID
+    assert host(8, null, 0) == WORKSPACE
+    assert host(8, ctypes.c_void_p(257), 1 << 30) == WORKSPACE
+    assert lib.fk_workspace_size_host(1, 1, 0, 8, 4) == 0
+    assert lib.fk_workspace_size_host(1, 1, 8, 8, 4) >= lib.fk_workspace_size(1, 1, 8, 8, 4)
     # trace
     assert lib.fk_trace_begin(0) == INVALID
     assert lib.fk_trace_end(None) == INVALID
