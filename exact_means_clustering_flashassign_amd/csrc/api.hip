@@ -51,18 +51,22 @@ hipError_t run_assign(const void* x, const void* c_lp, const float* cn, int dt, 
   return fk::launch_assign_splitd(x, c_lp, cn, dt, B, N, d, K, ids, s);
 }
 
-// Workspace beyond the update's: rounded centroids, norms, counts, shift.
+// Workspace beyond the update's: rounded centroids, norms, counts, shift,
+// and (for the tol test) copies of the ids and centres of the last iteration
+// whose stop decision is still pending.
 struct LloydWs {
   UpdateWs upd;
   void* c_lp;
   float* cnorm;
   int32_t* counts;
   float* shift;
+  int32_t* ids_bak;
+  float* centers_bak;
 };
 
-size_t lloyd_extra_bytes(int dt, int64_t B, int64_t d, int64_t K) {
+size_t lloyd_extra_bytes(int dt, int64_t B, int64_t N, int64_t d, int64_t K) {
   return align256((size_t)B * K * d * elem_bytes(dt)) + align256((size_t)B * K * 4) * 2 +
-         align256((size_t)B * 4);
+         align256((size_t)B * 4) + align256((size_t)B * N * 4) + align256((size_t)B * K * d * 4);
 }
 
 LloydWs carve_lloyd(void* base, int dt, int64_t B, int64_t N, int64_t d, int64_t K) {
@@ -76,8 +80,31 @@ LloydWs carve_lloyd(void* base, int dt, int64_t B, int64_t N, int64_t d, int64_t
   w.counts = reinterpret_cast<int32_t*>(p);
   p += align256((size_t)B * K * 4);
   w.shift = reinterpret_cast<float*>(p);
+  p += align256((size_t)B * 4);
+  w.ids_bak = reinterpret_cast<int32_t*>(p);
+  p += align256((size_t)B * N * 4);
+  w.centers_bak = reinterpret_cast<float*>(p);
   return w;
 }
+
+// Page-locked host copies of the shift of the two most recent iterations and
+// the events that say they have arrived; released on every return path.
+struct ShiftReadback {
+  float* host = nullptr;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  bool ok = false;
+  explicit ShiftReadback(int64_t B) {
+    ok = hipHostMalloc((void**)&host, (size_t)2 * B * sizeof(float), hipHostMallocDefault) ==
+             hipSuccess &&
+         hipEventCreateWithFlags(&ev[0], hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&ev[1], hipEventDisableTiming) == hipSuccess;
+  }
+  ~ShiftReadback() {   // teardown errors have no one to report to
+    for (int i = 0; i < 2; ++i)
+      if (ev[i]) (void)hipEventSynchronize(ev[i]), (void)hipEventDestroy(ev[i]);
+    if (host) (void)hipHostFree(host);
+  }
+};
 
 // Workspace of the host-streamed loop: two chunk buffers, the chunk's ids,
 // the update scratch for one chunk, the running sums and counts, the
@@ -193,7 +220,7 @@ int32_t fk_version(void) { return 100; }
 
 size_t fk_workspace_size(fk_dtype_t dt, int64_t B, int64_t N, int64_t d, int64_t K) {
   if (!valid_dt(dt) || !valid_sizes(B, N, d, K)) return 0;
-  const size_t n = fk::update_ws_bytes(B, N, d, K) + lloyd_extra_bytes(dt, B, d, K);
+  const size_t n = fk::update_ws_bytes(B, N, d, K) + lloyd_extra_bytes(dt, B, N, d, K);
   return n < 256 ? 256 : n;   // never 0 for a valid problem (0 flags bad arguments)
 }
 
@@ -245,8 +272,16 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
   if (e != hipSuccess) return FK_ERR_HIP;
   if (max_iter == 0) return hip_status(fk::launch_fill_i32(ids, 0, B * N, stream));
 
-  std::vector<float> host_shift(tol > 0.f ? (size_t)B : 0);
-  int32_t done = 0;
+  // With tol > 0 the stop decision for iteration t is taken while iteration
+  // t + 1 already runs: t's shift comes back to page-locked host memory
+  // asynchronously, and its ids and centres are copied aside. If t turns out
+  // to have converged, those copies replace what t + 1 wrote, so the result
+  // is exactly that of stopping after t; the GPU never waits for the host.
+  const bool test = tol > 0.f;
+  ShiftReadback rb(test ? B : 1);
+  if (test && !rb.ok) return FK_ERR_HIP;
+  int32_t done = 0, pending = -1;
+  const size_t ids_bytes = (size_t)B * N * 4, c_bytes = (size_t)B * K * d * 4;
   for (int32_t t = 0; t < max_iter; ++t) {
     const bool tr = g_trace.on && g_trace.used < g_trace.capacity;
     const int32_t slot = g_trace.used;
@@ -259,7 +294,7 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
     if (e != hipSuccess) return FK_ERR_HIP;
     if (tr && hipEventRecord(trace_event(slot, 2), stream) != hipSuccess) return FK_ERR_HIP;
     // the shift is only read for the tol test
-    e = fk::launch_update(x, ids, dt, B, N, d, K, centers, w.counts, tol > 0.f ? w.shift : nullptr,
+    e = fk::launch_update(x, ids, dt, B, N, d, K, centers, w.counts, test ? w.shift : nullptr,
                           w.upd, stream);
     if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
     if (e != hipSuccess) return FK_ERR_HIP;
@@ -268,16 +303,37 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
       ++g_trace.used;
     }
     done = t + 1;
-    if (tol > 0.f) {
-      if (hipMemcpyAsync(host_shift.data(), w.shift, (size_t)B * sizeof(float),
-                         hipMemcpyDeviceToHost, stream) != hipSuccess)
+    if (!test) continue;
+    float* hs = rb.host + (size_t)(t & 1) * B;
+    if (hipMemcpyAsync(hs, w.shift, (size_t)B * sizeof(float), hipMemcpyDeviceToHost,
+                       stream) != hipSuccess ||
+        hipEventRecord(rb.ev[t & 1], stream) != hipSuccess)
+      return FK_ERR_HIP;
+    if (pending >= 0) {                          // decide on the previous iteration
+      if (hipEventSynchronize(rb.ev[pending & 1]) != hipSuccess) return FK_ERR_HIP;
+      const float* ps = rb.host + (size_t)(pending & 1) * B;
+      float mx = ps[0];
+      for (int64_t b = 1; b < B; ++b) mx = ps[b] > mx ? ps[b] : mx;
+      if (mx < tol) {                            // it converged: undo iteration t
+        if (hipMemcpyAsync(ids, w.ids_bak, ids_bytes, hipMemcpyDeviceToDevice, stream) !=
+                hipSuccess ||
+            hipMemcpyAsync(centers, w.centers_bak, c_bytes, hipMemcpyDeviceToDevice, stream) !=
+                hipSuccess)
+          return FK_ERR_HIP;
+        done = pending + 1;
+        break;
+      }
+    }
+    if (t + 1 < max_iter) {                      // keep t's results until t is decided
+      if (hipMemcpyAsync(w.ids_bak, ids, ids_bytes, hipMemcpyDeviceToDevice, stream) !=
+              hipSuccess ||
+          hipMemcpyAsync(w.centers_bak, centers, c_bytes, hipMemcpyDeviceToDevice, stream) !=
+              hipSuccess)
         return FK_ERR_HIP;
-      if (hipStreamSynchronize(stream) != hipSuccess) return FK_ERR_HIP;
-      float mx = host_shift[0];
-      for (int64_t b = 1; b < B; ++b) mx = host_shift[b] > mx ? host_shift[b] : mx;
-      if (mx < tol) break;
+      pending = t;
     }
   }
+  if (test && hipStreamSynchronize(stream) != hipSuccess) return FK_ERR_HIP;
   *n_iter = done;
   return FK_OK;
 }

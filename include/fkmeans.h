@@ -33,7 +33,9 @@
  *                (host) is device memory owned by the caller. The library allocates no device memory and keeps
  *                no state between calls except the optional timing trace.
  *   Streams    : work is enqueued on `stream` and is asynchronous, except that
- *                fk_lloyd with tol > 0 waits for each iteration's shift.
+ *                fk_lloyd with tol > 0 reads each iteration's shift back
+ *                (while the next iteration already runs) and returns once
+ *                the stream is idle, and fk_lloyd_host always returns done.
  *   Sizes      : B >= 0, N >= 0, d >= 1, K >= 1, N < 2^31, K < 2^31,
  *                B*N*d, B*K*d < 2^62. B == 0 or N == 0 is a valid empty
  *                problem: nothing is read, outputs are set as documented.
@@ -138,6 +140,10 @@ fk_status_t fk_update(const void* x, const int32_t* ids, fk_dtype_t dt,
  *   x (B,N,d) dt, init (B,K,d) dt in; ids (B,N) int32 out (from the last
  *   assignment; all 0 when max_iter == 0); centers (B,K,d) fp32 out (after
  *   the last update); *n_iter (host) = completed iterations.
+ * With tol > 0, iteration t + 1 is enqueued before t's shift has reached the
+ * host; when t turns out to be the last, the ids and centres of t (kept in
+ * the workspace) replace what t + 1 wrote, so the results are exactly those
+ * of stopping after t.
  * The batched API and its tol argument: [hysenlabs] "Exact K-Means, with the
  * assignment step written in Triton"; one step = one assignment plus one
  * centroid update: [paixiang] "什么是 Flash-KMeans".

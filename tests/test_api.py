@@ -127,3 +127,24 @@ def test_flashkmeans_train_predict(fk):
     km32 = fk.FlashKMeans(d=128, k=30, niter=2, tol=0.0, dtype=torch.float32, seed=2)
     ids32 = km32.fit_predict(xd)
     assert ids32.dtype == torch.int32 and km32.centroids.dtype == torch.float32
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("tol", [1e30, 1e-2])
+def test_tol_stop_returns_the_stopping_iteration(fk, tol):
+    """fk_lloyd with tol > 0 enqueues the next iteration before the stop test
+    of the current one is read; on a stop, the results must be those of the
+    stopping iteration (the rolled-back one leaves no trace)."""
+    torch = _torch()
+    x, _ = _mixture(2, 6000, 64, 30, "f16", seed=13)
+    xd = to_dev(x, "f16")
+    init = fk.random_init(xd, 30, seed=4)
+    ids_t, c_t, n = fk.fk_lloyd(xd, init, 60, tol)
+    ids_0, c_0, n0 = fk.fk_lloyd(xd, init, n, 0.0)
+    torch.cuda.synchronize()
+    assert n0 == n and 1 <= n < 60
+    if n == 1:   # the first assign sees the initial centroids: ids bit-exact
+        assert torch.equal(ids_t, ids_0)
+    else:        # later assigns see centres summed in no fixed order
+        assert int((ids_t != ids_0).sum()) <= ids_t.numel() // 10000
+    assert centroid_rel_err(c_t.cpu().numpy(), c_0.double().cpu().numpy()) <= 1e-5
