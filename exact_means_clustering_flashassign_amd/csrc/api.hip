@@ -278,6 +278,7 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
   // to have converged, those copies replace what t + 1 wrote, so the result
   // is exactly that of stopping after t; the GPU never waits for the host.
   const bool test = tol > 0.f;
+  const bool defer = !test && N > 0;
   ShiftReadback rb(test ? B : 1);
   if (test && !rb.ok) return FK_ERR_HIP;
   int32_t done = 0, pending = -1;
@@ -286,7 +287,10 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
     const bool tr = g_trace.on && g_trace.used < g_trace.capacity;
     const int32_t slot = g_trace.used;
     if (tr && hipEventRecord(trace_event(slot, 0), stream) != hipSuccess) return FK_ERR_HIP;
-    e = fk::launch_norms(centers, w.c_lp, w.cnorm, dt, B * K, d, stream);
+    // without the tol test, the previous update's long clusters are divided
+    // by this norms pass (it reads the centres anyway): one launch less
+    e = fk::launch_norms(centers, w.c_lp, w.cnorm, dt, B * K, d, stream,
+                         defer && t > 0 ? fk::pending_finish(w.upd, K) : fk::PendingFinish());
     if (e != hipSuccess) return FK_ERR_HIP;
     if (tr && hipEventRecord(trace_event(slot, 1), stream) != hipSuccess) return FK_ERR_HIP;
     e = run_assign(x, w.c_lp, w.cnorm, dt, B, N, d, K, ids, stream);
@@ -295,7 +299,7 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
     if (tr && hipEventRecord(trace_event(slot, 2), stream) != hipSuccess) return FK_ERR_HIP;
     // the shift is only read for the tol test
     e = fk::launch_update(x, ids, dt, B, N, d, K, centers, w.counts, test ? w.shift : nullptr,
-                          w.upd, stream);
+                          w.upd, stream, defer);
     if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
     if (e != hipSuccess) return FK_ERR_HIP;
     if (tr) {
@@ -333,6 +337,8 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
       pending = t;
     }
   }
+  if (defer && done > 0 && fk::launch_finish(centers, w.upd, B, d, K, stream) != hipSuccess)
+    return FK_ERR_HIP;
   if (test && hipStreamSynchronize(stream) != hipSuccess) return FK_ERR_HIP;
   *n_iter = done;
   return FK_OK;

@@ -149,10 +149,42 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t grid) {
 }
 
 // ---------------------------------------------------------------------------
+// segments of the sort-inverse update
+// ---------------------------------------------------------------------------
+constexpr int kSegRun = 256;   // sorted positions per segment-reduce run
+
+// A segment longer than one run is reduced in pieces whose sums meet in an
+// fp32 sums row; shorter ones are reduced whole and written as their mean.
+__device__ __forceinline__ bool is_long(int lo, int hi) { return hi - lo > kSegRun; }
+
+// An update whose long clusters still hold their sums (the division by the
+// count is left to the next pass over the centroids). sums null: nothing
+// pending.
+struct PendingFinish {
+  const float* sums = nullptr;          // (B,K,d)
+  const int32_t* offsets = nullptr;     // (B,K+1)
+  const int32_t* has_long = nullptr;    // (B)
+  int64_t K = 0;
+};
+
+// For centroid row `row` (= b*K + k): the count to divide its sums row by,
+// or 0 when the row is already final.
+__device__ __forceinline__ float pending_count(const PendingFinish& pf, int64_t row) {
+  if (!pf.sums) return 0.f;
+  const int64_t b = row / pf.K, k = row - b * pf.K;
+  if (!pf.has_long[b]) return 0.f;
+  const int32_t* ob = pf.offsets + b * (pf.K + 1);
+  const int lo = ob[k], hi = ob[k + 1];
+  return is_long(lo, hi) ? (float)(hi - lo) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
 // launchers (host); each returns hipSuccess or the launch error
 // ---------------------------------------------------------------------------
+// pf: an update to finish first (its long clusters' rows of c are divided
+// and written back, so c must then be writable).
 hipError_t launch_norms(const float* c, void* c_lp, float* cnorm, int dt, int64_t rows,
-                        int64_t d, hipStream_t s);
+                        int64_t d, hipStream_t s, const PendingFinish& pf = PendingFinish());
 hipError_t launch_widen(const void* src, float* dst, int dt, int64_t count, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t count, hipStream_t s);
 
@@ -181,9 +213,14 @@ struct UpdateWs {
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K);
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K);
 // shift may be null: the new centroids are written and no shift is computed.
+// defer (only with shift == null): the long clusters' division is left to
+// the next norms pass (see pending_finish) or to launch_finish.
 hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, int64_t N,
                          int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
-                         const UpdateWs& ws, hipStream_t s);
+                         const UpdateWs& ws, hipStream_t s, bool defer = false);
+PendingFinish pending_finish(const UpdateWs& ws, int64_t K);
+hipError_t launch_finish(float* c, const UpdateWs& ws, int64_t B, int64_t d, int64_t K,
+                         hipStream_t s);
 
 // Accumulating update for points that arrive in chunks: the sorted segments
 // of one chunk are added into sums_run with atomics and its counts into

@@ -15,19 +15,27 @@ namespace {
 
 constexpr int kWaves = 4;
 
+// Every norms kernel first finishes a deferred update (pf): a long cluster's
+// row is its sums row divided by its count, written back to c.
 template <int DT>
-__global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ c,
+__global__ __launch_bounds__(256) void norms_kernel(float* __restrict__ c,
                                                     uint16_t* __restrict__ c_lp,
                                                     float* __restrict__ cnorm, int64_t rows,
-                                                    int64_t d) {
+                                                    int64_t d, PendingFinish pf) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const float* src = c + row * d;
+  const float cnt = pending_count(pf, row);
+  const float* src = cnt > 0.f ? pf.sums + row * d : c + row * d;
   uint16_t* dst = c_lp + row * d;
   float acc = 0.f;
   for (int64_t j = lane; j < d; j += 64) {
-    const uint16_t h = Elem<DT>::narrow(src[j]);
+    float v = src[j];
+    if (cnt > 0.f) {
+      v = v / cnt;
+      c[row * d + j] = v;
+    }
+    const uint16_t h = Elem<DT>::narrow(v);
     dst[j] = h;
     const float r = Elem<DT>::widen(h);
     acc = fmaf(r, r, acc);
@@ -40,20 +48,25 @@ __global__ __launch_bounds__(256) void norms_kernel(const float* __restrict__ c,
 // per row, 4 elements per lane per step, so one wave covers 64/LPR rows; the
 // row's squares are summed over its lane group.
 template <int DT, int LPR>
-__global__ __launch_bounds__(256) void norms_vec_kernel(const float* __restrict__ c,
+__global__ __launch_bounds__(256) void norms_vec_kernel(float* __restrict__ c,
                                                         uint16_t* __restrict__ c_lp,
                                                         float* __restrict__ cnorm, int64_t rows,
-                                                        int d) {
+                                                        int d, PendingFinish pf) {
   constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63, li = lane % LPR;
   const int64_t row = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * RPW + lane / LPR;
   const bool ok = row < rows;
   float acc = 0.f;
   if (ok) {
-    const float* src = c + row * d;
+    const float cnt = pending_count(pf, row);
+    const float* src = cnt > 0.f ? pf.sums + row * d : c + row * d;
     uint16_t* dst = c_lp + row * d;
     for (int j = li * 4; j < d; j += LPR * 4) {
-      const float4 v = *reinterpret_cast<const float4*>(src + j);
+      float4 v = *reinterpret_cast<const float4*>(src + j);
+      if (cnt > 0.f) {                      // sums rows are 16-byte aligned like c's
+        v = make_float4(v.x / cnt, v.y / cnt, v.z / cnt, v.w / cnt);
+        *reinterpret_cast<float4*>(c + row * d + j) = v;
+      }
       const uint16_t h[4] = {Elem<DT>::narrow(v.x), Elem<DT>::narrow(v.y), Elem<DT>::narrow(v.z),
                              Elem<DT>::narrow(v.w)};
       *reinterpret_cast<uint2*>(dst + j) =
@@ -71,39 +84,45 @@ __global__ __launch_bounds__(256) void norms_vec_kernel(const float* __restrict_
 }
 
 template <int DT, int LPR>
-hipError_t run_norms_vec(const float* c, uint16_t* c_lp, float* cnorm, int64_t rows, int64_t d,
-                         hipStream_t s) {
+hipError_t run_norms_vec(float* c, uint16_t* c_lp, float* cnorm, int64_t rows, int64_t d,
+                         const PendingFinish& pf, hipStream_t s) {
   constexpr int RPB = kWaves * (64 / LPR);       // rows per block
   const int64_t grid = (rows + RPB - 1) / RPB;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  norms_vec_kernel<DT, LPR><<<(unsigned)grid, 256, 0, s>>>(c, c_lp, cnorm, rows, (int)d);
+  norms_vec_kernel<DT, LPR><<<(unsigned)grid, 256, 0, s>>>(c, c_lp, cnorm, rows, (int)d, pf);
   return hipGetLastError();
 }
 
 // lanes per row: the vectors of a row, rounded up to a power of two in [4, 64]
 template <int DT>
-hipError_t norms_vec_dt(const float* c, uint16_t* c_lp, float* cnorm, int64_t rows, int64_t d,
-                        hipStream_t s) {
+hipError_t norms_vec_dt(float* c, uint16_t* c_lp, float* cnorm, int64_t rows, int64_t d,
+                        const PendingFinish& pf, hipStream_t s) {
   const int64_t nv = d / 4;
-  if (nv <= 4) return run_norms_vec<DT, 4>(c, c_lp, cnorm, rows, d, s);
-  if (nv <= 8) return run_norms_vec<DT, 8>(c, c_lp, cnorm, rows, d, s);
-  if (nv <= 16) return run_norms_vec<DT, 16>(c, c_lp, cnorm, rows, d, s);
-  if (nv <= 32) return run_norms_vec<DT, 32>(c, c_lp, cnorm, rows, d, s);
-  return run_norms_vec<DT, 64>(c, c_lp, cnorm, rows, d, s);
+  if (nv <= 4) return run_norms_vec<DT, 4>(c, c_lp, cnorm, rows, d, pf, s);
+  if (nv <= 8) return run_norms_vec<DT, 8>(c, c_lp, cnorm, rows, d, pf, s);
+  if (nv <= 16) return run_norms_vec<DT, 16>(c, c_lp, cnorm, rows, d, pf, s);
+  if (nv <= 32) return run_norms_vec<DT, 32>(c, c_lp, cnorm, rows, d, pf, s);
+  return run_norms_vec<DT, 64>(c, c_lp, cnorm, rows, d, pf, s);
 }
 
-__global__ __launch_bounds__(256) void norms_f32_kernel(const float* __restrict__ c,
+__global__ __launch_bounds__(256) void norms_f32_kernel(float* __restrict__ c,
                                                         float* __restrict__ c_lp,
                                                         float* __restrict__ cnorm,
-                                                        int64_t rows, int64_t d) {
+                                                        int64_t rows, int64_t d,
+                                                        PendingFinish pf) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const float* src = c + row * d;
+  const float cnt = pending_count(pf, row);
+  const float* src = cnt > 0.f ? pf.sums + row * d : c + row * d;
   float* dst = c_lp + row * d;
   float acc = 0.f;
   for (int64_t j = lane; j < d; j += 64) {
-    const float r = src[j];
+    float r = src[j];
+    if (cnt > 0.f) {
+      r = r / cnt;
+      c[row * d + j] = r;
+    }
     dst[j] = r;
     acc = fmaf(r, r, acc);
   }
@@ -141,20 +160,24 @@ unsigned grid_for(int64_t count) {
 
 }  // namespace
 
-hipError_t launch_norms(const float* c, void* c_lp, float* cnorm, int dt, int64_t rows,
-                        int64_t d, hipStream_t s) {
+hipError_t launch_norms(const float* c_in, void* c_lp, float* cnorm, int dt, int64_t rows,
+                        int64_t d, hipStream_t s, const PendingFinish& pf) {
   if (rows == 0) return hipSuccess;
+  // written only when an update is pending (pf.sums), on the caller's own buffer
+  float* c = const_cast<float*>(c_in);
   const bool vec = d % 4 == 0 && d <= 0x7FFFFFFF && ((uintptr_t)c % 16) == 0 &&
-                   ((uintptr_t)c_lp % 8) == 0;
-  if (vec && dt == FK_F16) return norms_vec_dt<FK_F16>(c, (uint16_t*)c_lp, cnorm, rows, d, s);
-  if (vec && dt == FK_BF16) return norms_vec_dt<FK_BF16>(c, (uint16_t*)c_lp, cnorm, rows, d, s);
+                   ((uintptr_t)c_lp % 8) == 0 && ((uintptr_t)pf.sums % 16) == 0;
+  if (vec && dt == FK_F16)
+    return norms_vec_dt<FK_F16>(c, (uint16_t*)c_lp, cnorm, rows, d, pf, s);
+  if (vec && dt == FK_BF16)
+    return norms_vec_dt<FK_BF16>(c, (uint16_t*)c_lp, cnorm, rows, d, pf, s);
   const unsigned grid = (unsigned)((rows + kWaves - 1) / kWaves);
   if (dt == FK_F16)
-    norms_kernel<FK_F16><<<grid, 256, 0, s>>>(c, (uint16_t*)c_lp, cnorm, rows, d);
+    norms_kernel<FK_F16><<<grid, 256, 0, s>>>(c, (uint16_t*)c_lp, cnorm, rows, d, pf);
   else if (dt == FK_BF16)
-    norms_kernel<FK_BF16><<<grid, 256, 0, s>>>(c, (uint16_t*)c_lp, cnorm, rows, d);
+    norms_kernel<FK_BF16><<<grid, 256, 0, s>>>(c, (uint16_t*)c_lp, cnorm, rows, d, pf);
   else
-    norms_f32_kernel<<<grid, 256, 0, s>>>(c, (float*)c_lp, cnorm, rows, d);
+    norms_f32_kernel<<<grid, 256, 0, s>>>(c, (float*)c_lp, cnorm, rows, d, pf);
   return hipGetLastError();
 }
 

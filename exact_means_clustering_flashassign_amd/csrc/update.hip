@@ -45,7 +45,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxLdsBins = 32768;            // 128 KB of LDS bins per block
-constexpr int kSegRun = 256;                  // sorted positions per segreduce run
 constexpr int kSortThreads = 1024;
 constexpr int kSortUnroll = 16;               // ids in flight per thread in the sort kernels
 constexpr int64_t kFusedOffsetsMax = 1 << 16; // G*K up to this: one offsets block per problem
@@ -54,7 +53,6 @@ constexpr int kLongList = 1024;               // long clusters listed per proble
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-__device__ __forceinline__ bool is_long(int lo, int hi) { return hi - lo > kSegRun; }
 
 // Runs whose first position lies in [lo, hi) start inside cluster k.
 __device__ __forceinline__ void mark_runs(int32_t* rf, int k, int lo, int hi) {
@@ -1166,7 +1164,7 @@ hipError_t run_sort(const int32_t* ids, int64_t B, int64_t N, int64_t d, int64_t
 
 hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, int64_t N,
                          int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
-                         const UpdateWs& ws, hipStream_t s) {
+                         const UpdateWs& ws, hipStream_t s, bool defer) {
   if (B == 0) return hipSuccess;
   if (N == 0) {
     // no point: every cluster is empty and keeps its centroid
@@ -1189,6 +1187,7 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const bool fvec = d % kFinVec == 0 && ((uintptr_t)c % 16) == 0;
   if (!shift) {                                  // the caller does not need the shift
+    if (defer) return hipSuccess;                // the next norms pass divides
     finalize_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(
         ws.sums, ws.offsets, c, ws.part, 0, ws.has_long, (int)d, (int)K, (int)fb, fvec);
     return hipGetLastError();
@@ -1198,6 +1197,26 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
       fvec);
   FK_CHECK(hipGetLastError());
   shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, (int)pstride);
+  return hipGetLastError();
+}
+
+PendingFinish pending_finish(const UpdateWs& ws, int64_t K) {
+  PendingFinish pf;
+  pf.sums = ws.sums;
+  pf.offsets = ws.offsets;
+  pf.has_long = ws.has_long;
+  pf.K = K;
+  return pf;
+}
+
+// The division a deferred update left, when no norms pass follows.
+hipError_t launch_finish(float* c, const UpdateWs& ws, int64_t B, int64_t d, int64_t K,
+                         hipStream_t s) {
+  const int64_t fb = fin_blocks(K, d);
+  if (B * fb > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const bool fvec = d % kFinVec == 0 && ((uintptr_t)c % 16) == 0;
+  finalize_kernel<false><<<(unsigned)(B * fb), kThreads, 0, s>>>(
+      ws.sums, ws.offsets, c, ws.part, 0, ws.has_long, (int)d, (int)K, (int)fb, fvec);
   return hipGetLastError();
 }
 
