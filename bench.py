@@ -219,6 +219,9 @@ def main():
     ap.add_argument("--host-stream", type=int, default=0, metavar="CHUNK",
                     help="keep x in page-locked host memory and run fk_lloyd_host, streaming "
                          "CHUNK points per problem per copy (0 = the device-resident loop)")
+    ap.add_argument("--tol-run", type=int, default=1,
+                    help="1 = after the timed region, time the workload's own tol-stopped run "
+                         "(workloads whose recipe has tol > 0), 0 = skip")
     ap.add_argument("--baselines", type=int, default=1,
                     help="1 = after the timed region, time the materialised-distance assign and "
                          "the scatter-atomic update on the same inputs, 0 = skip")
@@ -307,6 +310,15 @@ def main():
                             "frac": u_bytes / (u_ms * 1e-3) / 1e9 / PEAK_HBM,
                             "traffic": u_traffic},
     }
+    if args.tol_run > 0 and getattr(w, "tol", 0.0) > 0:
+        # the recipe's own stop rule (up to 100 iterations): time to solution
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        _, _, n_tol = fk.fk_lloyd(x, init, 100, float(w.tol), ids=ids, centers=centers, ws=ws)
+        torch.cuda.synchronize()
+        t_tol = time.perf_counter() - t2
+        out["tol_run"] = {"tol": float(w.tol), "max_iter": 100, "n_iter": n_tol,
+                          "ms": 1e3 * t_tol, "ms_per_iter": 1e3 * t_tol / max(n_tol, 1)}
     out["gpu_baselines"] = (gpu_baselines(fk, torch, x, ids, centers, ws, w.dtype)
                             if args.baselines > 0 else None)
     out["cpu_baseline"] = cpu_baseline(w, args.workload) if args.cpu_batches > 0 else None

@@ -103,7 +103,7 @@ def _run(cmd, log, limit):
 def _bench_cmd(args):
     return ["python3", os.path.join(ROOT, "bench.py"), "--workload", args.workload,
             "--steps", str(args.steps), "--warmup", str(args.warmup), "--cpu-batches", "0",
-            "--baselines", "0", "--copy-calibration", str(COPY_MIB)]
+            "--baselines", "0", "--tol-run", "0", "--copy-calibration", str(COPY_MIB)]
 
 
 def _find(d, suffix):
@@ -216,7 +216,7 @@ def baselines_pass(args) -> int:
     os.makedirs(raw, exist_ok=True)
     os.makedirs(args.out, exist_ok=True)
     bcmd = ["python3", os.path.join(ROOT, "bench.py"), "--workload", wl, "--steps", "2",
-            "--warmup", "1", "--cpu-batches", "0", "--baselines", "1"]
+            "--warmup", "1", "--cpu-batches", "0", "--tol-run", "0", "--baselines", "1"]
     cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
            os.path.join(raw, "baselines"), "-o", "run", "--"] + bcmd
     log = os.path.join(raw, "baselines.log")
