@@ -224,15 +224,22 @@ def baselines_pass(args) -> int:
         rc = _run(cmd, log, args.limit)
         if rc != 0:
             return rc
-    top = ("python3 -m exact_means_clustering_flashassign_amd.profiling --baselines --workload "
-           + wl)
+    top = _top_line(args, "--baselines --workload " + wl)
     rows = read_stats(_find(os.path.join(raw, "baselines"), "_kernel_stats.csv"))
     txt = stats_text([top, "  which runs:", cmd], rows, _bench_json(log))
-    txt = txt.replace(ROOT + "/", "").replace(args.raw, "gpurun_out/rocprof")
+    txt = txt.replace(ROOT + "/", "")
     with open(os.path.join(args.out, f"kernels_baselines_{wl}.txt"), "w") as f:
         f.write(txt)
     print(txt, flush=True)
     return 0
+
+
+def _top_line(args, what):
+    """The command line that reproduces these passes, with the output folders
+    given relative to the repository root."""
+    rel = [os.path.relpath(os.path.abspath(p), ROOT) for p in (args.out, args.raw)]
+    return ("python3 -m exact_means_clustering_flashassign_amd.profiling " + what
+            + f" --out {rel[0]} --raw {rel[1]}")
 
 
 def main(argv=None):
@@ -240,9 +247,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="api_example")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profiles"),
+    ap.add_argument("--out", default=os.path.join(ROOT, "prof_out", "profiles"),
                     help="where the text summaries and traffic.json go")
-    ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "rocprof"),
+    ap.add_argument("--raw", default=os.path.join(ROOT, "prof_out", "rocprof"),
                     help="where rocprofv3 writes its raw output")
     ap.add_argument("--limit", type=int, default=240, help="seconds per pass")
     ap.add_argument("--summarize-only", action="store_true",
@@ -261,7 +268,7 @@ def main(argv=None):
     os.makedirs(raw, exist_ok=True)
     os.makedirs(args.out, exist_ok=True)
     bcmd = _bench_cmd(args)
-    top = "python3 -m exact_means_clustering_flashassign_amd.profiling --workload " + wl
+    top = _top_line(args, "--workload " + wl)
     passes = {
         "stats": ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
                   os.path.join(raw, "stats"), "-o", "run", "--"] + bcmd,
@@ -282,7 +289,7 @@ def main(argv=None):
         digests = json.load(f)
 
     def clean(t):
-        return t.replace(ROOT + "/", "").replace(args.raw, "gpurun_out/rocprof")
+        return t.replace(ROOT + "/", "")
 
     rows = read_stats(_find(os.path.join(raw, "stats"), "_kernel_stats.csv"))
     txt = stats_text([top, "  which runs:", passes["stats"]], rows,
