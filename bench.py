@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_F16 = 2500.0       # TFLOP/s, dense fp16/bf16
 PEAK_HBM = 8000.0            # GB/s
 PEAK_VALU_F32 = 157.3        # TFLOP/s
+PEAK_MFMA_F32 = 157.3        # TFLOP/s, dense fp32 MFMA
 METRIC = "Lloyd iter/s + assign/update ms at B32 N75600 K1000 d128 fp16; % MFMA/HBM peak"
 WORKLOADS = ("api_example", "io_breakdown", "large_k_zipf", "split_d", "tiny_f32")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -194,6 +195,77 @@ def host_stream(fk, torch, synthdata, w, args):
     print(json.dumps(out))
 
 
+def host_sweep(fk, torch, synthdata, args):
+    """The large-tensor sweep's shapes: one problem of fp32 points, d = 128,
+    N = 2^e and K = sqrt(N), the points i.i.d. standard normal in page-locked
+    host memory ("Flash-KMeans：IO感知的精确K-Means…", section on large-tensor
+    and out-of-core runs). For each size: the Lloyd loop with x streamed over
+    PCIe every iteration (fk_lloyd_host), and the device-resident loop on the
+    same inputs (fk_lloyd) with its assign and update times. One JSON line per
+    size."""
+    dev = torch.device("cuda:0")
+    for e in [int(v) for v in args.host_sweep.split(",")]:
+        if e % 2 or not 10 <= e <= 28:
+            raise SystemExit(f"--host-sweep: exponents are even, 10..28 (got {e})")
+        B, N, d, K = 1, 1 << e, 128, 1 << (e // 2)
+        x, init, _ = synthdata.make_mixture(B, N, d, K, "f32", n_comp=0, mean_std=0.0,
+                                            seed=3000 + e, iid=True)
+        xh = torch.from_numpy(x).pin_memory()
+        del x
+        init_d = torch.from_numpy(init).to(dev)
+        ids = torch.empty((B, N), dtype=torch.int32, device=dev)
+        centers = torch.empty((B, K, d), dtype=torch.float32, device=dev)
+        chunk = min(N, args.host_stream if args.host_stream > 0 else 1 << 20)
+        n = fk.fk_workspace_size_host(xh.dtype, B, chunk, d, K)
+        raw = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        off = (-raw.data_ptr()) % 256
+        hws = raw[off:off + n]
+        if args.warmup > 0:
+            fk.fk_lloyd_host(xh, init_d, args.warmup, 0.0, chunk, ids, centers, hws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, _, n_iter = fk.fk_lloyd_host(xh, init_d, args.steps, 0.0, chunk, ids, centers, hws)
+        torch.cuda.synchronize()
+        t_host = time.perf_counter() - t0
+        assert n_iter == args.steps
+        del raw, hws
+        xd = xh.to(dev)
+        ws = fk.workspace(xd.dtype, B, N, d, K, dev)
+        if args.warmup > 0:
+            fk.fk_lloyd(xd, init_d, args.warmup, 0.0, ids=ids, centers=centers, ws=ws)
+        torch.cuda.synchronize()
+        fk.fk_trace_begin(args.steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fk.fk_lloyd(xd, init_d, args.steps, 0.0, ids=ids, centers=centers, ws=ws)
+        torch.cuda.synchronize()
+        t_dev = time.perf_counter() - t0
+        tr = fk.fk_trace_end()
+        a_ms = tr["assign_ms"] / tr["iterations"]
+        u_ms = tr["update_ms"] / tr["iterations"]
+        gbps = B * N * d * 4 * args.steps / t_host / 1e9
+        achieved = assign_flop(B, N, d, K) / (a_ms * 1e-3) / 1e12
+        print(json.dumps({
+            "metric": METRIC, "value": args.steps / t_host, "unit": "iter/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * t_host / args.steps,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": f"large-tensor sweep: B=1 N=2^{e} d=128 K={K} f32 i.i.d. "
+                                   f"normal, x in page-locked host memory, {chunk} points per "
+                                   f"copy, {args.steps} Lloyd iterations, tol=0",
+                       "B": B, "N": N, "d": d, "K": K, "chunk": chunk},
+            "pcie": {"achieved": gbps, "peak": PEAK_PCIE, "unit": "GB/s",
+                     "frac": gbps / PEAK_PCIE},
+            "device_resident": {"iter_s": args.steps / t_dev, "assign_ms": a_ms,
+                                "update_ms": u_ms,
+                                "assign_roofline": {"bound": "mfma", "achieved": achieved,
+                                                    "peak": PEAK_MFMA_F32, "unit": "TFLOP/s",
+                                                    "frac": achieved / PEAK_MFMA_F32}},
+        }), flush=True)
+        del xh, xd, ws, ids, centers, init_d
+        torch.cuda.empty_cache()
+
+
 def copy_calibration(mib: int, dev):
     """A plain elementwise kernel over a buffer of known size, for scaling
     the HBM byte counters (reads and writes mib MiB each)."""
@@ -219,6 +291,10 @@ def main():
     ap.add_argument("--host-stream", type=int, default=0, metavar="CHUNK",
                     help="keep x in page-locked host memory and run fk_lloyd_host, streaming "
                          "CHUNK points per problem per copy (0 = the device-resident loop)")
+    ap.add_argument("--host-sweep", default="", metavar="E,E,...",
+                    help="instead: the large-tensor sweep (fp32, d=128, N=2^E, K=2^(E/2)), "
+                         "host-streamed and device-resident, one line per size; CHUNK from "
+                         "--host-stream (default 2^20)")
     ap.add_argument("--tol-run", type=int, default=1,
                     help="1 = after the timed region, time the workload's own tol-stopped run "
                          "(workloads whose recipe has tol > 0), 0 = skip")
@@ -240,6 +316,9 @@ def main():
         sys.exit(1)
     fk.load()
     dev = torch.device("cuda:0")
+    if args.host_sweep:
+        host_sweep(fk, torch, synthdata, args)
+        return
     w = synthdata.make_workload(args.workload)
     if args.host_stream > 0:
         host_stream(fk, torch, synthdata, w, args)
@@ -272,8 +351,9 @@ def main():
     flop = assign_flop(B, N, d, K)
     a_bytes = assign_bytes(B, N, d, K, s)
     u_bytes = update_bytes(B, N, d, K, s)
-    if w.dtype == "f32":
-        bound, peak, unit = "alu", PEAK_VALU_F32, "TFLOP/s"
+    if w.dtype == "f32":     # fp32 MFMA for d <= 256, the VALU kernel above
+        bound, peak, unit = ("mfma", PEAK_MFMA_F32, "TFLOP/s") if d <= 256 else \
+            ("alu", PEAK_VALU_F32, "TFLOP/s")
         achieved = flop / (a_ms * 1e-3) / 1e12
     elif flop / a_bytes > PEAK_MFMA_F16 * 1e12 / (PEAK_HBM * 1e9):
         bound, peak, unit = "mfma", PEAK_MFMA_F16, "TFLOP/s"

@@ -21,9 +21,13 @@
 // The running max works on scores whose 4 low mantissa bits carry the row
 // slot, so one v_max3 tree gives the maximum and where it is.
 //
+// fp32 inputs with d <= 256 run the same kernel on rows of 2d 16-bit units:
+// every load and LDS copy moves bytes, so only the MFMA differs (four
+// v_mfma_f32_32x32x2_f32 per 16-byte k-step, Mfma<FK_F32>).
+//
 // The split-D path (d > 512) lives in assign_splitd.hip.
 //
-// fp32 inputs use a VALU kernel (exact fp32 products, fp32 fma chain).
+// fp32 inputs with d > 256 use a VALU kernel (fp32 products, fp32 fma chain).
 #include <math.h>
 
 #include "fk_internal.hpp"
@@ -526,8 +530,11 @@ hipError_t smalld_dt(const void* x, const void* c, const float* cn, int64_t B, i
 
 }  // namespace
 
-// The small-D tiles fit LDS for every d <= 512 (largest: 2 x 32 x 520 x 2 B).
-bool smalld_supported(int dt, int64_t d) { return (dt == FK_F16 || dt == FK_BF16) && d <= 512; }
+// The small-D tiles fit LDS for every d <= 512 16-bit units (largest:
+// 2 x 32 x 520 x 2 B); an fp32 row of d elements is 2d units.
+bool smalld_supported(int dt, int64_t d) {
+  return ((dt == FK_F16 || dt == FK_BF16) && d <= 512) || (dt == FK_F32 && d <= 256);
+}
 
 hipError_t launch_assign_smalld(const void* x, const void* c_lp, const float* cnorm, int dt,
                                 int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,
@@ -536,6 +543,8 @@ hipError_t launch_assign_smalld(const void* x, const void* c_lp, const float* cn
   if (K < 1) return hipErrorInvalidValue;    // the point-block loop needs a tile
   if (dt == FK_F16) return smalld_dt<FK_F16>(x, c_lp, cnorm, B, N, d, K, ids, s);
   if (dt == FK_BF16) return smalld_dt<FK_BF16>(x, c_lp, cnorm, B, N, d, K, ids, s);
+  if (dt == FK_F32 && d <= 256)     // rows of 2d 16-bit units
+    return smalld_dt<FK_F32>(x, c_lp, cnorm, B, N, 2 * d, K, ids, s);
   return hipErrorNotSupported;
 }
 

@@ -66,6 +66,22 @@ template <> struct Mfma<FK_BF16> {
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
 };
+// fp32: the 16 bytes a lane holds per k-step are 4 floats, k-elements
+// half*4 .. half*4+3 of an 8-wide k-step; four v_mfma_f32_32x32x2_f32 take
+// element j of every lane in turn (half 0 and half 1 give the two k of one
+// MFMA), so A and B, loaded with the same byte layout, pair up k for k.
+template <> struct Mfma<FK_F32> {
+  __device__ static __forceinline__ floatx16_t run(uint4 a, uint4 b, floatx16_t c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.x),
+                                             __builtin_bit_cast(float, b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.y),
+                                             __builtin_bit_cast(float, b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.z),
+                                             __builtin_bit_cast(float, b.z), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.w),
+                                                __builtin_bit_cast(float, b.w), c, 0, 0, 0);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // MFMA tile helpers (v_mfma_f32_32x32x16: lane = point column r32 + 32*half,

@@ -108,6 +108,11 @@ ASSIGN_CASES = [
     ("f32", 1, 2048, 32, 16, False),
     ("f32", 2, 999, 3, 50, False),
     ("f32", 1, 500, 100, 70, False),
+    ("f32", 2, 3000, 128, 300, False),      # fp32 MFMA, several tiles and point blocks
+    ("f32", 1, 2000, 64, 200, False),       # fp32 MFMA, 8-wave blocks with prefetch
+    ("f32", 1, 1000, 256, 100, False),      # fp32 MFMA at its widest rows
+    ("f32", 1, 500, 100, 70, True),         # fp32 VALU kernel (forced)
+    ("f32", 1, 400, 300, 50, False),        # fp32 VALU kernel (d > 256)
     ("f16", 1, 5, 16, 1, False),            # K = 1
     ("f16", 1, 10, 16, 40, False),          # K > N
     ("bf16", 3, 33, 64, 7, False),          # N below one tile
@@ -301,6 +306,18 @@ def test_full_size_assign_sampled(fk, name, per_batch):
     else:
         st = _sampled_assign_check(x64, c_hat, ids, rng, per_batch)
     print(name, st)
+
+
+def test_full_size_assign_f32_sweep_shape(fk):
+    """One size of the fp32 large-tensor sweep (N = 2^20, K = 1024, d = 128,
+    i.i.d. normal points), assigned on the GPU whole, checked on sampled rows."""
+    N, K, d = 1 << 20, 1024, 128
+    x, init, _ = synthdata.make_mixture(1, N, d, K, "f32", n_comp=0, mean_std=0.0, seed=3020,
+                                        iid=True)
+    _, _, ids = gpu_norms_assign(fk, to_dev(x, "f32"), init.astype(np.float64), "f32")
+    st = _sampled_assign_check(x.astype(np.float64), init.astype(np.float64), ids,
+                               np.random.default_rng(9), 1024)
+    print(st)
 
 
 @pytest.mark.parametrize("name,kind", [("api_example", "uniform"), ("split_d", "uniform")])
