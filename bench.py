@@ -208,10 +208,17 @@ def host_sweep(fk, torch, synthdata, args):
         if e % 2 or not 10 <= e <= 28:
             raise SystemExit(f"--host-sweep: exponents are even, 10..28 (got {e})")
         B, N, d, K = 1, 1 << e, 128, 1 << (e // 2)
-        x, init, _ = synthdata.make_mixture(B, N, d, K, "f32", n_comp=0, mean_std=0.0,
-                                            seed=3000 + e, iid=True)
-        xh = torch.from_numpy(x).pin_memory()
-        del x
+        # drawn straight into page-locked memory, or into ordinary memory
+        # where the driver cannot lock that much (2^28 points are 137 GB)
+        try:
+            xh = torch.empty((B, N, d), dtype=torch.float32, pin_memory=True)
+            host_mem = "page-locked"
+        except RuntimeError:
+            xh = torch.empty((B, N, d), dtype=torch.float32)
+            host_mem = "pageable"
+        _, init, _ = synthdata.make_mixture(B, N, d, K, "f32", n_comp=0, mean_std=0.0,
+                                            seed=3000 + e, iid=True, out=xh.numpy())
+        print(f"# N=2^{e}: points ready", file=sys.stderr, flush=True)
         init_d = torch.from_numpy(init).to(dev)
         ids = torch.empty((B, N), dtype=torch.int32, device=dev)
         centers = torch.empty((B, K, d), dtype=torch.float32, device=dev)
@@ -228,6 +235,7 @@ def host_sweep(fk, torch, synthdata, args):
         torch.cuda.synchronize()
         t_host = time.perf_counter() - t0
         assert n_iter == args.steps
+        print(f"# N=2^{e}: host-streamed loop done", file=sys.stderr, flush=True)
         del raw, hws
         xd = xh.to(dev)
         ws = fk.workspace(xd.dtype, B, N, d, K, dev)
@@ -251,9 +259,9 @@ def host_sweep(fk, torch, synthdata, args):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic",
             "config": {"workload": f"large-tensor sweep: B=1 N=2^{e} d=128 K={K} f32 i.i.d. "
-                                   f"normal, x in page-locked host memory, {chunk} points per "
+                                   f"normal, x in {host_mem} host memory, {chunk} points per "
                                    f"copy, {args.steps} Lloyd iterations, tol=0",
-                       "B": B, "N": N, "d": d, "K": K, "chunk": chunk},
+                       "B": B, "N": N, "d": d, "K": K, "chunk": chunk, "host_memory": host_mem},
             "pcie": {"achieved": gbps, "peak": PEAK_PCIE, "unit": "GB/s",
                      "frac": gbps / PEAK_PCIE},
             "device_resident": {"iter_s": args.steps / t_dev, "assign_ms": a_ms,

@@ -122,14 +122,16 @@ def _workers() -> int:
 
 
 def make_mixture(B, N, d, K, dtype, *, n_comp, mean_std, weights=None,
-                 seed, subspace_rank=None, iid=False, chunk_rows=1 << 16):
+                 seed, subspace_rank=None, iid=False, chunk_rows=1 << 16, out=None):
     """Gaussian-mixture points plus per-batch random-point initial centroids.
 
     One PCG64 stream seeded with ``seed`` draws, in order: the component means
     (all batches), the labels, then the init indices. The unit-variance noise
     of row chunk j (chunks of ``chunk_rows`` rows, batch-major) comes from its
     own stream, child j of ``SeedSequence(seed)``, so chunks can be drawn in
-    parallel and the result does not depend on the thread count.
+    parallel and the result does not depend on the thread count. ``out``, if
+    given, is a (B, N, d) array of the storage type that receives the points
+    (page-locked memory, say); the values do not depend on it.
     """
     import concurrent.futures as cf
 
@@ -159,7 +161,12 @@ def make_mixture(B, N, d, K, dtype, *, n_comp, mean_std, weights=None,
     init_idx = [rng.choice(N, size=K, replace=False) if K <= N else None for _ in range(B)]
 
     sdt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
-    x = np.empty((B, N, d), dtype=sdt)
+    if out is None:
+        x = np.empty((B, N, d), dtype=sdt)
+    else:
+        if out.shape != (B, N, d) or out.dtype != sdt:
+            raise ValueError("out: wrong shape or dtype")
+        x = out
     per_b = (N + chunk_rows - 1) // chunk_rows
     children = ss.spawn(B * per_b)
 
