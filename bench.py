@@ -198,8 +198,9 @@ def host_stream(fk, torch, synthdata, w, args):
 def host_sweep(fk, torch, synthdata, args):
     """The large-tensor sweep's shapes: one problem of fp32 points, d = 128,
     N = 2^e and K = sqrt(N), the points i.i.d. standard normal in page-locked
-    host memory ("Flash-KMeans：IO感知的精确K-Means…", section on large-tensor
-    and out-of-core runs). For each size: the Lloyd loop with x streamed over
+    host memory ("flash-kmeans and the return of exact K-Means on the GPU",
+    section "The benchmark compares against four other implementations, on one
+    GPU", the large-tensor paragraph). For each size: the Lloyd loop with x streamed over
     PCIe every iteration (fk_lloyd_host), and the device-resident loop on the
     same inputs (fk_lloyd) with its assign and update times. One JSON line per
     size."""
