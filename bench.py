@@ -25,7 +25,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_F16 = 2500.0       # TFLOP/s, dense fp16/bf16
 PEAK_HBM = 8000.0            # GB/s
-PEAK_VALU_F32 = 157.3        # TFLOP/s
 PEAK_MFMA_F32 = 157.3        # TFLOP/s, dense fp32 MFMA
 METRIC = "Lloyd iter/s + assign/update ms at B32 N75600 K1000 d128 fp16; % MFMA/HBM peak"
 WORKLOADS = ("api_example", "io_breakdown", "large_k_zipf", "split_d", "tiny_f32")
@@ -360,9 +359,8 @@ def main():
     flop = assign_flop(B, N, d, K)
     a_bytes = assign_bytes(B, N, d, K, s)
     u_bytes = update_bytes(B, N, d, K, s)
-    if w.dtype == "f32":     # fp32 MFMA for d <= 256, the VALU kernel above
-        bound, peak, unit = ("mfma", PEAK_MFMA_F32, "TFLOP/s") if d <= 256 else \
-            ("alu", PEAK_VALU_F32, "TFLOP/s")
+    if w.dtype == "f32":     # fp32 MFMA; compute-bound unless K is tiny
+        bound, peak, unit = "mfma", PEAK_MFMA_F32, "TFLOP/s"
         achieved = flop / (a_ms * 1e-3) / 1e12
     elif flop / a_bytes > PEAK_MFMA_F16 * 1e12 / (PEAK_HBM * 1e9):
         bound, peak, unit = "mfma", PEAK_MFMA_F16, "TFLOP/s"

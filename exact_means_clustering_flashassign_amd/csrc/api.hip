@@ -46,8 +46,6 @@ hipError_t run_assign(const void* x, const void* c_lp, const float* cn, int dt, 
                       int64_t N, int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
   if (!force_splitd() && fk::smalld_supported(dt, d))
     return fk::launch_assign_smalld(x, c_lp, cn, dt, B, N, d, K, ids, s);
-  if (dt == FK_F32)
-    return fk::launch_assign_f32((const float*)x, (const float*)c_lp, cn, B, N, d, K, ids, s);
   return fk::launch_assign_splitd(x, c_lp, cn, dt, B, N, d, K, ids, s);
 }
 

@@ -25,9 +25,8 @@
 // every load and LDS copy moves bytes, so only the MFMA differs (four
 // v_mfma_f32_32x32x2_f32 per 16-byte k-step, Mfma<FK_F32>).
 //
-// The split-D path (d > 512) lives in assign_splitd.hip.
-//
-// fp32 inputs with d > 256 use a VALU kernel (fp32 products, fp32 fma chain).
+// The split-D path (d > 512 units: fp16/bf16 d > 512, fp32 d > 256) lives in
+// assign_splitd.hip.
 #include <math.h>
 
 #include "fk_internal.hpp"
@@ -35,7 +34,6 @@
 namespace fk {
 namespace {
 
-constexpr int kThreads = 256;   // fp32 kernel block
 
 // Word 3 of a raw (unformatted, stride 0) buffer resource.
 constexpr int kRawBufferWord3 = 0x00020000;
@@ -404,60 +402,6 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
 }
 
 // ===========================================================================
-// fp32 (VALU)
-// ===========================================================================
-constexpr int kF32TK = 32;   // centroids per tile
-constexpr int kF32DC = 32;   // dims per chunk
-
-__global__ __launch_bounds__(kThreads) void assign_f32_kernel(
-    const float* __restrict__ x, const float* __restrict__ c, const float* __restrict__ cnorm,
-    int32_t* __restrict__ ids, int N, int d, int K, int blocks_per_batch, int grid) {
-  __shared__ float lds_c[kF32TK][kF32DC + 1];
-  __shared__ float lds_h[kF32TK];
-  const int tid = threadIdx.x;
-  const int64_t logical = xcd_remap(blockIdx.x, grid);
-  const int b = (int)(logical / blocks_per_batch);
-  const int n = (int)(logical % blocks_per_batch) * kThreads + tid;
-  const bool valid = n < N;
-  const float* xr = x + ((int64_t)b * N + (valid ? n : 0)) * d;
-  const float* cb = c + (int64_t)b * K * d;
-  const float* cnb = cnorm + (int64_t)b * K;
-
-  float best = -INFINITY;
-  int bidx = 0;
-  for (int k0 = 0; k0 < K; k0 += kF32TK) {
-    __syncthreads();
-    if (tid < kF32TK) lds_h[tid] = (k0 + tid < K) ? -0.5f * cnb[k0 + tid] : -INFINITY;
-    float acc[kF32TK];
-#pragma unroll
-    for (int k = 0; k < kF32TK; ++k) acc[k] = 0.f;
-    for (int j0 = 0; j0 < d; j0 += kF32DC) {
-      __syncthreads();
-      for (int e = tid; e < kF32TK * kF32DC; e += kThreads) {
-        const int k = e / kF32DC, j = e % kF32DC;
-        lds_c[k][j] = (k0 + k < K && j0 + j < d) ? cb[(int64_t)(k0 + k) * d + j0 + j] : 0.f;
-      }
-      __syncthreads();
-      const int jn = (d - j0) < kF32DC ? (d - j0) : kF32DC;
-      for (int j = 0; j < jn; ++j) {
-        const float xv = valid ? xr[j0 + j] : 0.f;
-#pragma unroll
-        for (int k = 0; k < kF32TK; ++k) acc[k] = fmaf(xv, lds_c[k][j], acc[k]);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kF32TK; ++k) {
-      const float v = acc[k] + lds_h[k];
-      if (v > best) {
-        best = v;
-        bidx = k0 + k;
-      }
-    }
-  }
-  if (valid) ids[(int64_t)b * N + n] = bidx;
-}
-
-// ===========================================================================
 // dispatch
 // ===========================================================================
 // 16-byte vector loads need rows of whole 8-element vectors and aligned bases.
@@ -546,17 +490,6 @@ hipError_t launch_assign_smalld(const void* x, const void* c_lp, const float* cn
   if (dt == FK_F32 && d <= 256)     // rows of 2d 16-bit units
     return smalld_dt<FK_F32>(x, c_lp, cnorm, B, N, 2 * d, K, ids, s);
   return hipErrorNotSupported;
-}
-
-hipError_t launch_assign_f32(const float* x, const float* c, const float* cnorm, int64_t B,
-                             int64_t N, int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
-  if (B == 0 || N == 0) return hipSuccess;
-  const int bpb = (int)((N + kThreads - 1) / kThreads);
-  const int64_t grid = B * bpb;
-  if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  assign_f32_kernel<<<(unsigned)grid, kThreads, 0, s>>>(x, c, cnorm, ids, (int)N, (int)d,
-                                                         (int)K, bpb, (int)grid);
-  return hipGetLastError();
 }
 
 }  // namespace fk

@@ -1,4 +1,5 @@
-// FlashAssign for large d (d > 512) on gfx950: outer K loop, inner D loop.
+// FlashAssign for large d (d > 512; fp32 d > 256) on gfx950: outer K loop,
+// inner D loop.
 //
 // Same contraction and argmax as the small-D path (score_k = x.c_k -
 // ||c_k||^2 / 2, lowest k on ties; the distance matrix is never written), but
@@ -322,6 +323,9 @@ hipError_t launch_assign_splitd(const void* x, const void* c_lp, const float* cn
   if (K < 1) return hipErrorInvalidValue;    // the point-block loop needs a tile
   if (dt == FK_F16) return splitd_dt<FK_F16>(x, c_lp, cnorm, B, N, d, K, ids, s);
   if (dt == FK_BF16) return splitd_dt<FK_BF16>(x, c_lp, cnorm, B, N, d, K, ids, s);
+  // fp32: rows of 2d 16-bit units (every load and LDS copy moves bytes), four
+  // v_mfma_f32_32x32x2_f32 per 16-byte k-step
+  if (dt == FK_F32) return splitd_dt<FK_F32>(x, c_lp, cnorm, B, N, 2 * d, K, ids, s);
   return hipErrorNotSupported;
 }
 

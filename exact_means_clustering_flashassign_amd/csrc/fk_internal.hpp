@@ -212,8 +212,6 @@ hipError_t launch_assign_smalld(const void* x, const void* c_lp, const float* cn
 hipError_t launch_assign_splitd(const void* x, const void* c_lp, const float* cnorm, int dt,
                                 int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,
                                 hipStream_t s);
-hipError_t launch_assign_f32(const float* x, const float* c, const float* cnorm, int64_t B,
-                             int64_t N, int64_t d, int64_t K, int32_t* ids, hipStream_t s);
 
 // Sort-inverse update; workspace carved by the API layer.
 struct UpdateWs {

@@ -94,14 +94,17 @@ fk_status_t fk_norms(const float* c, void* c_lp, float* cnorm, fk_dtype_t dt,
 /*
  * FlashAssign: ids[b,n] = argmin_k ( cnorm[b,k] - 2 x[b,n].c_lp[b,k] ),
  * i.e. the nearest centroid to x[b,n] among c_lp[b,:], lowest index on ties.
- * Products are exact and accumulated in fp32 (MFMA for fp16/bf16). The
- * fp16/bf16 path for d <= 512 carries each score's row in its 4 low mantissa
- * bits, so two centroids whose scores agree to 2^-19 of their size (within
- * the rounding of the fp32 sum itself) may resolve to either of the two.
+ * Every type runs on the matrix cores with fp32 accumulation: fp16/bf16
+ * products are exact, fp32 products are rounded to fp32. The small-D path
+ * (fp16/bf16 d <= 512, fp32 d <= 256) carries each score's row in its 4 low
+ * mantissa bits, so two centroids whose scores agree to 2^-19 of their size
+ * (within the rounding of the fp32 sum itself) may resolve to either of the
+ * two.
  * [hysenlabs] "The point of the kernel is that the distance matrix never
  * exists": points processed in tiles, centroids streamed in chunks, the
  * partial dot products kept in registers across the d loop; small-D path
- * for d <= 512 and split-D path otherwise, chosen automatically.
+ * for rows of at most 1 KB (d <= 512 fp16/bf16, d <= 256 fp32) and split-D
+ * path otherwise, chosen automatically.
  * [itinai] second paragraph, [iaemfoco] "FlashAssign", [arxiv] Abstract.
  *   x (B,N,d) dt, c_lp (B,K,d) dt, cnorm (B,K) fp32 in; ids (B,N) int32 out.
  */

@@ -111,8 +111,9 @@ ASSIGN_CASES = [
     ("f32", 2, 3000, 128, 300, False),      # fp32 MFMA, several tiles and point blocks
     ("f32", 1, 2000, 64, 200, False),       # fp32 MFMA, 8-wave blocks with prefetch
     ("f32", 1, 1000, 256, 100, False),      # fp32 MFMA at its widest rows
-    ("f32", 1, 500, 100, 70, True),         # fp32 VALU kernel (forced)
-    ("f32", 1, 400, 300, 50, False),        # fp32 VALU kernel (d > 256)
+    ("f32", 1, 500, 100, 70, True),         # fp32 split-D (forced at small d)
+    ("f32", 1, 400, 300, 50, False),        # fp32 split-D (d > 256)
+    ("f32", 2, 1000, 600, 300, False),      # fp32 split-D, two 256-row K tiles
     ("f16", 1, 5, 16, 1, False),            # K = 1
     ("f16", 1, 10, 16, 40, False),          # K > N
     ("bf16", 3, 33, 64, 7, False),          # N below one tile
