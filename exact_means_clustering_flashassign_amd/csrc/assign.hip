@@ -363,7 +363,12 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
     const int ft = last ? 0 : t + 1;
     fetch(last ? npb : pb, ft);
     if (XP > 0 && last) prefetch_x(npb, nrow0);
+    // the MFMA phase at raised wave priority: where the two waves of a SIMD
+    // are out of step, the one still in its tile issues ahead of the one
+    // staging and about to wait at the barrier
+    __builtin_amdgcn_s_setprio(1);
     if (act) tile(buf, t);
+    __builtin_amdgcn_s_setprio(0);
     stash(ft, buf ^ 1);
     if (last) {
       // the next point block's fragments first (the rest of its k-steps

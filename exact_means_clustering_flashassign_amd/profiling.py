@@ -258,6 +258,8 @@ def main(argv=None):
                     help="instead: one kernel-statistics pass of a short run that also times "
                          "the contrast baselines (kernels_baselines_<workload>.txt)")
     args = ap.parse_args(argv)
+    # the passes run from /tmp: output folders are fixed against the caller's cwd
+    args.out, args.raw = os.path.abspath(args.out), os.path.abspath(args.raw)
     if args.baselines:
         return baselines_pass(args)
     sys.path.insert(0, ROOT)
