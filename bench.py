@@ -222,7 +222,9 @@ def host_sweep(fk, torch, synthdata, args):
         init_d = torch.from_numpy(init).to(dev)
         ids = torch.empty((B, N), dtype=torch.int32, device=dev)
         centers = torch.empty((B, K, d), dtype=torch.float32, device=dev)
-        chunk = min(N, args.host_stream if args.host_stream > 0 else 1 << 20)
+        # at least four chunks, so copies overlap the kernels at every size
+        chunk = args.host_stream if args.host_stream > 0 else min(1 << 20, max(N // 4, 1))
+        chunk = min(N, chunk)
         n = fk.fk_workspace_size_host(xh.dtype, B, chunk, d, K)
         raw = torch.empty(n + 256, dtype=torch.uint8, device=dev)
         off = (-raw.data_ptr()) % 256
@@ -302,7 +304,7 @@ def main():
     ap.add_argument("--host-sweep", default="", metavar="E,E,...",
                     help="instead: the large-tensor sweep (fp32, d=128, N=2^E, K=2^(E/2)), "
                          "host-streamed and device-resident, one line per size; CHUNK from "
-                         "--host-stream (default 2^20)")
+                         "--host-stream (default min(2^20, N/4))")
     ap.add_argument("--tol-run", type=int, default=1,
                     help="1 = after the timed region, time the workload's own tol-stopped run "
                          "(workloads whose recipe has tol > 0), 0 = skip")
