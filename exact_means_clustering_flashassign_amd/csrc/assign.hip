@@ -117,7 +117,7 @@ __device__ __forceinline__ int argmax_row(const Argmax& st, int half) {
 // argmax drains, so consecutive point blocks run back to back.
 // FULL: d == 16*KS, so every column of a row is real and loads need no
 // column guard; otherwise columns >= d read as zero.
-template <int DT, int KS, int NF, int TK, int WAVES, bool VEC, bool FULL>
+template <int DT, int KS, int NF, int TK, int WAVES, bool VEC, bool FULL, bool RING>
 __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ c,
     const float* __restrict__ cnorm, int32_t* __restrict__ ids, int N, int d, int K,
@@ -134,8 +134,11 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   // k-steps of the next point block prefetched into registers during a
   // point block's last tile (8-wave blocks with whole rows only)
   constexpr int XP = (FULL && WAVES == 8) ? KS / 2 : 0;
-  __shared__ __align__(16) uint16_t lds_c[2][TK * PITCH];
-  __shared__ __align__(16) float lds_h[2][NT];
+  // RING: four tile buffers staged two tiles ahead, one barrier per two
+  // tiles (needs at least two tiles per point block); else double buffering
+  constexpr int NBUF = RING ? 4 : 2;
+  __shared__ __align__(16) uint16_t lds_c[NBUF][TK * PITCH];
+  __shared__ __align__(16) float lds_h[NBUF][NT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -353,15 +356,23 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   load_block(pb, row0);
   fetch(pb, 0);
   stash(0, 0);
+  if constexpr (RING) {
+    fetch(pb, 1);
+    stash(1, 1);
+  }
   reset();
   __syncthreads();
   int buf = 0, t = 0;
+  uint32_t it = 0;   // tiles done by the block
   for (;;) {
-    // one centroid tile; the tile staged meanwhile is the next one of this
-    // point block or, during the last, tile 0 of the next point block
+    // one centroid tile; the tile staged meanwhile is the next one (RING:
+    // the one after next) in the stream of this point block's tiles followed
+    // by the next point block's
     const bool last = t == ntiles - 1;
-    const int ft = last ? 0 : t + 1;
-    fetch(last ? npb : pb, ft);
+    const int ahead = t + (RING ? 2 : 1);
+    const bool in_next = ahead >= ntiles;
+    const int ft = in_next ? ahead - ntiles : ahead;
+    fetch(in_next ? npb : pb, ft);
     if (XP > 0 && last) prefetch_x(npb, nrow0);
     // the MFMA phase at raised wave priority: where the two waves of a SIMD
     // are out of step, the one still in its tile issues ahead of the one
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
     __builtin_amdgcn_s_setprio(1);
     if (act) tile(buf, t);
     __builtin_amdgcn_s_setprio(0);
-    stash(ft, buf ^ 1);
+    stash(ft, RING ? (buf + 2) & 3 : buf ^ 1);
     if (last) {
       // the next point block's fragments first (the rest of its k-steps
       // load while this one's final subtile drains), then this one's ids
@@ -389,8 +400,12 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
       }
       reset();
     }
-    __syncthreads();
-    buf ^= 1;
+    // RING: a buffer is restaged two tiles after it was read, and the
+    // barrier after every odd tile separates each such read from the write
+    // and each write from its read
+    if (!RING || (it & 1)) __syncthreads();
+    ++it;
+    buf = RING ? (buf + 1) & 3 : buf ^ 1;
     if (!last) {
       ++t;
       continue;
@@ -431,11 +446,11 @@ int resident_blocks(Kern kern, int threads, int (&cache)[64]) {
   return cache[dev];
 }
 
-template <int DT, int KS, int NF, int TK, int WAVES, bool VEC, bool FULL>
+template <int DT, int KS, int NF, int TK, int WAVES, bool VEC, bool FULL, bool RING>
 hipError_t launch_smalld(const uint16_t* x, const uint16_t* c, const float* cn, int64_t total,
                          int bpb, int64_t N, int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
   static int cache[64];
-  auto kern = assign_smalld_kernel<DT, KS, NF, TK, WAVES, VEC, FULL>;
+  auto kern = assign_smalld_kernel<DT, KS, NF, TK, WAVES, VEC, FULL, RING>;
   const int resident = resident_blocks(kern, WAVES * 64, cache);
   if (resident <= 0) return hipErrorInvalidConfiguration;
   // a multiple of 8 so each block's point blocks stay on its XCD
@@ -455,11 +470,16 @@ hipError_t run_smalld(const void* x, const void* c, const float* cn, int64_t B, 
   if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const uint16_t* xp = (const uint16_t*)x;
   const uint16_t* cp = (const uint16_t*)c;
+  if constexpr (TK == 128 && WAVES == 8) {   // the ring needs two tiles per point block
+    if (vec_ok(x, c, d) && d == 16 * KS && K > TK)
+      return launch_smalld<DT, KS, NF, TK, WAVES, true, true, true>(xp, cp, cn, total, bpb, N, d, K,
+                                                                     ids, s);
+  }
   if (vec_ok(x, c, d) && d == 16 * KS)
-    return launch_smalld<DT, KS, NF, TK, WAVES, true, true>(xp, cp, cn, total, bpb, N, d, K, ids, s);
+    return launch_smalld<DT, KS, NF, TK, WAVES, true, true, false>(xp, cp, cn, total, bpb, N, d, K, ids, s);
   if (vec_ok(x, c, d))
-    return launch_smalld<DT, KS, NF, TK, WAVES, true, false>(xp, cp, cn, total, bpb, N, d, K, ids, s);
-  return launch_smalld<DT, KS, NF, TK, WAVES, false, false>(xp, cp, cn, total, bpb, N, d, K, ids, s);
+    return launch_smalld<DT, KS, NF, TK, WAVES, true, false, false>(xp, cp, cn, total, bpb, N, d, K, ids, s);
+  return launch_smalld<DT, KS, NF, TK, WAVES, false, false, false>(xp, cp, cn, total, bpb, N, d, K, ids, s);
 }
 
 // Shapes per d: k-steps KS (16 elements each), point fragments NF per wave,
