@@ -276,6 +276,50 @@ def host_sweep(fk, torch, synthdata, args):
         torch.cuda.empty_cache()
 
 
+def mfma_peak(fk, torch, args):
+    """The MFMA peak probe: v_mfma_f32_32x32x16_f16 back to back on every SIMD
+    (two waves per SIMD, random operands), the instruction and occupancy of
+    the small-D assign. Reports the achieved TFLOP/s against the nominal dense
+    fp16 peak and the shader clock the loop ran at (from the in-kernel clock
+    counters). One JSON line."""
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * cus                      # 2 blocks of 4 waves per CU: 2 waves per SIMD
+    iters = args.peak_iters
+    fk.load_baseline()
+    out, stamps = fk.fkb_mfma_peak(blocks, iters, 12345, device=dev)   # warm-up
+    torch.cuda.synchronize()
+    reps = max(args.steps, 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        fk.fkb_mfma_peak(blocks, iters, 1000 + r, out=out, stamps=stamps)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flop = blocks * 4.0 * iters * 32 * 32768
+    tflops = flop / (ms * 1e-3) / 1e12
+    st = stamps.cpu().numpy().astype("float64")
+    khz = fk.fkb_wall_clock_khz()
+    ticks = st[:, 1] - st[:, 0]
+    real = st[:, 3] - st[:, 2]
+    clock_mhz = float((ticks / real).mean() * khz / 1e3) if khz > 0 and (real > 0).all() else None
+    print(json.dumps({
+        "metric": "MFMA peak probe (v_mfma_f32_32x32x16_f16, random operands)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"mfma peak probe: {blocks} blocks x 4 waves, {iters} x 32 MFMAs "
+                               "per wave, 8 accumulator chains", "blocks": blocks,
+                   "iters": iters, "cus": cus},
+        "frac_of_nominal": tflops / PEAK_MFMA_F16,
+        "shader_clock_mhz": clock_mhz,
+        "wall_clock_khz": khz,
+        "frac_of_peak_at_measured_clock": (tflops / (PEAK_MFMA_F16 * clock_mhz / 2400.0)
+                                           if clock_mhz else None),
+    }), flush=True)
+
+
 def copy_calibration(mib: int, dev):
     """A plain elementwise kernel over a buffer of known size, for scaling
     the HBM byte counters (reads and writes mib MiB each)."""
@@ -311,6 +355,10 @@ def main():
     ap.add_argument("--baselines", type=int, default=1,
                     help="1 = after the timed region, time the materialised-distance assign and "
                          "the scatter-atomic update on the same inputs, 0 = skip")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="instead: the MFMA peak probe (--steps timed launches)")
+    ap.add_argument("--peak-iters", type=int, default=20000,
+                    help="loop iterations (32 MFMAs each) per wave of the MFMA peak probe")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -326,6 +374,9 @@ def main():
         sys.exit(1)
     fk.load()
     dev = torch.device("cuda:0")
+    if args.mfma_peak:
+        mfma_peak(fk, torch, args)
+        return
     if args.host_sweep:
         host_sweep(fk, torch, synthdata, args)
         return

@@ -23,7 +23,9 @@ from ._binding import (  # noqa: F401
     fk_workspace_size,
     fk_workspace_size_host,
     fkb_assign_materialized,
+    fkb_mfma_peak,
     fkb_update_atomic,
+    fkb_wall_clock_khz,
     load,
     load_baseline,
     torch_dtype,

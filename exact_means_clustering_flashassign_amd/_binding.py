@@ -283,6 +283,10 @@ def load_baseline(path: Optional[str] = None):
     lib.fkb_assign_materialized.argtypes = [P, P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P]
     lib.fkb_update_atomic.restype = ctypes.c_int
     lib.fkb_update_atomic.argtypes = [P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, P]
+    lib.fkb_mfma_peak.restype = ctypes.c_int
+    lib.fkb_mfma_peak.argtypes = [I64, ctypes.c_int32, ctypes.c_uint32, P, P, P]
+    lib.fkb_wall_clock_khz.restype = ctypes.c_int32
+    lib.fkb_wall_clock_khz.argtypes = []
     _blib = lib
     return lib
 
@@ -322,3 +326,24 @@ def fkb_update_atomic(x, ids, c, counts=None, sums=None):
         _dev(sums, "sums", torch.float32, (B, K, d)), _stream(x))
     _check(st, "fkb_update_atomic")
     return c, counts
+
+
+def fkb_mfma_peak(blocks: int, iters: int, seed: int, out=None, stamps=None, device="cuda"):
+    """MFMA peak probe: blocks x 4 waves, each iters x 32 v_mfma_f32_32x32x16_f16.
+    Returns (out, stamps); stamps (blocks, 4) int64 = memtime start/end,
+    realtime start/end per block."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    if stamps is None:
+        stamps = torch.empty((blocks, 4), dtype=torch.int64, device=device)
+    st = load_baseline().fkb_mfma_peak(int(blocks), int(iters), int(seed) & 0xFFFFFFFF,
+                                       _dev(out, "out", torch.float32, (blocks * 256,)),
+                                       _dev(stamps, "stamps", torch.int64, (blocks, 4)),
+                                       _stream(out))
+    _check(st, "fkb_mfma_peak")
+    return out, stamps
+
+
+def fkb_wall_clock_khz() -> int:
+    return int(load_baseline().fkb_wall_clock_khz())

@@ -112,6 +112,81 @@ __global__ __launch_bounds__(kThreads) void divide_kernel(const float* __restric
   }
 }
 
+// MFMA peak probe: every wave issues v_mfma_f32_32x32x16_f16 back to back on
+// operands drawn from a counter-based hash (values in [-1, 1), different per
+// lane and per operand), kPeakChains independent accumulator chains so no
+// MFMA waits for the previous one's result, rotating through four A and two B
+// operands; one loop iteration is 4 rounds of kPeakChains MFMAs.
+// Lane 0 of each block records the shader-clock counter (s_memtime) and the
+// constant-rate counter (s_memrealtime) at its start and end, so the host can
+// tell the clock the loop ran at; every wave writes the sum of its
+// accumulators so nothing is optimised away.
+typedef _Float16 fkb_half8 __attribute__((ext_vector_type(8)));
+typedef float fkb_floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t hash32(uint32_t v) {
+  v ^= v >> 16;
+  v *= 0x7feb352dU;
+  v ^= v >> 15;
+  v *= 0x846ca68bU;
+  v ^= v >> 16;
+  return v;
+}
+
+__device__ __forceinline__ fkb_half8 random_half8(uint32_t seed) {
+  fkb_half8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t r = hash32(seed * 8u + (uint32_t)i);
+    h[i] = (_Float16)((float)(r >> 8) * (1.0f / 8388608.0f) - 1.0f);
+  }
+  return h;
+}
+
+constexpr int kPeakChains = 8;
+
+__global__ __launch_bounds__(kThreads) void mfma_peak_kernel(float* __restrict__ out,
+                                                             long long* __restrict__ stamps,
+                                                             int iters, uint32_t seed) {
+  const uint32_t gl = (uint32_t)(blockIdx.x * kThreads + threadIdx.x);
+  long long t0 = 0, r0 = 0;
+  if (threadIdx.x == 0) {
+    t0 = (long long)__builtin_amdgcn_s_memtime();
+    r0 = (long long)__builtin_amdgcn_s_memrealtime();
+  }
+  fkb_half8 a[4], b[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = random_half8(hash32(seed ^ (gl * 16u + (uint32_t)i)));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) b[i] = random_half8(hash32(~seed ^ (gl * 16u + (uint32_t)i)));
+  fkb_floatx16 acc[kPeakChains];
+#pragma unroll
+  for (int c = 0; c < kPeakChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < kPeakChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[(c + r) & 3], b[c & 1], acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kPeakChains; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  out[gl] = s;
+  if (threadIdx.x == 0) {
+    const long long t1 = (long long)__builtin_amdgcn_s_memtime();
+    const long long r1 = (long long)__builtin_amdgcn_s_memrealtime();
+    stamps[4 * blockIdx.x + 0] = t0;
+    stamps[4 * blockIdx.x + 1] = t1;
+    stamps[4 * blockIdx.x + 2] = r0;
+    stamps[4 * blockIdx.x + 3] = r1;
+  }
+}
+
 unsigned grid_for(int64_t n) {
   int64_t g = (n + kThreads - 1) / kThreads;
   return (unsigned)(g < 1 ? 1 : (g > 65536 ? 65536 : g));
@@ -179,4 +254,19 @@ extern "C" fk_status_t fkb_update_atomic(const void* x, const int32_t* ids, fk_d
   if (hipGetLastError() != hipSuccess) return FK_ERR_HIP;
   divide_kernel<<<grid_for(kd), kThreads, 0, stream>>>(sums, counts, c, kd, (int)d);
   return hipGetLastError() == hipSuccess ? FK_OK : FK_ERR_HIP;
+}
+
+extern "C" fk_status_t fkb_mfma_peak(int64_t blocks, int32_t iters, uint32_t seed, float* out,
+                                     long long* stamps, hipStream_t stream) {
+  if (blocks < 1 || blocks > 0x7FFFFFFF || iters < 1 || !out || !stamps) return FK_ERR_INVALID;
+  mfma_peak_kernel<<<(unsigned)blocks, kThreads, 0, stream>>>(out, stamps, iters, seed);
+  return hipGetLastError() == hipSuccess ? FK_OK : FK_ERR_HIP;
+}
+
+extern "C" int32_t fkb_wall_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return 0;
+  return khz;
 }

@@ -234,6 +234,201 @@ def baselines_pass(args) -> int:
     return 0
 
 
+# Counters of the MFMA-utilisation pass: the MFMA pipe's busy cycles, the
+# GPU's busy clock cycles, and what the LDS and the VALU issue. One pass holds
+# at most 8 SQ and 2 GRBM counters.
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU",
+                 "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT",
+                 "GRBM_GUI_ACTIVE")
+PROBE_TAG = "mfma_peak_kernel"
+SIMDS_PER_CU = 4
+# Second pass: where the waves' cycles go (issue, waits by kind, MFMA
+# co-execution with other VALU work).
+STALL_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                  "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
+                  "SQ_VALU_MFMA_COEXEC_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def read_dispatch_counters(path):
+    """Counter values per dispatch: {dispatch id: {"kernel": name, counter: value}}."""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            e = out.setdefault(r["Dispatch_Id"], {"kernel": r["Kernel_Name"]})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def read_dispatch_durations(path):
+    """Kernel durations in ns per dispatch id, from a kernel-trace csv."""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out[r["Dispatch_Id"]] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return out
+
+
+def counter_means(disp, durs, select):
+    """Mean counter values and duration over the dispatches whose kernel name
+    satisfies `select`; None if there are none."""
+    rows = [dict(e, dur_ns=durs.get(i)) for i, e in disp.items() if select(e["kernel"])]
+    if not rows:
+        return None
+    keys = [k for k in rows[0] if k != "kernel"]
+    m = {k: sum(r[k] for r in rows if r.get(k) is not None) /
+         max(1, sum(1 for r in rows if r.get(k) is not None)) for k in keys}
+    m["kernel"] = rows[0]["kernel"]
+    m["dispatches"] = len(rows)
+    return m
+
+
+def mfma_derived(m, cus, flop_per_launch=None, peak_tflops=None, nominal_mhz=2400.0,
+                 xcds=8):
+    """Clock and MFMA utilisation from one kernel's mean counters.
+    GRBM_GUI_ACTIVE is summed over the XCDs (each has its own GRBM), so one
+    XCD's busy cycles are GRBM_GUI_ACTIVE / xcds.
+      clock (MHz)     = GRBM_GUI_ACTIVE / xcds / kernel duration (us)
+      MFMA busy       = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / xcds * CUs * 4 SIMDs)
+      achieved        = flop per launch / duration
+      frac at clock   = achieved / (peak * clock / nominal clock)"""
+    d = {}
+    g = m.get("GRBM_GUI_ACTIVE")
+    dur = m.get("dur_ns")
+    cyc = g / xcds if g else None
+    if cyc and dur:
+        d["clock_mhz"] = cyc / (dur / 1e3)
+    if cyc and m.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+        d["mfma_busy"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * SIMDS_PER_CU)
+    if cyc and m.get("SQ_VALU_MFMA_COEXEC_CYCLES") is not None:
+        d["mfma_coexec"] = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cyc * cus * SIMDS_PER_CU)
+    w = m.get("SQ_WAVE_CYCLES")
+    if w:
+        for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_WAIT_INST_LDS"):
+            if m.get(k) is not None:
+                d[k.replace("SQ_", "").lower() + "_per_wave_cycle"] = m[k] / w
+    if flop_per_launch and dur:
+        d["achieved_tflops"] = flop_per_launch / (dur * 1e-9) / 1e12
+        if peak_tflops:
+            d["frac_of_nominal"] = d["achieved_tflops"] / peak_tflops
+            if "clock_mhz" in d:
+                d["frac_at_clock"] = d["achieved_tflops"] / (peak_tflops * d["clock_mhz"] /
+                                                             nominal_mhz)
+    return d
+
+
+def counters_text(cmds, entries, cus, xcds=8):
+    out = ["rocprofv3 counters: MFMA utilisation and clock", "",
+           "command (passes run from /tmp with TMPDIR=/tmp):"]
+    out += _cmd_lines(cmds)
+    out += ["", f"compute units: {cus} in {xcds} XCDs; GRBM_GUI_ACTIVE is summed over the XCDs;",
+            f"clock = GRBM_GUI_ACTIVE / {xcds} / kernel duration;",
+            f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x {cus} CUs x "
+            f"{SIMDS_PER_CU} SIMDs);",
+            "frac at clock = achieved / (nominal peak x measured clock / 2400 MHz);",
+            "*_per_wave_cycle = counter / SQ_WAVE_CYCLES (second pass).", ""]
+    for name, e in entries.items():
+        m, dv = e["means"], e["derived"]
+        out.append(f"{name}: {short_name(m['kernel'])} ({m['dispatches']} dispatches"
+                   + (f", kernel source digest {e['digest']}" if e.get("digest") else "") + ")")
+        out.append(f"  duration avg {m.get('dur_ns', 0) / 1e3:.1f} us")
+        for k in dict.fromkeys(MFMA_COUNTERS + STALL_COUNTERS):
+            if k in m:
+                out.append(f"  {k:28s} {m[k]:.6g}")
+        for k, v in dv.items():
+            out.append(f"  {k:28s} {v:.4g}")
+        out.append("")
+    return "\n".join(out) + "\n"
+
+
+def counters_pass(args) -> int:
+    """MFMA utilisation and stall attribution of the assign kernel of a
+    workload, next to the same counters for the MFMA peak probe (bench.py
+    --mfma-peak). Each counter set runs in its own rocprofv3 process with
+    --pmc and --kernel-trace (durations per dispatch)."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    wl = args.workload
+    raw = os.path.join(args.raw, wl)
+    os.makedirs(raw, exist_ok=True)
+    os.makedirs(args.out, exist_ok=True)
+    wcmd = ["python3", os.path.join(ROOT, "bench.py"), "--workload", wl, "--steps",
+            str(args.steps), "--warmup", str(args.warmup), "--cpu-batches", "0", "--baselines", "0",
+            "--tol-run", "0"]
+    pcmd = ["python3", os.path.join(ROOT, "bench.py"), "--mfma-peak", "--steps", "3",
+            "--peak-iters", "4000"]
+    sets = {"mfma": args.counter_list.split(","), "stalls": list(STALL_COUNTERS)}
+    passes = {}
+    for prog, cmd in (("workload", wcmd), ("probe", pcmd)):
+        for cset, ctrs in sets.items():
+            tag = f"counters_{cset}_{prog}"
+            passes[tag] = (["rocprofv3", "--pmc", *ctrs, "--kernel-trace", "--output-format",
+                            "csv", "-d", os.path.join(raw, tag), "-o", "run", "--"] + cmd)
+    if not args.summarize_only:
+        with open(os.path.join(raw, "counters_sources.json"), "w") as f:
+            json.dump({ph: source_digest(ph) for ph in PHASE_SOURCES}, f)
+        for tag, cmd in passes.items():
+            rc = _run(cmd, os.path.join(raw, tag + ".log"), min(args.limit, 180))
+            if rc != 0:
+                return rc
+    with open(os.path.join(raw, "counters_sources.json")) as f:
+        digests = json.load(f)
+    from synthdata import SHAPES
+    B, N, d_, K, dt, _, _ = SHAPES[wl]
+    flop = bench.assign_flop(B, N, d_, K)
+    peak = bench.PEAK_MFMA_F32 if dt == "f32" else bench.PEAK_MFMA_F16
+    merged = {"workload": {}, "probe": {}}
+    probe_flop = None
+    for tag in passes:
+        prog = tag.rsplit("_", 1)[1]
+        disp = read_dispatch_counters(_find(os.path.join(raw, tag), "_counter_collection.csv"))
+        durs = read_dispatch_durations(_find(os.path.join(raw, tag), "_kernel_trace.csv"))
+        if prog == "workload":
+            m = counter_means(disp, durs, lambda k: phase_of(k) == "assign")
+        else:
+            m = counter_means(disp, durs, lambda k: PROBE_TAG in k)
+            pj = _bench_json(os.path.join(raw, tag + ".log")) or {}
+            cfg = pj.get("config", {})
+            # blocks x 4 waves x iters x 32 MFMAs of 32768 flop (the probe's grid)
+            probe_flop = (cfg.get("blocks", 0) * 4.0 * cfg.get("iters", 0) * 32 * 32768) or None
+        if m:
+            e = merged[prog]
+            dur = e.get("dur_ns")
+            e.update(m)
+            if dur is not None:        # the first pass's duration (the MFMA counter set)
+                e["dur_ns"] = dur
+    entries = {}
+    if merged["workload"]:
+        m = merged["workload"]
+        entries[f"assign ({wl})"] = {"means": m, "digest": digests["assign"],
+                                     "derived": mfma_derived(m, args.cus, flop, peak)}
+    if merged["probe"]:
+        m = merged["probe"]
+        entries["mfma peak probe"] = {"means": m, "derived": mfma_derived(
+            m, args.cus, probe_flop, bench.PEAK_MFMA_F16)}
+    top = _top_line(args, "--counters --workload " + wl)
+    txt = counters_text([top, "  which runs:"] + list(passes.values()),
+                        entries, args.cus).replace(ROOT + "/", "")
+    with open(os.path.join(args.out, f"counters_{wl}.txt"), "w") as f:
+        f.write(txt)
+    print(txt, flush=True)
+    cpath = os.path.join(args.out, "counters.json")
+    table = {}
+    for base in (os.path.join(ROOT, "profiles", "counters.json"), cpath):
+        try:
+            with open(base) as f:
+                table.update(json.load(f))
+        except (OSError, ValueError):
+            pass
+    table[wl] = {k: {"kernel_source_digest": v.get("digest"), **v["derived"],
+                     "duration_us": v["means"].get("dur_ns", 0) / 1e3}
+                 for k, v in entries.items()}
+    with open(cpath, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    return 0
+
+
 def _top_line(args, what):
     """The command line that reproduces these passes, with the output folders
     given relative to the repository root."""
@@ -257,11 +452,19 @@ def main(argv=None):
     ap.add_argument("--baselines", action="store_true",
                     help="instead: one kernel-statistics pass of a short run that also times "
                          "the contrast baselines (kernels_baselines_<workload>.txt)")
+    ap.add_argument("--counters", action="store_true",
+                    help="instead: the MFMA-utilisation counter pass of the workload's assign and "
+                         "of the MFMA peak probe (counters_<workload>.txt)")
+    ap.add_argument("--counter-list", default=",".join(MFMA_COUNTERS),
+                    help="counters of the --counters pass (at most 8 SQ_ and 2 GRBM_)")
+    ap.add_argument("--cus", type=int, default=256, help="compute units of the GPU")
     args = ap.parse_args(argv)
     # the passes run from /tmp: output folders are fixed against the caller's cwd
     args.out, args.raw = os.path.abspath(args.out), os.path.abspath(args.raw)
     if args.baselines:
         return baselines_pass(args)
+    if args.counters:
+        return counters_pass(args)
     sys.path.insert(0, ROOT)
     import bench  # algorithmic byte counts; bench imports torch lazily
 

@@ -61,6 +61,27 @@ fk_status_t fkb_update_atomic(const void* x, const int32_t* ids, fk_dtype_t dt, 
                               int64_t N, int64_t d, int64_t K, float* c, int32_t* counts,
                               float* sums, hipStream_t stream);
 
+
+/*
+ * MFMA peak probe (a measurement of the chip, not a K-Means step): `blocks`
+ * blocks of 256 threads; every wave issues `iters` x 32 back-to-back
+ * v_mfma_f32_32x32x16_f16 (the instruction the small-D FlashAssign kernel
+ * uses) over 8 independent accumulators, on operands drawn in [-1, 1) from a
+ * counter-based hash of `seed` and the thread index. Each MFMA is 32768 flop,
+ * so the call performs blocks * 4 * iters * 32 * 32768 flop.
+ *   out    (blocks * 256) fp32: per-thread sums of the accumulators;
+ *   stamps (blocks * 4) int64: per block, s_memtime at start and end, then
+ *          s_memrealtime (constant rate, hipDeviceAttributeWallClockRate kHz)
+ *          at start and end; the shader clock follows from their ratio.
+ * FK_ERR_INVALID: blocks < 1, iters < 1 or a null pointer.
+ */
+fk_status_t fkb_mfma_peak(int64_t blocks, int32_t iters, uint32_t seed, float* out,
+                          long long* stamps, hipStream_t stream);
+
+/* Rate of the constant-rate counter read by s_memrealtime on the current
+ * device, in kHz (hipDeviceAttributeWallClockRate); 0 if it cannot be read. */
+int32_t fkb_wall_clock_khz(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -126,7 +126,8 @@ def test_baseline_library_exports_its_header():
     text = open(os.path.join(ROOT, "include", "fkmeans_baselines.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(fkb_[a-z_]+)\s*\(", text)))
-    assert names == ["fkb_assign_materialized", "fkb_update_atomic"]
+    assert names == ["fkb_assign_materialized", "fkb_mfma_peak", "fkb_update_atomic",
+                     "fkb_wall_clock_khz"]
     if not os.path.exists(_binding.BASELINE_LIB_PATH):
         pytest.fail("libfkbaseline.so is not built (run __graft_entry__.build())")
     lib = _binding.load_baseline()
