@@ -1,7 +1,9 @@
 // FlashAssign for gfx950: fused point-centroid distance + online argmin.
 //
 // What is computed (per problem b and point n):
-//   ids[b,n] = argmin_k  ||c_k||^2 - 2 x_n . c_k      (lowest k on ties)
+//   ids[b,n] = argmin_k  ||c_k||^2 - 2 x_n . c_k
+// (scores equal to within the fp32 rounding may resolve to either centroid;
+// see the slot code below)
 // maximised here in the equivalent, exactly scaled form
 //   score_k = x_n . c_k - ||c_k||^2 / 2.
 // The B x N x K distance matrix is never written: point tiles and centroid

@@ -169,29 +169,71 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t grid) {
 // ---------------------------------------------------------------------------
 constexpr int kSegRun = 256;   // sorted positions per segment-reduce run
 
-// A segment longer than one run is reduced in pieces whose sums meet in an
-// fp32 sums row; shorter ones are reduced whole and written as their mean.
+// A segment longer than one run is reduced in pieces (one per run it
+// touches, see LongPieces); shorter ones are reduced whole and written as
+// their mean.
 __device__ __forceinline__ bool is_long(int lo, int hi) { return hi - lo > kSegRun; }
 
-// An update whose long clusters still hold their sums (the division by the
-// count is left to the next pass over the centroids). sums null: nothing
-// pending.
+// Pieces of long segments, reduced in a fixed order. The segment-reduce wave
+// of run r writes at most two pieces: slot 0, the piece of the long segment
+// that covers the run's first position and started before it (its "head"),
+// and slot 1, the piece of a long segment that starts inside the run (at
+// most one can: it then covers the rest of the run). Q1 row j holds the sum
+// of the slot-0 pieces of runs 32j .. 32j+31 in run order, Q2 row i the sum
+// of Q1 rows 32i .. 32i+31 in order; each exists only for full blocks. A long
+// cluster with positions [lo, hi) then sums to
+//   slot1[lo/256] + (slot0 of runs lo/256+1 .. (hi-1)/256, in run order)
+// where whole aligned blocks of 32 (1024) runs are taken from Q1 (Q2). The
+// order depends only on lo and hi, so the result does not depend on how the
+// GPU schedules its waves.
+constexpr int kQ1 = 32;     // runs per Q1 block
+constexpr int kQ2 = 32;     // Q1 blocks per Q2 block
+
+struct LongPieces {
+  const float* pieces = nullptr;   // (B, runs, 2, d)
+  const float* q1 = nullptr;       // (B, nq1, d)
+  const float* q2 = nullptr;       // (B, nq2, d)
+  int runs = 0, nq1 = 0, nq2 = 0;
+};
+
+// Column c of the sum of long segment [lo, hi) of problem b.
+__device__ __forceinline__ float long_sum(const LongPieces& lp, int64_t b, int64_t d, int lo,
+                                          int hi, int64_t c) {
+  const int rlo = lo / kSegRun, e = (hi - 1) / kSegRun + 1;
+  const float* pb = lp.pieces + (int64_t)b * lp.runs * 2 * d + c;
+  const float* q1 = lp.q1 + (int64_t)b * lp.nq1 * d + c;
+  const float* q2 = lp.q2 + (int64_t)b * lp.nq2 * d + c;
+  float t = 0.f;
+  int r = rlo + 1;
+  for (; r < e && (r % kQ1) != 0; ++r) t += pb[(int64_t)r * 2 * d];
+  for (; r + kQ1 <= e && (r % (kQ1 * kQ2)) != 0; r += kQ1) t += q1[(int64_t)(r / kQ1) * d];
+  for (; r + kQ1 * kQ2 <= e; r += kQ1 * kQ2) t += q2[(int64_t)(r / (kQ1 * kQ2)) * d];
+  for (; r + kQ1 <= e; r += kQ1) t += q1[(int64_t)(r / kQ1) * d];
+  for (; r < e; ++r) t += pb[(int64_t)r * 2 * d];
+  return pb[((int64_t)rlo * 2 + 1) * d] + t;
+}
+
+// An update whose long clusters are still in pieces (their sum and the
+// division by the count are left to the next pass over the centroids).
+// offsets null: nothing pending.
 struct PendingFinish {
-  const float* sums = nullptr;          // (B,K,d)
+  LongPieces lp;
   const int32_t* offsets = nullptr;     // (B,K+1)
   const int32_t* has_long = nullptr;    // (B)
   int64_t K = 0;
 };
 
-// For centroid row `row` (= b*K + k): the count to divide its sums row by,
-// or 0 when the row is already final.
-__device__ __forceinline__ float pending_count(const PendingFinish& pf, int64_t row) {
-  if (!pf.sums) return 0.f;
+// For centroid row `row` (= b*K + k): its long segment [lo, hi) when the row
+// is pending, else hi == lo.
+__device__ __forceinline__ void pending_segment(const PendingFinish& pf, int64_t row, int& lo,
+                                                int& hi) {
+  lo = hi = 0;
+  if (!pf.offsets) return;
   const int64_t b = row / pf.K, k = row - b * pf.K;
-  if (!pf.has_long[b]) return 0.f;
+  if (!pf.has_long[b]) return;
   const int32_t* ob = pf.offsets + b * (pf.K + 1);
-  const int lo = ob[k], hi = ob[k + 1];
-  return is_long(lo, hi) ? (float)(hi - lo) : 0.f;
+  const int l = ob[k], h = ob[k + 1];
+  if (is_long(l, h)) lo = l, hi = h;
 }
 
 // ---------------------------------------------------------------------------
@@ -215,14 +257,22 @@ hipError_t launch_assign_splitd(const void* x, const void* c_lp, const float* cn
 
 // Sort-inverse update; workspace carved by the API layer.
 struct UpdateWs {
-  float* sums;          // (B,K,d) fp32: short clusters' means, long clusters' sums
+  float* pieces;        // (B,runs,2,d) fp32 pieces of long segments (see LongPieces)
+  float* q1;            // (B,nq1,d) sums of 32 consecutive slot-0 pieces
+  float* q2;            // (B,nq2,d) sums of 32 consecutive Q1 rows
   int32_t* offsets;     // (B,K+1) segment starts
-  int32_t* cursor;      // (B,K) scatter cursors (multi-block sort)
   int32_t* perm;        // (B,N) point index per sorted position
   int32_t* run_first;   // (B,runs) cluster holding each run's first position
   float* part;          // (B, finalize blocks) partial squared moves
   int32_t* hist;        // (B, G, K) per-chunk counts of the split sort
   int32_t* has_long;    // (B) nonzero when the problem has a long cluster
+  int32_t* rkeys[2];    // (B,N) keys between radix passes (large chunks / large K)
+  int32_t* ridx[2];     // (B,N) point indices between radix passes
+  int32_t* rhist;       // (B, radix chunks, 256) digit counts of one radix pass
+  int32_t* rcolsum;     // (passes, B, chunk groups, 256) digit counts per group of chunks
+  int32_t* rgbase;      // (B, chunk groups, 256) first output position per group and digit
+  int32_t* cursor;      // (B,K) scatter cursors (K above 2^16 only)
+  int runs, nq1, nq2;
 };
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K);
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K);
@@ -233,6 +283,7 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
                          int64_t d, int64_t K, float* c, int32_t* counts, float* shift,
                          const UpdateWs& ws, hipStream_t s, bool defer = false);
 PendingFinish pending_finish(const UpdateWs& ws, int64_t K);
+LongPieces long_pieces(const UpdateWs& ws);
 hipError_t launch_finish(float* c, const UpdateWs& ws, int64_t B, int64_t d, int64_t K,
                          hipStream_t s);
 

@@ -16,7 +16,8 @@ namespace {
 constexpr int kWaves = 4;
 
 // Every norms kernel first finishes a deferred update (pf): a long cluster's
-// row is its sums row divided by its count, written back to c.
+// row is the sum of its pieces (fixed order, see LongPieces) divided by its
+// count, written back to c.
 template <int DT>
 __global__ __launch_bounds__(256) void norms_kernel(float* __restrict__ c,
                                                     uint16_t* __restrict__ c_lp,
@@ -25,14 +26,15 @@ __global__ __launch_bounds__(256) void norms_kernel(float* __restrict__ c,
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const float cnt = pending_count(pf, row);
-  const float* src = cnt > 0.f ? pf.sums + row * d : c + row * d;
+  int lo, hi;
+  pending_segment(pf, row, lo, hi);
+  const int64_t b = pf.offsets ? row / pf.K : 0;
   uint16_t* dst = c_lp + row * d;
   float acc = 0.f;
   for (int64_t j = lane; j < d; j += 64) {
-    float v = src[j];
-    if (cnt > 0.f) {
-      v = v / cnt;
+    float v = c[row * d + j];
+    if (hi > lo) {
+      v = long_sum(pf.lp, b, d, lo, hi, j) / (float)(hi - lo);
       c[row * d + j] = v;
     }
     const uint16_t h = Elem<DT>::narrow(v);
@@ -58,14 +60,21 @@ __global__ __launch_bounds__(256) void norms_vec_kernel(float* __restrict__ c,
   const bool ok = row < rows;
   float acc = 0.f;
   if (ok) {
-    const float cnt = pending_count(pf, row);
-    const float* src = cnt > 0.f ? pf.sums + row * d : c + row * d;
+    int lo, hi;
+    pending_segment(pf, row, lo, hi);
+    const int64_t b = pf.offsets ? row / pf.K : 0;
+    const float cnt = (float)(hi - lo);
     uint16_t* dst = c_lp + row * d;
     for (int j = li * 4; j < d; j += LPR * 4) {
-      float4 v = *reinterpret_cast<const float4*>(src + j);
-      if (cnt > 0.f) {                      // sums rows are 16-byte aligned like c's
-        v = make_float4(v.x / cnt, v.y / cnt, v.z / cnt, v.w / cnt);
+      float4 v;
+      if (hi > lo) {
+        v = make_float4(long_sum(pf.lp, b, d, lo, hi, j) / cnt,
+                        long_sum(pf.lp, b, d, lo, hi, j + 1) / cnt,
+                        long_sum(pf.lp, b, d, lo, hi, j + 2) / cnt,
+                        long_sum(pf.lp, b, d, lo, hi, j + 3) / cnt);
         *reinterpret_cast<float4*>(c + row * d + j) = v;
+      } else {
+        v = *reinterpret_cast<const float4*>(c + row * d + j);
       }
       const uint16_t h[4] = {Elem<DT>::narrow(v.x), Elem<DT>::narrow(v.y), Elem<DT>::narrow(v.z),
                              Elem<DT>::narrow(v.w)};
@@ -113,14 +122,15 @@ __global__ __launch_bounds__(256) void norms_f32_kernel(float* __restrict__ c,
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const float cnt = pending_count(pf, row);
-  const float* src = cnt > 0.f ? pf.sums + row * d : c + row * d;
+  int lo, hi;
+  pending_segment(pf, row, lo, hi);
+  const int64_t b = pf.offsets ? row / pf.K : 0;
   float* dst = c_lp + row * d;
   float acc = 0.f;
   for (int64_t j = lane; j < d; j += 64) {
-    float r = src[j];
-    if (cnt > 0.f) {
-      r = r / cnt;
+    float r = c[row * d + j];
+    if (hi > lo) {
+      r = long_sum(pf.lp, b, d, lo, hi, j) / (float)(hi - lo);
       c[row * d + j] = r;
     }
     dst[j] = r;
@@ -163,10 +173,10 @@ unsigned grid_for(int64_t count) {
 hipError_t launch_norms(const float* c_in, void* c_lp, float* cnorm, int dt, int64_t rows,
                         int64_t d, hipStream_t s, const PendingFinish& pf) {
   if (rows == 0) return hipSuccess;
-  // written only when an update is pending (pf.sums), on the caller's own buffer
+  // written only when an update is pending (pf.offsets), on the caller's own buffer
   float* c = const_cast<float*>(c_in);
   const bool vec = d % 4 == 0 && d <= 0x7FFFFFFF && ((uintptr_t)c % 16) == 0 &&
-                   ((uintptr_t)c_lp % 8) == 0 && ((uintptr_t)pf.sums % 16) == 0;
+                   ((uintptr_t)c_lp % 8) == 0;
   if (vec && dt == FK_F16)
     return norms_vec_dt<FK_F16>(c, (uint16_t*)c_lp, cnorm, rows, d, pf, s);
   if (vec && dt == FK_BF16)

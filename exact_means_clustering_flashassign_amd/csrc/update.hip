@@ -4,40 +4,56 @@
 // segments through an inverse permutation of point indices; the point matrix
 // itself never moves. Each segment is then reduced on chip, and a cluster
 // whose segment is longer than one run of sorted positions is summed in
-// pieces, with one atomic add per element per piece instead of one scatter
-// atomic per point (itinai.com summary, third paragraph; "Flash-KMeans：IO感知
-// 的精确K-Means…", section "它攻克的两大瓶颈" and the update-contention panel of
-// "交互式讲解"; "Flash-KMeans: Implementação Exata…", section "Sort-Inverse
-// Update"; "Flash-KMeans: Fast and Memory-Efficient Exact K-Means", Abstract).
+// pieces, one per run it touches, instead of one scatter atomic per point
+// (itinai.com summary, third paragraph; "Flash-KMeans：IO感知的精确K-Means…",
+// section "它攻克的两大瓶颈" and the update-contention panel of "交互式讲解";
+// "Flash-KMeans: Implementação Exata…", section "Sort-Inverse Update";
+// "Flash-KMeans: Fast and Memory-Efficient Exact K-Means", Abstract).
 //
 // Terms. Sorted positions of a problem are cut into runs of kSegRun; the
 // segment [lo, hi) of cluster k is short when it holds at most kSegRun
 // positions, long otherwise.
 //
+// Every result is independent of how the GPU schedules its work: the sort is
+// stable (a cluster's points keep their index order in perm), each segment
+// is summed in a fixed order, and long clusters' pieces are combined in an
+// order fixed by their positions. Ids, counts and centroids are therefore
+// bit-identical from run to run (clusters up to 2^16: larger K takes an
+// atomic-cursor scatter).
+//
 // Steps:
 //   sort      counts, offsets (exclusive prefix sum of counts), perm
-//             (perm[offsets[id] + rank] = n) and, per run, the cluster that
-//             holds its first position; long clusters get zeroed sums rows.
+//             (perm[offsets[id] + rank] = n, rank = order of n among the
+//             points of its cluster) and, per run, the cluster that holds
+//             its first position.
 //             Split sort (K <= 32768): per-chunk LDS histograms into a count
-//             matrix, column prefixes and offsets, then LDS-ranked scatter;
-//             no global atomics. Larger K: per-range LDS histograms with one
-//             global atomic per non-empty bin, scan, prep, scatter.
+//             matrix, column prefixes and offsets (no global atomics); then
+//             either each chunk is sorted stably in LDS and scattered
+//             (chunks that fit LDS), or perm comes from LSD radix passes over
+//             the whole problem, 8 key bits per pass, each pass a stable
+//             counting sort (per-chunk digit counts, their prefixes, a
+//             scatter ranked by wave order and lane order).
+//             Larger K: per-range LDS histograms with one global atomic per
+//             non-empty bin, scan, prep, then the radix passes (K <= 2^16) or
+//             an atomic-cursor scatter.
 //   segreduce one wave per (run, column slice). A short segment is summed
 //             whole by the wave whose run holds its first position (it may
 //             read up to kSegRun - 1 positions past its run) and its mean
 //             (sum / count) is written straight into c, the squared move into
 //             the wave's shift partial. A long segment is summed piecewise,
-//             one piece per run it touches, into its zeroed sums row with one
-//             fp32 atomic per element: at most (number of long clusters +
-//             number of runs) * d atomics per problem, none at all when every
-//             cluster is short.
+//             one piece per run it touches, each piece stored to its run's
+//             slot (see LongPieces).
+//   q1/q2     sums of the head pieces of every full block of 32 runs (Q1),
+//             and of 32 Q1 rows (Q2), in order.
 //   finalize  elementwise over (cluster, column) of long clusters:
-//             c = sums / count, squared moves into the block's partial; with
-//             a shift buffer, shift_reduce sums a problem's partials (its
-//             segreduce waves', then its finalize blocks') in a fixed order
-//             into shift[b].
+//             c = (sum of its pieces in fixed order) / count, squared moves
+//             into the block's partial; with a shift buffer, shift_reduce
+//             sums a problem's partials (its segreduce waves', then its
+//             finalize blocks') in a fixed order into shift[b].
 // Empty clusters are never touched, so they keep their centroid. Ids outside
 // [0, K) are skipped: they count nowhere and add to no cluster.
+#include <stdlib.h>
+
 #include "fk_internal.hpp"
 
 namespace fk {
@@ -48,8 +64,7 @@ constexpr int kMaxLdsBins = 32768;            // 128 KB of LDS bins per block
 constexpr int kSortThreads = 1024;
 constexpr int kSortUnroll = 16;               // ids in flight per thread in the sort kernels
 constexpr int64_t kFusedOffsetsMax = 1 << 16; // G*K up to this: one offsets block per problem
-constexpr size_t kSortedScatterLds = 96 * 1024;  // LDS budget of the sorted scatter
-constexpr int kLongList = 1024;               // long clusters listed per problem by offsets
+constexpr size_t kStableLdsMax = 144 * 1024;  // dynamic LDS of one stable-scatter block, at most
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -57,16 +72,6 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Runs whose first position lies in [lo, hi) start inside cluster k.
 __device__ __forceinline__ void mark_runs(int32_t* rf, int k, int lo, int hi) {
   for (int64_t r = (lo + (int64_t)kSegRun - 1) / kSegRun; r * kSegRun < hi; ++r) rf[r] = k;
-}
-
-// A long cluster's sums row, zeroed by one thread before its pieces are added
-// (rows start 16-byte aligned when d % 4 == 0: the buffer is 256-byte aligned).
-__device__ __forceinline__ void zero_row(float* row, int d) {
-  if (d % 4 == 0) {
-    for (int j = 0; j < d; j += 4) *reinterpret_cast<float4*>(row + j) = make_float4(0.f, 0.f, 0.f, 0.f);
-  } else {
-    for (int j = 0; j < d; ++j) row[j] = 0.f;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -105,6 +110,82 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wtot, int& t
   return before + incl - v;
 }
 
+// Exclusive prefix maximum over the kSortThreads threads of a block (-1 for
+// thread 0). wtot: kSortThreads / 64 ints of LDS.
+__device__ __forceinline__ int block_exclusive_max(int v, int32_t* wtot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl = max(incl, u);
+  }
+  const int excl_in_wave = __shfl_up(incl, 1, 64);
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = -1;
+#pragma unroll
+  for (int i = 0; i < kSortThreads / 64; ++i) before = i < w ? max(before, wtot[i]) : before;
+  __syncthreads();
+  return lane > 0 ? max(before, excl_in_wave) : before;
+}
+
+constexpr int kWavesSort = kSortThreads / 64;   // 16 waves per sort block
+
+// Elements a wave walks in a stable pass over n elements: consecutive ranges
+// of whole 64-element steps, wave 0 first.
+__device__ __forceinline__ int wave_span(int n) {
+  return (n + kSortThreads - 1) / kSortThreads * 64;
+}
+
+// One counting-sort pass over the n words of src (LDS) into dst (LDS), by
+// the digit (word >> shift) & (2^nbits - 1). Wave w walks its own
+// consecutive range of elements 64 at a time and counts into its own
+// counters (hist: 16 x 2^nbits ints, wave-major), so no two waves share a
+// counter; a word's new position is the number of words with a smaller
+// digit, plus those with the same digit in earlier waves, plus what its
+// wave's counter returns (earlier steps of the walk, and within a step the
+// order in which the LDS unit serves the lanes of one instruction). Nothing
+// depends on how the waves are scheduled. The starts come from one exclusive
+// scan over (digit, wave) in digit-major order.
+__device__ void lds_stable_pass(const uint32_t* src, uint32_t* dst, int n, int shift, int nbits,
+                                int32_t* hist, int32_t* wtot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int R = 1 << nbits;
+  const int per = wave_span(n);
+  const int s0 = min(w * per, n), s1 = min(s0 + per, n);
+  for (int r = lane; r < R; r += 64) hist[w * R + r] = 0;
+  for (int i = s0 + lane; i < s1; i += 64)
+    atomicAdd(&hist[w * R + ((src[i] >> shift) & (uint32_t)(R - 1))], 1);
+  __syncthreads();
+  const int M = R * kWavesSort;
+  const int E = (M + kSortThreads - 1) / kSortThreads;
+  const int e0 = min((int)threadIdx.x * E, M), e1 = min(e0 + E, M);
+  int sum = 0;
+  for (int e = e0; e < e1; ++e) sum += hist[(e % kWavesSort) * R + e / kWavesSort];
+  int total;
+  int run = block_exclusive_scan(sum, wtot, total);
+  for (int e = e0; e < e1; ++e) {
+    int* h = &hist[(e % kWavesSort) * R + e / kWavesSort];
+    const int c = *h;
+    *h = run;
+    run += c;
+  }
+  __syncthreads();
+  for (int i = s0 + lane; i < s1; i += 64) {
+    const uint32_t word = src[i];
+    dst[atomicAdd(&hist[w * R + ((word >> shift) & (uint32_t)(R - 1))], 1)] = word;
+  }
+  __syncthreads();
+}
+
+// Bits needed for the values 0 .. K (K itself marks an id outside [0, K)).
+__host__ __device__ __forceinline__ int key_bits(int64_t K) {
+  int b = 1;
+  while (((int64_t)1 << b) <= K) ++b;
+  return b;
+}
+
 // ---------------------------------------------------------------------------
 // Split sort (K <= kMaxLdsBins): each problem's ids are cut into G chunks, one
 // block each.
@@ -112,11 +193,11 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wtot, int& t
 //            problem's (G, K) count matrix H (no global atomics);
 //   offsets  per problem: H's columns become exclusive prefix sums over g,
 //            their totals are the counts, whose exclusive prefix sum gives
-//            the segment offsets; also the run starts and zeroed sums rows of
-//            long clusters (one block per problem when G*K is small;
-//            colscan + scan + prep otherwise);
-//   scatter2 block (b, g): LDS cursors offsets[k] + H[g][k], LDS ranks,
-//            perm[cursor] = n.
+//            the segment offsets; also the run starts and the long-cluster
+//            flag (one block per problem when G*K is small; colscan + offsets
+//            + prep otherwise);
+//   perm     chunks that fit LDS: scatter_stable_kernel; otherwise the radix
+//            passes.
 __global__ __launch_bounds__(kSortThreads) void hist2_kernel(const int32_t* __restrict__ ids,
                                                              int32_t* __restrict__ H, int N, int K,
                                                              int G, int chunk) {
@@ -131,7 +212,8 @@ __global__ __launch_bounds__(kSortThreads) void hist2_kernel(const int32_t* __re
 #pragma unroll
     for (int q = 0; q < kSortUnroll; ++q) {
       const int n = m + q * kSortThreads + t;
-      kk[q] = n < n1 ? ib[n] : -1;
+      const int v = ib[min(n, n1 - 1)];           // unconditional: loads in flight together
+      kk[q] = n < n1 ? v : -1;
     }
 #pragma unroll
     for (int q = 0; q < kSortUnroll; ++q)
@@ -165,14 +247,13 @@ __device__ __forceinline__ int column_prefix(int32_t* hb, int64_t K, int G, int 
 }
 
 // offsets: G > 0: column prefixes of H and counts first, then offsets, run
-// starts and zeroed long rows; G == 0: counts given, offsets only.
+// starts and the long-cluster flag; G == 0:
+// counts given, offsets only.
 __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
     int32_t* __restrict__ H, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ run_first, float* __restrict__ sums, int32_t* __restrict__ has_long,
-    int K, int d, int G, int runs) {
+    int32_t* __restrict__ run_first, int32_t* __restrict__ has_long, int K, int G, int runs) {
   extern __shared__ int32_t cnt[];              // K + 1
   __shared__ int32_t wtot[kSortThreads / 64];
-  __shared__ int32_t longs[kLongList];           // long clusters, zeroed by the whole block
   __shared__ int32_t nlong;
   const int b = blockIdx.x, t = threadIdx.x;
   if (t == 0) nlong = 0;
@@ -199,38 +280,23 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   int run = block_exclusive_scan(s, wtot, total);
   int32_t* ob = offsets + (int64_t)b * (K + 1);
   int32_t* rf = run_first + (int64_t)b * runs;
-  float* sb = sums ? sums + (int64_t)b * K * d : nullptr;   // null: no rows to zero
+  int mylong = 0;
   for (int i = lo; i < hi; ++i) {
     const int c = cnt[i];
     if (G > 0) cb[i] = c;
     cnt[i] = run;
     if (G > 0 && c > 0) mark_runs(rf, i, run, run + c);
-    if (G > 0 && sb && is_long(run, run + c)) {
-      const int q = atomicAdd(&nlong, 1);
-      if (q < kLongList) longs[q] = i;
-      else zero_row(sb + (int64_t)i * d, d);     // past the list: this thread alone
-    }
+    mylong += is_long(run, run + c) ? 1 : 0;
     run += c;
   }
+  if (mylong) atomicAdd(&nlong, mylong);
   if (t == 0) cnt[K] = total;
   __syncthreads();
   for (int k = t; k <= K; k += kSortThreads) ob[k] = cnt[k];   // coalesced
-  if (G == 0) return;                            // run starts, rows, flag: prep_kernel
+  if (G == 0) return;                            // run starts, flag, counters: prep_kernel
   if (t == 0) has_long[b] = nlong;
   for (int64_t r = (total + (int64_t)kSegRun - 1) / kSegRun + t; r < runs; r += kSortThreads)
     rf[r] = K;                                   // runs past the last valid position
-  // the listed long clusters' sums rows, spread over the block
-  if (!sb) return;
-  const int nl = min(nlong, kLongList);
-  if (d % 4 == 0) {
-    const int nv = d / 4;
-    for (int64_t e = t; e < (int64_t)nl * nv; e += kSortThreads) {
-      const int k = longs[e / nv];
-      *reinterpret_cast<float4*>(sb + (int64_t)k * d + (e % nv) * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  } else {
-    for (int64_t e = t; e < (int64_t)nl * d; e += kSortThreads) sb[(int64_t)longs[e / d] * d + e % d] = 0.f;
-  }
 }
 
 // Large G*K: column prefixes on a grid, one thread per (problem, cluster).
@@ -243,100 +309,434 @@ __global__ __launch_bounds__(kThreads) void colscan_kernel(int32_t* __restrict__
   counts[(int64_t)b * K + k] = column_prefix(H + (int64_t)b * G * K, K, G, k);
 }
 
-__global__ __launch_bounds__(kSortThreads) void scatter2_kernel(
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ H,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int N, int K, int G,
-    int chunk) {
-  extern __shared__ int32_t bins[];
-  const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
-  const int32_t* hr = H + ((int64_t)b * G + g) * K;
-  const int32_t* ob = offsets + (int64_t)b * (K + 1);
-  for (int i = t; i < K; i += kSortThreads) bins[i] = ob[i] + hr[i];
-  __syncthreads();
-  const int32_t* ib = ids + (int64_t)b * N;
-  int32_t* pb = perm + (int64_t)b * N;
-  const int n0 = g * chunk, n1 = min(n0 + chunk, N);
-  for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
-    int kk[kSortUnroll];
-#pragma unroll
-    for (int q = 0; q < kSortUnroll; ++q) {
-      const int n = m + q * kSortThreads + t;
-      kk[q] = n < n1 ? ib[n] : -1;
-    }
-#pragma unroll
-    for (int q = 0; q < kSortUnroll; ++q)
-      if ((unsigned)kk[q] < (unsigned)K) pb[atomicAdd(&bins[kk[q]], 1)] = m + q * kSortThreads + t;
-  }
+// Direct scatter (ids in at most kDirectKeyBits bits, chunks of at most
+// kStableChunk ids): the chunk's ids are staged in LDS and walked twice, wave
+// w over its own consecutive range in steps of 64, counting into its own
+// counters. The first walk counts each id per wave; prefixes over the waves
+// (per id) and over the ids then give each (id, wave) its first rank among
+// the chunk's points of that id, and where the id's points start in the
+// chunk's id order. The second walk's counters return each point's rank r,
+// and point n goes to
+//   perm[offsets[id] + H[g][id] + r]
+// The ranks follow the walk (earlier waves, earlier steps, and within a step
+// the order in which the LDS unit serves one instruction's lanes), never the
+// scheduling of the waves. The stores are staged in LDS in id order first,
+// so they go out as runs of consecutive addresses. The counters are 16-bit
+// halves of 32-bit words (waves 2j and 2j+1 share a word; a chunk holds at
+// most 2^14 ids, so a half never carries into the other).
+constexpr int kDirectKeyBits = 11;
+constexpr int kLocalBits = 14;                 // point index within a chunk
+constexpr int kStableChunk = 1 << kLocalBits;  // ids per chunk of an LDS sort, at most
+
+size_t direct_lds_bytes(int64_t chunk, int64_t K) {
+  return (size_t)chunk * 8 + (size_t)(K + 1) * 8 + (size_t)(K + 1) * (kSortThreads / 128) * 4;
 }
 
-// scatter2, sorted form (when 2K + 2*chunk ints fit LDS): the chunk is
-// counting-sorted in LDS first, so the perm stores of one cluster's piece go
-// out as consecutive addresses instead of one scattered 4-byte store per
-// point.
-//   cur[k]  local cursor, from the chunk's exclusive prefix of cluster sizes
-//   gof[k]  global position of the chunk's piece of cluster k minus its local
-//           start: perm[gof[k] + p] = sidx[p] for local sorted position p
-__global__ __launch_bounds__(kSortThreads) void scatter2s_kernel(
+__global__ __launch_bounds__(kSortThreads) void scatter_direct_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ H,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int N, int K, int G,
     int chunk) {
-  extern __shared__ int32_t sm[];
-  int32_t* cur = sm;
-  int32_t* gof = sm + K;
-  int32_t* skey = sm + 2 * K;
-  int32_t* sidx = skey + chunk;
-  __shared__ int32_t wtot[kSortThreads / 64];
+  extern __shared__ int32_t sdir[];
+  __shared__ int32_t wtot[kWavesSort];
+  constexpr int SMAX = kStableChunk / kSortThreads;   // steps of 64 per wave, at most
+  constexpr int WP = kWavesSort / 2;                   // counter words per id
   const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
-  const int32_t* hr = H + ((int64_t)b * G + g) * K;
-  const int32_t* ob = offsets + (int64_t)b * (K + 1);
-  const int32_t* ib = ids + (int64_t)b * N;
-  const int n0 = g * chunk, n1 = min(n0 + chunk, N);
-  for (int i = t; i < K; i += kSortThreads) cur[i] = 0;
-  __syncthreads();
-  for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
+  const int lane = t & 63, w = t >> 6;
+  const int n0 = g * chunk;
+  const int n = min(chunk, N - n0);
+  if (n <= 0) return;                            // whole block: no barrier follows
+  const int K1 = K + 1;
+  int32_t* skey = sdir;                          // chunk: ids, then global positions
+  int32_t* sval = sdir + chunk;                  // chunk: point indices in id order
+  int32_t* gstart = sval + chunk;                // K + 1
+  int32_t* lstart = gstart + K1;                 // K + 1
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(lstart + K1);   // WP x (K + 1)
+  uint32_t* mycnt = cnt + (w >> 1) * K1;
+  const uint32_t inc = 1u << (16 * (w & 1));
+  const int sh = 16 * (w & 1);
+  const int32_t* ib = ids + (int64_t)b * N + n0;
+  for (int m = 0; m < n; m += kSortThreads * kSortUnroll) {
     int kk[kSortUnroll];
 #pragma unroll
     for (int q = 0; q < kSortUnroll; ++q) {
-      const int n = m + q * kSortThreads + t;
-      kk[q] = n < n1 ? ib[n] : -1;
+      const int i = m + q * kSortThreads + t;
+      kk[q] = ib[min(i, n - 1)];                 // unconditional: loads in flight together
     }
 #pragma unroll
-    for (int q = 0; q < kSortUnroll; ++q)
-      if ((unsigned)kk[q] < (unsigned)K) atomicAdd(&cur[kk[q]], 1);
+    for (int q = 0; q < kSortUnroll; ++q) {
+      const int i = m + q * kSortThreads + t;
+      if (i < n) skey[i] = (unsigned)kk[q] < (unsigned)K ? kk[q] : K;
+    }
   }
+  const int32_t* hr = H + ((int64_t)b * G + g) * K;
+  const int32_t* ob = offsets + (int64_t)b * K1;
+  for (int k = t; k < K; k += kSortThreads) gstart[k] = ob[k] + hr[k];
+  for (int e = t; e < WP * K1; e += kSortThreads) cnt[e] = 0;
   __syncthreads();
-  const int per = (K + kSortThreads - 1) / kSortThreads;
-  const int lo = min(t * per, K), hi = min(lo + per, K);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += cur[i];
-  int total;
-  int run = block_exclusive_scan(sum, wtot, total);
-  for (int i = lo; i < hi; ++i) {
-    const int c = cur[i];
-    cur[i] = run;
-    gof[i] = ob[i] + hr[i] - run;
+  const int per = wave_span(n);
+  const int s0 = min(w * per, n), s1 = min(s0 + per, n);
+  for (int i = s0 + lane; i < s1; i += 64) atomicAdd(&mycnt[skey[i]], inc);
+  __syncthreads();
+  // per id: prefix over the waves and the id's total; ids are spread over
+  // the threads in consecutive groups so one scan gives their local starts
+  const int KPT = (K1 + kSortThreads - 1) / kSortThreads;
+  const int k0 = min(t * KPT, K1), k1 = min(k0 + KPT, K1);
+  int tsum = 0;
+  for (int k = k0; k < k1; ++k) {
+    uint32_t cw[WP];
+#pragma unroll
+    for (int j = 0; j < WP; ++j) cw[j] = cnt[j * K1 + k];
+    int run = 0;
+#pragma unroll
+    for (int j = 0; j < WP; ++j) {
+      const int ce = (int)(cw[j] & 0xFFFFu), co = (int)(cw[j] >> 16);
+      cnt[j * K1 + k] = (uint32_t)run | ((uint32_t)(run + ce) << 16);
+      run += ce + co;
+    }
+    lstart[k] = run;                             // the id's total, for now
+    tsum += run;
+  }
+  int all;
+  int run = block_exclusive_scan(tsum, wtot, all);
+  for (int k = k0; k < k1; ++k) {
+    const int c = lstart[k];
+    lstart[k] = run;
     run += c;
   }
   __syncthreads();
-  for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
-    int kk[kSortUnroll];
+  // second walk: each point's place in the chunk's id order and its global
+  // position, held in registers until every wave has read its ids
+  int lp[SMAX], gp[SMAX];
 #pragma unroll
-    for (int q = 0; q < kSortUnroll; ++q) {
-      const int n = m + q * kSortThreads + t;
-      kk[q] = n < n1 ? ib[n] : -1;
+  for (int j = 0; j < SMAX; ++j) {
+    const int i = s0 + j * 64 + lane;
+    lp[j] = gp[j] = -1;
+    if (i < s1) {
+      const int key = skey[i];
+      const int r = (int)((atomicAdd(&mycnt[key], inc) >> sh) & 0xFFFFu);
+      lp[j] = lstart[key] + r;
+      gp[j] = key < K ? gstart[key] + r : -1;
     }
+  }
+  __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kSortUnroll; ++q) {
-      if ((unsigned)kk[q] < (unsigned)K) {
-        const int p = atomicAdd(&cur[kk[q]], 1);
-        skey[p] = kk[q];
-        sidx[p] = m + q * kSortThreads + t;
-      }
+  for (int j = 0; j < SMAX; ++j) {
+    if (lp[j] >= 0) {
+      skey[lp[j]] = gp[j];
+      sval[lp[j]] = n0 + s0 + j * 64 + lane;
     }
   }
   __syncthreads();
   int32_t* pb = perm + (int64_t)b * N;
-  for (int p = t; p < total; p += kSortThreads) pb[gof[skey[p]] + p] = sidx[p];
+  for (int l = t; l < n; l += kSortThreads) {
+    const int pos = skey[l];
+    if (pos >= 0) pb[pos] = sval[l];
+  }
+}
+
+// scatter2, stable form (chunks of at most kStableChunk ids): the chunk's
+// words (id << kLocalBits | local index; ids outside [0, K) become K) are
+// sorted in LDS by stable passes of at most 8 id bits, which orders them by
+// (id, index). Position p of the sorted chunk belongs to the segment that
+// starts at the last p0 <= p with a new id, and goes to
+//   perm[offsets[id] + H[g][id] + (p - p0)]
+// (H holds the column prefixes: where the chunk's piece of each cluster
+// starts). The start of each p is found with a block-wide prefix maximum, the
+// segment's base read from global memory once per segment.
+
+__global__ __launch_bounds__(kSortThreads) void scatter_stable_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ H,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int N, int K, int G,
+    int chunk, int kbits) {
+  extern __shared__ uint32_t swords[];
+  __shared__ int32_t wtot[kWavesSort];
+  const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
+  const int n0 = g * chunk;
+  const int n = min(chunk, N - n0);
+  if (n <= 0) return;                            // whole block: no barrier follows
+  uint32_t* src = swords;
+  uint32_t* dst = swords + chunk;
+  int32_t* hist = reinterpret_cast<int32_t*>(swords + 2 * chunk);
+  const int32_t* ib = ids + (int64_t)b * N + n0;
+  for (int m = 0; m < n; m += kSortThreads * kSortUnroll) {
+    int kk[kSortUnroll];
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q) {
+      const int i = m + q * kSortThreads + t;
+      kk[q] = ib[min(i, n - 1)];                 // unconditional: loads in flight together
+    }
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q) {
+      const int i = m + q * kSortThreads + t;
+      const uint32_t key = (unsigned)kk[q] < (unsigned)K ? (uint32_t)kk[q] : (uint32_t)K;
+      if (i < n) src[i] = key << kLocalBits | (uint32_t)i;
+    }
+  }
+  __syncthreads();
+  const int passes = (kbits + 7) / 8;
+  const int db = (kbits + passes - 1) / passes;
+  for (int q = 0; q < passes; ++q) {
+    lds_stable_pass(src, dst, n, kLocalBits + q * db, min(db, kbits - q * db), hist, wtot);
+    uint32_t* tmp = src;
+    src = dst;
+    dst = tmp;
+  }
+  // src: sorted words; dst: free. Segment starts write their base minus their
+  // position into dst; then every position takes the base of its segment.
+  const int32_t* hr = H + ((int64_t)b * G + g) * K;
+  const int32_t* ob = offsets + (int64_t)b * (K + 1);
+  constexpr int EMAX = kStableChunk / kSortThreads;
+  const int E = (n + kSortThreads - 1) / kSortThreads;
+  const int q0 = min(t * E, n), q1 = min(q0 + E, n);
+  int last = -1;
+  uint32_t sk[EMAX];
+  int sb[EMAX];
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {               // segment starts of my range
+    const int p = q0 + j;
+    const uint32_t key = p < q1 ? src[p] >> kLocalBits : (uint32_t)K;
+    const bool st = p < q1 && (p == 0 || key != (src[p - 1] >> kLocalBits));
+    sk[j] = st && key < (uint32_t)K ? key : (uint32_t)K;
+    last = st ? p : last;
+  }
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {               // their bases, every load in flight
+    const uint32_t kc = min(sk[j], (uint32_t)(K - 1));
+    sb[j] = ob[kc] + hr[kc];
+  }
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {
+    const int p = q0 + j;
+    const bool st = p < q1 && (p == 0 || (src[p] >> kLocalBits) != (src[p - 1] >> kLocalBits));
+    if (st) dst[p] = (uint32_t)(sb[j] - p);
+  }
+  const int carry = block_exclusive_max(last, wtot);   // barrier inside: dst complete
+  int cur = (q0 < q1 && carry >= 0) ? (int)dst[carry] : 0;
+  __syncthreads();                               // every carried base read before overwrites
+  for (int p = q0; p < q1; ++p) {
+    const uint32_t key = src[p] >> kLocalBits;
+    if (p == 0 || key != (src[p - 1] >> kLocalBits)) cur = (int)dst[p];
+    dst[p] = (uint32_t)(cur + p);
+  }
+  __syncthreads();
+  int32_t* pb = perm + (int64_t)b * N;
+  for (int p = t; p < n; p += kSortThreads) {
+    const uint32_t w = src[p];
+    if ((w >> kLocalBits) < (uint32_t)K) pb[dst[p]] = n0 + (int)(w & (kStableChunk - 1));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LSD radix passes over a whole problem (chunks too large for LDS, or large
+// K): pass q sorts stably by bits [8q, 8q + 8) of the key, so after the last
+// pass the order is by key and, within a key, by point index. Each pass is a
+// counting sort over chunks of kRadixChunk positions:
+//   radix_hist     block (b, g): counts of each digit in chunk g -> rhist row
+//                  g, also added (integer atomics) to its group of
+//                  kRadixRows chunks' column sums
+//   radix_scan     per problem: digit starts (exclusive prefix of the digit
+//                  totals) plus the column sums of earlier chunk groups ->
+//                  each group's first output position per digit
+//   radix_scatter  block (b, g): its chunk's start per digit (its group's
+//                  start plus the earlier chunks of the group), then
+//                  sub-chunks of kRadixSub keys staged in LDS; wave w walks
+//                  its own consecutive range in steps of 64, and a key's
+//                  position is its digit's running start plus the same-digit
+//                  keys of earlier waves, earlier steps and lower lanes.
+//                  Writes the key and the point index, or after the last pass
+//                  only the point index, into perm.
+// Keys outside [0, K) are taken as K: they sort after every real key.
+constexpr int kRadix = 256;
+constexpr int kRadixChunk = 16384;
+constexpr int kRadixSub = 4096;
+constexpr int kRadixRows = 64;
+
+__device__ __forceinline__ uint32_t radix_key(int32_t k, int K) {
+  return (unsigned)k < (unsigned)K ? (uint32_t)k : (uint32_t)K;
+}
+
+__global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
+    const int32_t* __restrict__ keys, int32_t* __restrict__ rhist, int32_t* __restrict__ colsum,
+    int N, int K, int G, int RG, int shift) {
+  __shared__ int32_t h[kWavesSort][kRadix];       // one histogram per wave
+  const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
+  const int w = t >> 6;
+  for (int r = t; r < kWavesSort * kRadix; r += kSortThreads) (&h[0][0])[r] = 0;
+  __syncthreads();
+  const int n0 = g * kRadixChunk, n1 = min(n0 + kRadixChunk, N);
+  const int32_t* kb = keys + (int64_t)b * N;
+  for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
+    uint32_t dg[kSortUnroll];
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q) {
+      const int i = m + q * kSortThreads + t;
+      const uint32_t kv = radix_key(kb[min(i, n1 - 1)], K);   // unconditional: loads in flight together
+      dg[q] = i < n1 ? (kv >> shift) & (kRadix - 1) : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int q = 0; q < kSortUnroll; ++q)
+      if (dg[q] != 0xFFFFFFFFu) atomicAdd(&h[w][dg[q]], 1);
+  }
+  __syncthreads();
+  int32_t* row = rhist + ((int64_t)b * G + g) * kRadix;
+  int32_t* cs = colsum + ((int64_t)b * RG + g / kRadixRows) * kRadix;
+  for (int r = t; r < kRadix; r += kSortThreads) {
+    int c = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWavesSort; ++ww) c += h[ww][r];
+    row[r] = c;
+    if (c) atomicAdd(&cs[r], c);
+  }
+}
+
+// One block per problem: rgbase[b][rg][r] = (keys with a smaller digit) +
+// (keys with digit r in chunk groups before rg).
+__global__ __launch_bounds__(kSortThreads) void radix_scan_kernel(const int32_t* __restrict__ colsum,
+                                                                  int32_t* __restrict__ rgbase,
+                                                                  int RG) {
+  __shared__ int32_t wtot[kWavesSort];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int32_t* cs = colsum + (int64_t)b * RG * kRadix;
+  int tot = 0;
+  if (t < kRadix)
+    for (int rg = 0; rg < RG; ++rg) tot += cs[(int64_t)rg * kRadix + t];
+  int all;
+  int run = block_exclusive_scan(t < kRadix ? tot : 0, wtot, all);
+  if (t >= kRadix) return;
+  int32_t* out = rgbase + (int64_t)b * RG * kRadix;
+  for (int rg = 0; rg < RG; ++rg) {
+    const int c = cs[(int64_t)rg * kRadix + t];
+    out[(int64_t)rg * kRadix + t] = run;
+    run += c;
+  }
+}
+
+// keys_in null: the keys are the ids themselves and the point index is the
+// position (first pass). keys_out null: last pass, only the index goes out.
+// Each sub-chunk is reordered by digit in LDS first (the second walk keeps
+// its keys in registers, then stores them at their local sorted places), so
+// the global stores go out as runs of consecutive addresses, one run per
+// digit.
+__global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ keys_in,
+    const int32_t* __restrict__ idx_in, const int32_t* __restrict__ rhist,
+    const int32_t* __restrict__ rgbase, int32_t* __restrict__ keys_out,
+    int32_t* __restrict__ idx_out, int N, int K, int G, int RG, int shift) {
+  __shared__ int32_t skey[kRadixSub];
+  __shared__ int32_t sidx[kRadixSub];
+  __shared__ int32_t hist[kRadix * kWavesSort];
+  __shared__ int32_t carry[kRadix];              // next global position of each digit
+  __shared__ int32_t gbase[kRadix];              // global position minus local position
+  __shared__ int32_t wtot[kWavesSort];
+  constexpr int QS = kSortThreads / kRadix;      // row quarters for the chunk start
+  constexpr int SPW = kRadixSub / kSortThreads;  // steps of 64 per wave per sub-chunk
+  static_assert(kRadixRows % QS == 0, "rows per quarter");
+  const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int32_t* kb = (keys_in ? keys_in : ids) + (int64_t)b * N;
+  const int32_t* xb = idx_in ? idx_in + (int64_t)b * N : nullptr;
+  // chunk start per digit: its group's start plus the group's earlier chunks
+  {
+    const int r = t % kRadix, q = t / kRadix;
+    const int gs = g / kRadixRows * kRadixRows;
+    const int a0 = gs + q * (kRadixRows / QS), a1 = min(a0 + kRadixRows / QS, g);
+    const int32_t* hr = rhist + (int64_t)b * G * kRadix;
+    int v[kRadixRows / QS];
+#pragma unroll
+    for (int j = 0; j < kRadixRows / QS; ++j)   // unconditional: loads in flight together
+      v[j] = hr[(int64_t)min(a0 + j, G - 1) * kRadix + r];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kRadixRows / QS; ++j) sum += a0 + j < a1 ? v[j] : 0;
+    hist[q * kRadix + r] = sum;
+  }
+  __syncthreads();
+  if (t < kRadix) {
+    int c = rgbase[((int64_t)b * RG + g / kRadixRows) * kRadix + t];
+#pragma unroll
+    for (int q = 0; q < QS; ++q) c += hist[q * kRadix + t];
+    carry[t] = c;
+  }
+  __syncthreads();
+  int32_t* ko = keys_out ? keys_out + (int64_t)b * N : nullptr;
+  int32_t* xo = idx_out + (int64_t)b * N;
+  const int n0 = g * kRadixChunk, n1 = min(n0 + kRadixChunk, N);
+  for (int m0 = n0; m0 < n1; m0 += kRadixSub) {
+    const int m = min(kRadixSub, n1 - m0);
+    int kk[SPW], xx[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {               // unconditional: loads in flight together
+      const int i = min(m0 + j * kSortThreads + t, n1 - 1);
+      kk[j] = kb[i];
+      xx[j] = xb ? xb[i] : i;
+    }
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int l = j * kSortThreads + t;
+      skey[l] = (int32_t)radix_key(kk[j], K);
+      sidx[l] = xx[j];
+    }
+    for (int r = lane; r < kRadix; r += 64) hist[w * kRadix + r] = 0;
+    __syncthreads();
+    const int per = wave_span(m);
+    const int s0 = min(w * per, m), s1 = min(s0 + per, m);
+    for (int i = s0 + lane; i < s1; i += 64)
+      atomicAdd(&hist[w * kRadix + (((uint32_t)skey[i] >> shift) & (kRadix - 1))], 1);
+    __syncthreads();
+    // local start of each (digit, wave): digits in order, waves in order
+    int hv[kWavesSort];
+    int tot = 0;
+    if (t < kRadix) {
+#pragma unroll
+      for (int ww = 0; ww < kWavesSort; ++ww) hv[ww] = hist[ww * kRadix + t];
+#pragma unroll
+      for (int ww = 0; ww < kWavesSort; ++ww) tot += hv[ww];
+    }
+    int all;
+    const int lstart = block_exclusive_scan(t < kRadix ? tot : 0, wtot, all);
+    if (t < kRadix) {
+      int run = lstart;
+#pragma unroll
+      for (int ww = 0; ww < kWavesSort; ++ww) {
+        hist[ww * kRadix + t] = run;
+        run += hv[ww];
+      }
+      gbase[t] = carry[t] - lstart;
+      carry[t] += tot;
+    }
+    __syncthreads();
+    // local sorted place of each key, kept in registers until every wave has
+    // read its keys
+    int lp[SPW], lk[SPW], lx[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int i = s0 + j * 64 + lane;
+      lp[j] = -1;
+      lk[j] = lx[j] = 0;
+      if (i < s1) {
+        const uint32_t key = (uint32_t)skey[i];
+        lp[j] = atomicAdd(&hist[w * kRadix + ((key >> shift) & (kRadix - 1))], 1);
+        lk[j] = (int)key;
+        lx[j] = sidx[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      if (lp[j] >= 0) {
+        skey[lp[j]] = lk[j];
+        sidx[lp[j]] = lx[j];
+      }
+    }
+    __syncthreads();
+    for (int l = t; l < m; l += kSortThreads) {
+      const int key = skey[l];
+      const int pos = gbase[((uint32_t)key >> shift) & (kRadix - 1)] + l;
+      if (ko) ko[pos] = key;
+      xo[pos] = sidx[l];
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -374,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
 }
 
 // scan: one block per problem; offsets = exclusive prefix sum of counts,
-// cursor = offsets.
+// cursor = offsets (cursor null: not needed).
 __global__ __launch_bounds__(kSortThreads) void scan_kernel(const int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ cursor, int K) {
@@ -389,22 +789,23 @@ __global__ __launch_bounds__(kSortThreads) void scan_kernel(const int32_t* __res
   int total;
   int run = block_exclusive_scan(s, wtot, total);
   int32_t* ob = offsets + (int64_t)b * (K + 1);
-  int32_t* kb = cursor + (int64_t)b * K;
+  int32_t* kb = cursor ? cursor + (int64_t)b * K : nullptr;
   for (int64_t i = lo; i < hi; ++i) {
     ob[i] = run;
-    kb[i] = run;
+    if (kb) kb[i] = run;
     run += cb[i];
   }
   if (t == 0) ob[K] = total;
 }
 
-// prep: one wave per cluster marks the runs that start inside it and zeroes
-// the sums row of a long cluster; runs past the last position get K.
+// prep: one wave per cluster marks the runs that start inside it; runs past
+// the last position get K; the long-cluster flag is set (finalize checks
+// every cluster).
 __global__ __launch_bounds__(kThreads) void prep_kernel(const int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ run_first,
-                                                        float* __restrict__ sums,
-                                                        int32_t* __restrict__ has_long, int K,
-                                                        int d, int runs, int blocks_per_batch) {
+                                                        int32_t* __restrict__ has_long,
+                                                        int K, int runs,
+                                                        int blocks_per_batch) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int b = blockIdx.x / blocks_per_batch;
   const int j = blockIdx.x % blocks_per_batch;
@@ -417,10 +818,6 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const int32_t* __restric
     if (hi <= lo) continue;
     for (int64_t r = (lo + (int64_t)kSegRun - 1) / kSegRun + lane; r * kSegRun < hi; r += 64)
       rf[r] = k;
-    if (sums && is_long(lo, hi)) {
-      float* row = sums + ((int64_t)b * K + k) * d;
-      for (int i = lane; i < d; i += 64) row[i] = 0.f;
-    }
   }
   const int64_t r0 = (total + (int64_t)kSegRun - 1) / kSegRun;
   for (int64_t r = r0 + (int64_t)j * kThreads + threadIdx.x; r < runs;
@@ -489,7 +886,9 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const int32_t* __rest
 // segment's rows are added under a 0/1 position weight; when a segment ends,
 // the R row groups are summed across lanes and the sum goes out: divided by
 // the count into the cluster's row of c for a short segment (the finished
-// mean), added with atomics to its sums row for a piece of a long one.
+// mean), stored to the run's slot for a piece of a long one (see
+// LongPieces), or, when accumulating over chunks of points, added with
+// atomics to its sums row.
 template <int DT>
 __device__ __forceinline__ void widen16(const uint4 v, float* out) {
   if constexpr (DT == FK_F32) {
@@ -545,7 +944,8 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
     const void* __restrict__ x, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ run_first,
     float* __restrict__ sums, float* __restrict__ c, float* __restrict__ part, int part_stride,
-    int N, int d, int K, int runs, int slices, int64_t total_waves, bool acc_all) {
+    float* __restrict__ pieces, int N, int d, int K, int runs, int slices, int64_t total_waves,
+    bool acc_all) {
   constexpr int R = 64 / LPR;                    // rows per wave instruction
   constexpr int EB = DT == FK_F32 ? 4 : 2;
   constexpr int EV = 16 / EB;                    // elements per 16-byte vector
@@ -569,8 +969,9 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   const bool colok = col < d;
   const int32_t* ob = offsets + (int64_t)b * (K + 1);
   const char* xb = reinterpret_cast<const char*>(x) + (int64_t)b * N * d * EB;
-  float* sb = sums + (int64_t)b * K * d;
-  float* cb = c + (int64_t)b * K * d;
+  float* sb = acc_all ? sums + (int64_t)b * K * d : nullptr;
+  float* cb = acc_all ? nullptr : c + (int64_t)b * K * d;
+  float* pr = acc_all ? nullptr : pieces + ((int64_t)b * runs + run) * 2 * d;   // this run's slots
   float moved = 0.f;                             // squared moves of this wave's short clusters
   [&]() {
 
@@ -622,8 +1023,8 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   if (nseg == 0) return;
   // first row: a long piece starts at max(lo, p0), a short segment at lo
   const int c0 = __builtin_amdgcn_readlane(sc, 0);
-  const int s = c0 < 0 ? max(off(__builtin_amdgcn_readlane(sk, 0)), p0)
-                       : __builtin_amdgcn_readlane(se, 0) - c0;
+  const int lo0 = off(__builtin_amdgcn_readlane(sk, 0));
+  const int s = c0 < 0 ? max(lo0, p0) : __builtin_amdgcn_readlane(se, 0) - c0;
   // last row + 1: the end of the last owned segment
   int E = __builtin_amdgcn_readlane(se, nseg - 1);
   for (int kk = knext; kk < K; ++kk) {           // only with more than 64 segments
@@ -642,6 +1043,9 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   int jend = __builtin_amdgcn_readlane(se, 0);
   int jcnt = __builtin_amdgcn_readlane(sc, 0);
   int jstart = s;
+  // the current piece is the run's head piece (slot 0): a long segment that
+  // started before the run; any later long piece starts inside it (slot 1)
+  bool jhead = c0 < 0 && lo0 < p0;
   float acc[EV];
 #pragma unroll
   for (int i = 0; i < EV; ++i) acc[i] = 0.f;
@@ -708,11 +1112,22 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
             }
           }
         }
-      } else {                                   // a piece of a long segment, or any
-        float* row = sb + (int64_t)jk * d + col;   // segment when accumulating
+      } else if (acc_all) {                      // accumulating: every segment into sums
+        float* row = sb + (int64_t)jk * d + col;
 #pragma unroll
         for (int i = 0; i < EV; ++i)
           if (col + i < d) unsafeAtomicAdd(row + i, acc[i]);
+      } else {                                   // a piece of a long segment: its slot
+        float* row = pr + (jhead ? 0 : d) + col;
+        if constexpr (VEC) {                     // d % 4 == 0: 16-byte aligned slots
+#pragma unroll
+          for (int i = 0; i < EV; i += 4)
+            *reinterpret_cast<float4*>(row + i) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < EV; ++i)
+            if (col + i < d) row[i] = acc[i];
+        }
       }
     }
 #pragma unroll
@@ -741,6 +1156,7 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
         si = 0;
       }
       jstart = jend;
+      jhead = false;
       jk = __builtin_amdgcn_readlane(sk, si);
       jend = __builtin_amdgcn_readlane(se, si);
       jcnt = __builtin_amdgcn_readlane(sc, si);
@@ -767,19 +1183,56 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   }
 }
 
+// Q1 and Q2 rows of the long pieces (see LongPieces), once segreduce has
+// stored them. q1blocks: block (b, j) sums the slot-0 pieces of runs
+// 32j .. 32j+31 in run order into Q1 row j; q2blocks: block (b, i) sums Q1
+// rows 32i .. 32i+31 in order into Q2 row i. Only full blocks are formed;
+// problems without long clusters do nothing. Kernels of their own: their
+// start sees every piece, with no device-wide fence.
+__global__ __launch_bounds__(kThreads) void q1blocks_kernel(LongPieces lp, float* __restrict__ q1,
+                                                            const int32_t* __restrict__ has_long,
+                                                            int d) {
+  const int b = blockIdx.x / lp.nq1, j = blockIdx.x % lp.nq1;
+  if (!has_long[b] || (j + 1) * kQ1 > lp.runs) return;
+  const float* pb = lp.pieces + (int64_t)b * lp.runs * 2 * d;
+  float* out = q1 + ((int64_t)b * lp.nq1 + j) * d;
+  for (int c = threadIdx.x; c < d; c += kThreads) {
+    float t = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < kQ1; ++r) t += pb[((int64_t)(j * kQ1 + r) * 2) * d + c];
+    out[c] = t;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void q2blocks_kernel(LongPieces lp, const float* __restrict__ q1,
+                                                            float* __restrict__ q2,
+                                                            const int32_t* __restrict__ has_long,
+                                                            int d) {
+  const int b = blockIdx.x / lp.nq2, i = blockIdx.x % lp.nq2;
+  if (!has_long[b] || (i + 1) * kQ1 * kQ2 > lp.runs) return;
+  const float* qb = q1 + (int64_t)b * lp.nq1 * d;
+  float* out = q2 + ((int64_t)b * lp.nq2 + i) * d;
+  for (int c = threadIdx.x; c < d; c += kThreads) {
+    float t = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < kQ2; ++r) t += qb[(int64_t)(i * kQ2 + r) * d + c];
+    out[c] = t;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // finalize, one thread per group of kFinVec consecutive elements of a
-// problem's (K, d) centroid block: a non-empty cluster takes its new value
-// from its sums row (already the mean for a short segment; divided by the
-// count for a long one), and the block's squared moves go to its partial.
-// Empty clusters keep their centroid.
+// problem's (K, d) centroid block: a long cluster's new value is the sum of
+// its pieces (fixed order, LongPieces) divided by its count, and the block's
+// squared moves go to its partial. Short clusters were finished by segreduce;
+// empty clusters keep their centroid.
 constexpr int kFinVec = 4;
 
 template <bool SHIFT>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(
-    const float* __restrict__ sums, const int32_t* __restrict__ offsets, float* __restrict__ c,
+    LongPieces lp, const int32_t* __restrict__ offsets, float* __restrict__ c,
     float* __restrict__ part, int part_stride, const int32_t* __restrict__ has_long, int d, int K,
-    int blocks_per_batch, bool vec) {
+    int blocks_per_batch) {
   __shared__ float wsum[kThreads / 64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -791,43 +1244,18 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
   const int64_t per = (int64_t)K * d;
   const int64_t e0 = ((int64_t)j * kThreads + threadIdx.x) * kFinVec;
   const int32_t* ob = offsets + (int64_t)b * (K + 1);
-  const float* sb = sums + (int64_t)b * per;
   float* cb = c + (int64_t)b * per;
   float moved = 0.f;
-  if (e0 < per) {
-    if (vec && e0 + kFinVec <= per) {         // vec: d % kFinVec == 0, c 16-byte aligned
-      const int k = (int)(e0 / d);               // the kFinVec elements share a row
-      const int lo = ob[k], hi = ob[k + 1];
-      if (is_long(lo, hi)) {
-        const float4 sv = *reinterpret_cast<const float4*>(sb + e0);
-        const float cnt = (float)(hi - lo);
-        float nw[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nw[i] = nw[i] / cnt;
-        if constexpr (SHIFT) {
-          const float4 cv = *reinterpret_cast<const float4*>(cb + e0);
-          const float od[4] = {cv.x, cv.y, cv.z, cv.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float dl = nw[i] - od[i];
-            moved = fmaf(dl, dl, moved);
-          }
-        }
-        *reinterpret_cast<float4*>(cb + e0) = make_float4(nw[0], nw[1], nw[2], nw[3]);
-      }
-    } else {
-      for (int64_t e = e0; e < e0 + kFinVec && e < per; ++e) {
-        const int k = (int)(e / d);
-        const int lo = ob[k], hi = ob[k + 1];
-        if (!is_long(lo, hi)) continue;
-        const float nw = sb[e] / (float)(hi - lo);
-        if constexpr (SHIFT) {
-          const float dl = nw - cb[e];
-          moved = fmaf(dl, dl, moved);
-        }
-        cb[e] = nw;
-      }
+  for (int64_t e = e0; e < e0 + kFinVec && e < per; ++e) {
+    const int k = (int)(e / d);
+    const int lo = ob[k], hi = ob[k + 1];
+    if (!is_long(lo, hi)) continue;
+    const float nw = long_sum(lp, b, d, lo, hi, e - (int64_t)k * d) / (float)(hi - lo);
+    if constexpr (SHIFT) {
+      const float dl = nw - cb[e];
+      moved = fmaf(dl, dl, moved);
     }
+    cb[e] = nw;
   }
   if constexpr (SHIFT) {
     moved = wave_sum(moved);
@@ -987,15 +1415,16 @@ hipError_t run_segreduce(const void* x, const UpdateWs& ws, int64_t B, int64_t N
   const int64_t grid = (total + 3) / 4;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   // vector path: 16-byte x rows and 16-byte-aligned rows of c
-  const bool vec = (d * EB) % 16 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)c % 16) == 0;
+  const float* cc = acc_all ? sums : c;
+  const bool vec = (d * EB) % 16 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)cc % 16) == 0;
   if (vec)
     segreduce_kernel<DT, LPR, true><<<(unsigned)grid, kThreads, 0, s>>>(
-        x, ws.perm, ws.offsets, ws.run_first, sums, c, part, part_stride, (int)N, (int)d,
-        (int)K, runs, slices, total, acc_all);
+        x, ws.perm, ws.offsets, ws.run_first, sums, c, part, part_stride, ws.pieces, (int)N,
+        (int)d, (int)K, runs, slices, total, acc_all);
   else
     segreduce_kernel<DT, LPR, false><<<(unsigned)grid, kThreads, 0, s>>>(
-        x, ws.perm, ws.offsets, ws.run_first, sums, c, part, part_stride, (int)N, (int)d,
-        (int)K, runs, slices, total, acc_all);
+        x, ws.perm, ws.offsets, ws.run_first, sums, c, part, part_stride, ws.pieces, (int)N,
+        (int)d, (int)K, runs, slices, total, acc_all);
   return hipGetLastError();
 }
 
@@ -1025,12 +1454,16 @@ hipError_t segreduce_any(const void* x, int dt, const UpdateWs& ws, int64_t B, i
   return segreduce_dt<FK_F32>(x, ws, B, N, d, K, sums, c, part, part_stride, acc_all, s);
 }
 
+// column slices of a segreduce row (fp32 rows have the most)
+int seg_slices(int dt, int64_t d) {
+  if (dt == FK_F16) return seg_slices_dt<FK_F16>(d);
+  if (dt == FK_BF16) return seg_slices_dt<FK_BF16>(d);
+  return seg_slices_dt<FK_F32>(d);
+}
+
 // segreduce waves per problem (one per run and column slice)
 int64_t seg_waves(int dt, int64_t N, int64_t d) {
-  const int64_t runs = (N + kSegRun - 1) / kSegRun;
-  if (dt == FK_F16) return runs * seg_slices_dt<FK_F16>(d);
-  if (dt == FK_BF16) return runs * seg_slices_dt<FK_BF16>(d);
-  return runs * seg_slices_dt<FK_F32>(d);
+  return (N + kSegRun - 1) / kSegRun * seg_slices(dt, d);
 }
 
 }  // namespace
@@ -1054,52 +1487,169 @@ int64_t fin_blocks(int64_t K, int64_t d) {
   return (K * d + (int64_t)kThreads * kFinVec - 1) / ((int64_t)kThreads * kFinVec);
 }
 
+// How perm is built: in LDS per chunk of the split sort (chunks of at most
+// kStableChunk ids), by radix passes over the whole problem (K <= 2^16), or
+// by the atomic-cursor scatter (larger K).
+enum PermPath { kPermDirect, kPermStable, kPermRadix, kPermAtomic };
+
+// FK_FORCE_RADIX=1 (a test hook) takes the radix passes whenever K allows.
+bool force_radix() {
+  const char* v = getenv("FK_FORCE_RADIX");
+  return v && v[0] == '1';
+}
+
+PermPath perm_path(int64_t B, int64_t N, int64_t K) {
+  const int G = split_groups(B, N, K);
+  if (G > 0 && (N + G - 1) / G <= kStableChunk && !(force_radix() && K <= 65536))
+    return key_bits(K) <= kDirectKeyBits && direct_lds_bytes((N + G - 1) / G, K) <= kStableLdsMax
+               ? kPermDirect
+               : kPermStable;
+  if (K <= 65536) return kPermRadix;
+  return kPermAtomic;
+}
+
+int radix_passes(int64_t K) { return (key_bits(K) + 7) / 8; }
+
+// Radix chunks per problem and their groups.
+int64_t radix_chunks(int64_t N) { return N > 0 ? (N + kRadixChunk - 1) / kRadixChunk : 1; }
+int64_t radix_rgroups(int64_t N) { return (radix_chunks(N) + kRadixRows - 1) / kRadixRows; }
+
+struct WsLayout {
+  int64_t runs, nq1, nq2, slices, G, GR, RG;
+  bool radix, two_sets, cursor;
+};
+
+WsLayout ws_layout(int64_t B, int64_t N, int64_t d, int64_t K) {
+  WsLayout L;
+  L.runs = (N + kSegRun - 1) / kSegRun;
+  L.nq1 = (L.runs + kQ1 - 1) / kQ1;
+  L.nq2 = (L.nq1 + kQ2 - 1) / kQ2;
+  L.slices = seg_slices(FK_F32, d);              // the most of any element type
+  L.G = split_groups(B, N, K);
+  const PermPath pp = perm_path(B, N, K);
+  L.radix = pp == kPermRadix;
+  L.two_sets = L.radix && radix_passes(K) > 2;
+  L.cursor = pp == kPermAtomic;
+  L.GR = L.radix ? radix_chunks(N) : 0;
+  L.RG = L.radix ? radix_rgroups(N) : 0;
+  return L;
+}
+
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K) {
-  const int64_t runs = (N + kSegRun - 1) / kSegRun;
-  return align256((size_t)B * K * d * 4) + align256((size_t)B * (K + 1) * 4) +
-         align256((size_t)B * K * 4) + align256((size_t)B * N * 4) +
-         align256((size_t)B * runs * 4) +
-         align256((size_t)B * (seg_waves(FK_F32, N, d) + fin_blocks(K, d)) * 4) +
-         align256((size_t)B * split_groups(B, N, K) * K * 4) + align256((size_t)B * 4);
+  const WsLayout L = ws_layout(B, N, d, K);
+  size_t n = align256((size_t)B * L.runs * 2 * d * 4) + align256((size_t)B * L.nq1 * d * 4) +
+             align256((size_t)B * L.nq2 * d * 4) +
+             align256((size_t)B * (K + 1) * 4) + align256((size_t)B * N * 4) +
+             align256((size_t)B * L.runs * 4) +
+             align256((size_t)B * (seg_waves(FK_F32, N, d) + fin_blocks(K, d)) * 4) +
+             align256((size_t)B * L.G * K * 4) + align256((size_t)B * 4);
+  if (L.radix)
+    n += (L.two_sets ? 4 : 2) * align256((size_t)B * N * 4) +
+         align256((size_t)B * L.GR * kRadix * 4) +
+         align256((size_t)radix_passes(K) * B * L.RG * kRadix * 4) +
+         align256((size_t)B * L.RG * kRadix * 4);
+  if (L.cursor) n += align256((size_t)B * K * 4);
+  return n;
 }
 
 UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K) {
-  const int64_t runs = (N + kSegRun - 1) / kSegRun;
+  const WsLayout L = ws_layout(B, N, d, K);
   char* p = static_cast<char*>(base);
   UpdateWs w;
-  w.sums = reinterpret_cast<float*>(p);
-  p += align256((size_t)B * K * d * 4);
-  w.offsets = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)B * (K + 1) * 4);
-  w.cursor = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)B * K * 4);
-  w.perm = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)B * N * 4);
-  w.run_first = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)B * runs * 4);
-  w.part = reinterpret_cast<float*>(p);
-  p += align256((size_t)B * (seg_waves(FK_F32, N, d) + fin_blocks(K, d)) * 4);
-  w.hist = reinterpret_cast<int32_t*>(p);
-  p += align256((size_t)B * split_groups(B, N, K) * K * 4);
-  w.has_long = reinterpret_cast<int32_t*>(p);
+  auto take = [&](size_t bytes) {
+    char* q = p;
+    p += align256(bytes);
+    return q;
+  };
+  w.pieces = reinterpret_cast<float*>(take((size_t)B * L.runs * 2 * d * 4));
+  w.q1 = reinterpret_cast<float*>(take((size_t)B * L.nq1 * d * 4));
+  w.q2 = reinterpret_cast<float*>(take((size_t)B * L.nq2 * d * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((size_t)B * (K + 1) * 4));
+  w.perm = reinterpret_cast<int32_t*>(take((size_t)B * N * 4));
+  w.run_first = reinterpret_cast<int32_t*>(take((size_t)B * L.runs * 4));
+  w.part = reinterpret_cast<float*>(take((size_t)B * (seg_waves(FK_F32, N, d) + fin_blocks(K, d)) * 4));
+  w.hist = reinterpret_cast<int32_t*>(take((size_t)B * L.G * K * 4));
+  w.has_long = reinterpret_cast<int32_t*>(take((size_t)B * 4));
+  w.rkeys[0] = w.rkeys[1] = nullptr;
+  w.ridx[0] = w.ridx[1] = nullptr;
+  w.rhist = w.rcolsum = w.rgbase = nullptr;
+  w.cursor = nullptr;
+  if (L.radix) {
+    w.rkeys[0] = reinterpret_cast<int32_t*>(take((size_t)B * N * 4));
+    w.ridx[0] = reinterpret_cast<int32_t*>(take((size_t)B * N * 4));
+    if (L.two_sets) {
+      w.rkeys[1] = reinterpret_cast<int32_t*>(take((size_t)B * N * 4));
+      w.ridx[1] = reinterpret_cast<int32_t*>(take((size_t)B * N * 4));
+    }
+    w.rhist = reinterpret_cast<int32_t*>(take((size_t)B * L.GR * kRadix * 4));
+    w.rcolsum = reinterpret_cast<int32_t*>(take((size_t)radix_passes(K) * B * L.RG * kRadix * 4));
+    w.rgbase = reinterpret_cast<int32_t*>(take((size_t)B * L.RG * kRadix * 4));
+  }
+  if (L.cursor) w.cursor = reinterpret_cast<int32_t*>(take((size_t)B * K * 4));
+  w.runs = (int)L.runs;
+  w.nq1 = (int)L.nq1;
+  w.nq2 = (int)L.nq2;
   return w;
 }
 
+LongPieces long_pieces(const UpdateWs& ws) {
+  LongPieces lp;
+  lp.pieces = ws.pieces;
+  lp.q1 = ws.q1;
+  lp.q2 = ws.q2;
+  lp.runs = ws.runs;
+  lp.nq1 = ws.nq1;
+  lp.nq2 = ws.nq2;
+  return lp;
+}
+
+// perm by LSD radix passes (8 key bits each) over whole problems.
+hipError_t run_radix(const int32_t* ids, int64_t B, int64_t N, int64_t K, const UpdateWs& ws,
+                     hipStream_t s) {
+  const int64_t G = radix_chunks(N), RG = radix_rgroups(N);
+  const int passes = radix_passes(K);
+  if (B * G > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const int64_t ncs = passes * B * RG * kRadix;
+  int64_t zg = (ncs + kThreads - 1) / kThreads;
+  zg = zg < 1 ? 1 : (zg > 4096 ? 4096 : zg);
+  zero_kernel<<<(unsigned)zg, kThreads, 0, s>>>(ws.rcolsum, ncs);
+  FK_CHECK(hipGetLastError());
+  const int32_t* kin = nullptr;
+  const int32_t* xin = nullptr;
+  for (int q = 0; q < passes; ++q) {
+    const bool last = q == passes - 1;
+    int32_t* kout = last ? nullptr : ws.rkeys[q & 1];
+    int32_t* xout = last ? ws.perm : ws.ridx[q & 1];
+    int32_t* cs = ws.rcolsum + (int64_t)q * B * RG * kRadix;
+    radix_hist_kernel<<<(unsigned)(B * G), kSortThreads, 0, s>>>(kin ? kin : ids, ws.rhist, cs,
+                                                                (int)N, (int)K, (int)G, (int)RG,
+                                                                8 * q);
+    FK_CHECK(hipGetLastError());
+    radix_scan_kernel<<<(unsigned)B, kSortThreads, 0, s>>>(cs, ws.rgbase, (int)RG);
+    FK_CHECK(hipGetLastError());
+    radix_scatter_kernel<<<(unsigned)(B * G), kSortThreads, 0, s>>>(
+        ids, kin, xin, ws.rhist, ws.rgbase, kout, xout, (int)N, (int)K, (int)G, (int)RG, 8 * q);
+    FK_CHECK(hipGetLastError());
+    kin = kout;
+    xin = xout;
+  }
+  return hipSuccess;
+}
+
 // Counting sort of a batch's ids into per-cluster segments: counts, offsets,
-// run starts, perm. zsums: the sums rows of long clusters are zeroed there
-// (null: left alone).
-hipError_t run_sort(const int32_t* ids, int64_t B, int64_t N, int64_t d, int64_t K,
-                    int32_t* counts, float* zsums, const UpdateWs& ws, hipStream_t s) {
+// run starts, the long-cluster flag, perm.
+hipError_t run_sort(const int32_t* ids, int dt, int64_t B, int64_t N, int64_t d, int64_t K,
+                    int32_t* counts, const UpdateWs& ws, hipStream_t s) {
   const int runs = (int)((N + kSegRun - 1) / kSegRun);
   const int G = split_groups(B, N, K);
+  const PermPath pp = perm_path(B, N, K);
   if (G > 0) {
     const int chunk = (int)((N + G - 1) / G);
     const size_t lds = (size_t)K * sizeof(int32_t);            // bins
     const size_t lds1 = (size_t)(K + 1) * sizeof(int32_t);     // offsets + total
     static bool attr = false;
     if (!attr && lds1 > 65536) {
-      for (const void* f : {(const void*)hist2_kernel, (const void*)offsets_kernel,
-                            (const void*)scatter2_kernel})
+      for (const void* f : {(const void*)hist2_kernel, (const void*)offsets_kernel})
         (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (kMaxLdsBins + 64) * sizeof(int32_t));
       (void)hipGetLastError();
@@ -1110,8 +1660,8 @@ hipError_t run_sort(const int32_t* ids, int64_t B, int64_t N, int64_t d, int64_t
     FK_CHECK(hipGetLastError());
     if ((int64_t)G * K <= kFusedOffsetsMax) {
       offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
-                                                            ws.run_first, zsums, ws.has_long,
-                                                            (int)K, (int)d, G, runs);
+                                                            ws.run_first, ws.has_long, (int)K,
+                                                            G, runs);
       FK_CHECK(hipGetLastError());
     } else {
       const int kblocks = (int)((K + kThreads - 1) / kThreads);
@@ -1119,47 +1669,60 @@ hipError_t run_sort(const int32_t* ids, int64_t B, int64_t N, int64_t d, int64_t
                                                                   kblocks);
       FK_CHECK(hipGetLastError());
       offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
-                                                             ws.run_first, zsums, ws.has_long,
-                                                             (int)K, (int)d, 0, runs);
+                                                             ws.run_first, ws.has_long, (int)K,
+                                                             0, runs);
       FK_CHECK(hipGetLastError());
       const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);
-      prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, zsums,
-                                                           ws.has_long, (int)K, (int)d, runs, pb);
+      prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.has_long,
+                                                           (int)K, runs, pb);
       FK_CHECK(hipGetLastError());
     }
-    // the sorted form pays off with enough chunks to fill the chip; with few,
-    // its extra passes cost more than the scattered stores
-    const size_t lds_sorted = (size_t)(2 * K + 2 * (int64_t)chunk) * sizeof(int32_t);
-    if (lds_sorted <= kSortedScatterLds && B * G >= 256) {
+    if (pp == kPermDirect) {
+      const size_t dlds = direct_lds_bytes(chunk, K);
+      static bool dattr = false;
+      if (!dattr) {
+        (void)hipFuncSetAttribute((const void*)scatter_direct_kernel,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kStableLdsMax);
+        (void)hipGetLastError();
+        dattr = true;
+      }
+      scatter_direct_kernel<<<(unsigned)(B * G), kSortThreads, dlds, s>>>(
+          ids, ws.hist, ws.offsets, ws.perm, (int)N, (int)K, G, chunk);
+      FK_CHECK(hipGetLastError());
+      return hipSuccess;
+    }
+    if (pp == kPermStable) {
+      const int kb = key_bits(K);
+      const int passes = (kb + 7) / 8;
+      const int db = (kb + passes - 1) / passes;
+      const size_t slds = (size_t)2 * chunk * 4 + ((size_t)1 << db) * kWavesSort * 4;
       static bool sattr = false;
-      if (!sattr && lds_sorted > 65536) {
-        (void)hipFuncSetAttribute((const void*)scatter2s_kernel,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kSortedScatterLds);
+      if (!sattr) {
+        (void)hipFuncSetAttribute((const void*)scatter_stable_kernel,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kStableLdsMax);
         (void)hipGetLastError();
         sattr = true;
       }
-      scatter2s_kernel<<<(unsigned)(B * G), kSortThreads, lds_sorted, s>>>(
-          ids, ws.hist, ws.offsets, ws.perm, (int)N, (int)K, G, chunk);
-    } else {
-      scatter2_kernel<<<(unsigned)(B * G), kSortThreads, lds, s>>>(
-          ids, ws.hist, ws.offsets, ws.perm, (int)N, (int)K, G, chunk);
+      scatter_stable_kernel<<<(unsigned)(B * G), kSortThreads, slds, s>>>(
+          ids, ws.hist, ws.offsets, ws.perm, (int)N, (int)K, G, chunk, kb);
+      FK_CHECK(hipGetLastError());
+      return hipSuccess;
     }
-    FK_CHECK(hipGetLastError());
-  } else {
-    int64_t g = (B * K + kThreads - 1) / kThreads;
-    g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
-    zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
-    FK_CHECK(hipGetLastError());
-    FK_CHECK(run_hist_scatter<64>(ids, counts, nullptr, nullptr, B, N, K, false, s));
-    scan_kernel<<<(unsigned)B, kSortThreads, 0, s>>>(counts, ws.offsets, ws.cursor, (int)K);
-    FK_CHECK(hipGetLastError());
-    const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);   // blocks per problem
-    prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, zsums,
-                                                         ws.has_long, (int)K, (int)d, runs, pb);
-    FK_CHECK(hipGetLastError());
-    FK_CHECK(run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s));
+    return run_radix(ids, B, N, K, ws, s);
   }
-  return hipSuccess;
+  int64_t g = (B * K + kThreads - 1) / kThreads;
+  g = g < 1 ? 1 : (g > 4096 ? 4096 : g);
+  zero_kernel<<<(unsigned)g, kThreads, 0, s>>>(counts, B * K);
+  FK_CHECK(hipGetLastError());
+  FK_CHECK(run_hist_scatter<64>(ids, counts, nullptr, nullptr, B, N, K, false, s));
+  scan_kernel<<<(unsigned)B, kSortThreads, 0, s>>>(counts, ws.offsets, ws.cursor, (int)K);
+  FK_CHECK(hipGetLastError());
+  const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);   // blocks per problem
+  prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.has_long,
+                                                       (int)K, runs, pb);
+  FK_CHECK(hipGetLastError());
+  if (pp == kPermRadix) return run_radix(ids, B, N, K, ws, s);
+  return run_hist_scatter<64>(ids, nullptr, ws.cursor, ws.perm, B, N, K, true, s);
 }
 
 hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, int64_t N,
@@ -1176,25 +1739,35 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
     return hipGetLastError();
   }
   const int64_t fb = fin_blocks(K, d);
-  FK_CHECK(run_sort(ids, B, N, d, K, counts, ws.sums, ws, s));
+  FK_CHECK(run_sort(ids, dt, B, N, d, K, counts, ws, s));
   // shift partials of a problem: its segreduce waves, then its finalize blocks
   const int64_t sw = seg_waves(dt, N, d);
   const int64_t pstride = sw + fb;
   if (pstride > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   float* spart = shift ? ws.part : nullptr;
-  FK_CHECK(segreduce_any(x, dt, ws, B, N, d, K, ws.sums, c, spart, (int)pstride, false, s));
+  FK_CHECK(segreduce_any(x, dt, ws, B, N, d, K, nullptr, c, spart, (int)pstride, false, s));
   const int64_t grid = B * fb;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const bool fvec = d % kFinVec == 0 && ((uintptr_t)c % 16) == 0;
+  if (B * ws.nq1 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (ws.runs >= kQ1) {                          // some full Q1 block
+    q1blocks_kernel<<<(unsigned)(B * ws.nq1), kThreads, 0, s>>>(long_pieces(ws), ws.q1,
+                                                                ws.has_long, (int)d);
+    FK_CHECK(hipGetLastError());
+  }
+  if (ws.runs >= kQ1 * kQ2) {                    // some full Q2 block
+    q2blocks_kernel<<<(unsigned)(B * ws.nq2), kThreads, 0, s>>>(long_pieces(ws), ws.q1, ws.q2,
+                                                                ws.has_long, (int)d);
+    FK_CHECK(hipGetLastError());
+  }
   if (!shift) {                                  // the caller does not need the shift
-    if (defer) return hipSuccess;                // the next norms pass divides
+    if (defer) return hipSuccess;                // the next norms pass finishes long clusters
     finalize_kernel<false><<<(unsigned)grid, kThreads, 0, s>>>(
-        ws.sums, ws.offsets, c, ws.part, 0, ws.has_long, (int)d, (int)K, (int)fb, fvec);
+        long_pieces(ws), ws.offsets, c, ws.part, 0, ws.has_long, (int)d, (int)K, (int)fb);
     return hipGetLastError();
   }
   finalize_kernel<true><<<(unsigned)grid, kThreads, 0, s>>>(
-      ws.sums, ws.offsets, c, ws.part + sw, (int)pstride, ws.has_long, (int)d, (int)K, (int)fb,
-      fvec);
+      long_pieces(ws), ws.offsets, c, ws.part + sw, (int)pstride, ws.has_long, (int)d, (int)K,
+      (int)fb);
   FK_CHECK(hipGetLastError());
   shift_reduce_kernel<<<(unsigned)B, kThreads, 0, s>>>(ws.part, shift, (int)pstride);
   return hipGetLastError();
@@ -1202,21 +1775,20 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
 
 PendingFinish pending_finish(const UpdateWs& ws, int64_t K) {
   PendingFinish pf;
-  pf.sums = ws.sums;
+  pf.lp = long_pieces(ws);
   pf.offsets = ws.offsets;
   pf.has_long = ws.has_long;
   pf.K = K;
   return pf;
 }
 
-// The division a deferred update left, when no norms pass follows.
+// The long clusters a deferred update left, when no norms pass follows.
 hipError_t launch_finish(float* c, const UpdateWs& ws, int64_t B, int64_t d, int64_t K,
                          hipStream_t s) {
   const int64_t fb = fin_blocks(K, d);
   if (B * fb > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const bool fvec = d % kFinVec == 0 && ((uintptr_t)c % 16) == 0;
   finalize_kernel<false><<<(unsigned)(B * fb), kThreads, 0, s>>>(
-      ws.sums, ws.offsets, c, ws.part, 0, ws.has_long, (int)d, (int)K, (int)fb, fvec);
+      long_pieces(ws), ws.offsets, c, ws.part, 0, ws.has_long, (int)d, (int)K, (int)fb);
   return hipGetLastError();
 }
 
@@ -1231,7 +1803,7 @@ hipError_t launch_update_accumulate(const void* x, const int32_t* ids, int dt, i
                                     int32_t* counts_run, int32_t* counts_chunk,
                                     const UpdateWs& ws, hipStream_t s) {
   if (B == 0 || N == 0) return hipSuccess;
-  FK_CHECK(run_sort(ids, B, N, d, K, counts_chunk, nullptr, ws, s));
+  FK_CHECK(run_sort(ids, dt, B, N, d, K, counts_chunk, ws, s));
   FK_CHECK(segreduce_any(x, dt, ws, B, N, d, K, sums_run, nullptr, nullptr, 0, true, s));
   int64_t g = (B * K + kThreads - 1) / kThreads;
   g = g < 1 ? 1 : (g > 4096 ? 4096 : g);

@@ -11,7 +11,8 @@
  *   - fk_update: sort-inverse update -- counting sort of the assignment into
  *                per-cluster segments (an inverse permutation of point
  *                indices; the points themselves never move), on-chip segment
- *                reductions with one atomic per segment piece, then the new
+ *                reductions, one stored piece per run of 256 sorted positions
+ *                for long segments (no scatter atomics), then the new
  *                centroids and the centre shift;
  *   - fk_lloyd : the loop over those steps with the tol test;
  *   - fk_lloyd_host: the same loop for points kept in host memory, streamed
@@ -93,13 +94,15 @@ fk_status_t fk_norms(const float* c, void* c_lp, float* cnorm, fk_dtype_t dt,
 
 /*
  * FlashAssign: ids[b,n] = argmin_k ( cnorm[b,k] - 2 x[b,n].c_lp[b,k] ),
- * i.e. the nearest centroid to x[b,n] among c_lp[b,:], lowest index on ties.
+ * i.e. the nearest centroid to x[b,n] among c_lp[b,:].
  * Every type runs on the matrix cores with fp32 accumulation: fp16/bf16
- * products are exact, fp32 products are rounded to fp32. The small-D path
- * (fp16/bf16 d <= 512, fp32 d <= 256) carries each score's row in its 4 low
- * mantissa bits, so two centroids whose scores agree to 2^-19 of their size
- * (within the rounding of the fp32 sum itself) may resolve to either of the
- * two.
+ * products are exact, fp32 products are rounded to fp32. Ties: centroids
+ * whose fp32 scores are equal, or (small-D path) agree to within 2^-19 of
+ * their size -- the rounding of the fp32 sum itself, since that path carries
+ * each score's row in its 4 low mantissa bits -- may resolve to either one;
+ * between 32-row blocks and in the split-D path exact ties go to the lower
+ * index. The small-D path covers fp16/bf16 d <= 512 and fp32 d <= 256. The
+ * result is the same on every run.
  * [hysenlabs] "The point of the kernel is that the distance matrix never
  * exists": points processed in tiles, centroids streamed in chunks, the
  * partial dot products kept in registers across the d loop; small-D path
@@ -120,16 +123,20 @@ fk_status_t fk_assign(const void* x, const void* c_lp, const float* cnorm, fk_dt
  *   shift[b]    = sum_k || c_new[b,k] - c_old[b,k] ||^2                (fp32)
  * The ids are counting-sorted into per-cluster segments through an inverse
  * permutation of point indices (the point matrix is never permuted); each
- * segment is reduced on chip and each block issues one atomic add per
- * segment piece, not one per point: [itinai] third paragraph, [paixiang]
+ * segment is reduced on chip, a segment longer than 256 sorted positions in
+ * pieces (one per run of 256 positions it touches, combined in a fixed
+ * order), instead of one scatter atomic per point: [itinai] third paragraph, [paixiang]
  * "它攻克的两大瓶颈" and the update-contention panel of "交互式讲解",
  * [iaemfoco] "Sort-Inverse Update", [arxiv] Abstract.
  *   x (B,N,d) dt, ids (B,N) int32 in (each in [0,K));
  *   c (B,K,d) fp32 in/out; counts (B,K) int32 out; shift (B) fp32 out;
  *   ws: device workspace of at least fk_workspace_size(dt,B,N,d,K) bytes.
  * Ids outside [0,K) give undefined results (not checked on the device).
- * fp32 sums use atomics, so centroids may differ in the last bits between
- * runs; counts never do.
+ * Deterministic for K <= 65536: the sort keeps a fixed order of each
+ * cluster's points and every fp32 sum is formed in a fixed order, so the
+ * same inputs give bit-identical centroids, counts and shift on every run.
+ * Above that the sort ranks points with global atomics and centroids may
+ * differ in the last bits between runs; counts never do.
  */
 fk_status_t fk_update(const void* x, const int32_t* ids, fk_dtype_t dt,
                       int64_t B, int64_t N, int64_t d, int64_t K,
@@ -146,7 +153,10 @@ fk_status_t fk_update(const void* x, const int32_t* ids, fk_dtype_t dt,
  * With tol > 0, iteration t + 1 is enqueued before t's shift has reached the
  * host; when t turns out to be the last, the ids and centres of t (kept in
  * the workspace) replace what t + 1 wrote, so the results are exactly those
- * of stopping after t.
+ * of stopping after t. Deterministic like fk_update (K <= 65536).
+ * init is in dt: a run continued from the fp32 centres of an earlier call
+ * starts from those centres rounded to dt, so such a resume is approximate
+ * (exact when the centres are representable in dt).
  * The batched API and its tol argument: [hysenlabs] "Exact K-Means, with the
  * assignment step written in Triton"; one step = one assignment plus one
  * centroid update: [paixiang] "什么是 Flash-KMeans".

@@ -55,17 +55,23 @@ def test_status_strings(lib):
 def test_workspace_size(lib):
     ws = lib.fk_workspace_size
     big = ws(1, 32, 75600, 128, 1000)
-    # sums, offsets, cursor, perm, run starts (one per 256 sorted positions),
-    # shift partials (one per segment-reduce wave -- a run and a column slice,
-    # sized for fp32 rows, 32 columns per slice -- and one per finalize block
-    # of 1024 centroid elements), the split sort's count matrix (16 chunks per
-    # problem here), a long-cluster flag per problem, rounded centroids, norms,
-    # counts, shift, and the copies of ids and centres the tol test keeps
+    # long-segment pieces (two slots of d floats per run of 256 sorted
+    # positions), their Q1 and Q2 block sums (one row per 32 runs, one per 32
+    # Q1 rows), offsets,
+    # perm, run starts, shift partials (one per segment-reduce wave -- a run
+    # and a column slice, sized for fp32 rows, 32 columns per slice -- and one
+    # per finalize block of 1024 centroid elements), the split sort's count
+    # matrix (16 chunks per problem here), a long-cluster flag per problem,
+    # rounded centroids, norms, counts, shift, and the copies of ids and
+    # centres the tol test keeps
     runs = -(-75600 // 256)
+    nq1 = -(-runs // 32)
+    nq2 = -(-nq1 // 32)
     slices = -(-128 // 32)
     fb = -(-1000 * 128 // 1024)
     G = 16
-    need = 32 * 1000 * 128 * 4 + 32 * 1001 * 4 + 32 * 1000 * 4 + 32 * 75600 * 4 + \
+    need = 32 * runs * 2 * 128 * 4 + 32 * nq1 * 128 * 4 + 32 * nq2 * 128 * 4 + \
+        32 * 1001 * 4 + 32 * 75600 * 4 + \
         32 * runs * 4 + 32 * (runs * slices + fb) * 4 + 32 * G * 1000 * 4 + 32 * 4 + \
         32 * 1000 * 128 * 2 + 32 * 1000 * 4 * 2 + 32 * 4 + 32 * 75600 * 4 + 32 * 1000 * 128 * 4
     assert need <= big <= need + 14 * 256

@@ -154,6 +154,12 @@ UPDATE_CASES = [
     ("f16", 2, 10000, 130, 40000, "uniform"),  # K above one LDS bin range
     ("f32", 1, 777, 3, 5, "zipf"),
     ("f16", 1, 9000, 2000, 20, "uniform"),     # d above one segreduce pass
+    ("f16", 2, 300000, 32, 8, "zipf"),         # clusters over 32 runs: Q1 block sums
+    ("bf16", 1, 300000, 64, 5, "one"),         # one cluster over 1024 runs: a Q2 block sum
+    ("f32", 1, 70000, 36, 3, "zipf"),          # long pieces with d % 4 == 0, fp32 slices
+    ("f16", 1, 70000, 33, 3, "zipf"),          # long pieces with ragged d (scalar stores)
+    ("f16", 2, 20000, 64, 5000, "zipf"),       # ids over 11 bits: the two-pass LDS sort
+    ("bf16", 1, 50000, 64, 2047, "uniform"),   # the widest ids of the direct scatter
 ]
 
 
@@ -184,6 +190,45 @@ def test_update_parity(fk, dtype, B, N, d, K, kind):
     err = centroid_rel_err(c_new, u.centers)
     assert err <= CENTROID_RTOL, err
     check_shift(shift.cpu().numpy().astype(np.float64), u.shift, u.centers)
+
+
+RADIX_CASES = [c for c in UPDATE_CASES if c[4] <= 65536 and c[2] * c[1] <= 700000]
+
+
+@pytest.mark.parametrize("dtype,B,N,d,K,kind", RADIX_CASES)
+def test_update_parity_radix(fk, monkeypatch, dtype, B, N, d, K, kind):
+    """The same cases with perm built by the whole-problem radix passes."""
+    monkeypatch.setenv("FK_FORCE_RADIX", "1")
+    test_update_parity(fk, dtype, B, N, d, K, kind)
+
+
+@pytest.mark.parametrize("radix", [False, True])
+def test_update_is_deterministic(fk, monkeypatch, radix):
+    """Hot clusters (pieces over many runs): ten fk_update calls on the same
+    ids give bit-identical centroids, counts and shift; the perm is the
+    stable order (each cluster's points by increasing index)."""
+    torch = _torch()
+    if radix:
+        monkeypatch.setenv("FK_FORCE_RADIX", "1")
+    else:
+        monkeypatch.delenv("FK_FORCE_RADIX", raising=False)
+    x, _, _ = synthdata.make_mixture(2, 120000, 128, 1, "f16", n_comp=8, mean_std=1.0, seed=31)
+    ids = synthdata.zipf_ids(2, 120000, 300, 32)
+    c0 = np.random.default_rng(33).standard_normal((2, 300, 128)).astype(np.float32)
+    x_dev, ids_dev = to_dev(x, "f16"), torch.from_numpy(ids).cuda()
+    outs = []
+    for _ in range(10):
+        c = torch.from_numpy(c0).cuda()
+        _, counts, shift = fk.fk_update(x_dev, ids_dev, c)
+        torch.cuda.synchronize()
+        outs.append((c.cpu().numpy(), counts.cpu().numpy(), shift.cpu().numpy()))
+    for c, counts, shift in outs[1:]:
+        assert np.array_equal(c.view(np.uint32), outs[0][0].view(np.uint32))
+        assert np.array_equal(counts, outs[0][1])
+        assert np.array_equal(shift.view(np.uint32), outs[0][2].view(np.uint32))
+    u = oracle.update(synthdata.to_f64(x, "f16"), ids, c0.astype(np.float64))
+    assert u.counts.max() > 20 * 256                # long clusters over many runs
+    assert centroid_rel_err(outs[0][0], u.centers) <= CENTROID_RTOL
 
 
 # ---------------------------------------------------------------------------
@@ -411,13 +456,25 @@ def test_zero_iterations_returns_init(fk):
     np.testing.assert_array_equal(centers.cpu().numpy(), w.init)
 
 
-def test_determinism_of_ids_and_counts(fk):
+@pytest.mark.parametrize("tol", [0.0, 1e-30])
+def test_lloyd_is_deterministic(fk, tol):
+    """Long clusters (a 12-component mixture clustered into K = 16, so every
+    cluster holds thousands of points and is summed in pieces): ten fk_lloyd
+    runs give bit-identical ids, centres and iteration counts, with and
+    without the tol test (the deferred division in the norms pass and the
+    finalize kernel)."""
     torch = _torch()
-    w = synthdata.make_workload("io_breakdown", scale_n=20000, B=3)
-    x_dev, init_dev = to_dev(w.x, w.dtype), to_dev(w.init, w.dtype)
-    runs = [fk.fk_lloyd(x_dev, init_dev, 3, 0.0) for _ in range(3)]
-    for ids, _, _ in runs[1:]:
-        assert torch.equal(ids, runs[0][0])
+    x, init, _ = synthdata.make_mixture(2, 40000, 128, 16, "f16", n_comp=12, mean_std=2.0,
+                                        seed=41)
+    x_dev, init_dev = to_dev(x, "f16"), to_dev(init, "f16")
+    runs = [fk.fk_lloyd(x_dev, init_dev, 6, tol) for _ in range(10)]
+    ids0, c0, n0 = runs[0]
+    counts = np.bincount(ids0.cpu().numpy()[0], minlength=16)
+    assert counts.max() > 4 * 256
+    for ids, c, n in runs[1:]:
+        assert n == n0
+        assert torch.equal(ids, ids0)
+        assert torch.equal(c.view(torch.int32), c0.view(torch.int32))
 
 
 def test_status_codes_through_binding(fk):
