@@ -19,6 +19,8 @@ from ._binding import (  # noqa: F401
     fk_trace_begin,
     fk_trace_end,
     fk_update,
+    fk_update_noalloc,
+    FK_NOALLOC_SCRATCH_BYTES,
     fk_version,
     fk_workspace_size,
     fk_workspace_size_host,

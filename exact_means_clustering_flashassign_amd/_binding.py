@@ -50,6 +50,7 @@ def load(path: Optional[str] = None):
         "fk_norms": (ctypes.c_int, [P, P, P, ctypes.c_int, I64, I64, I64, P]),
         "fk_assign": (ctypes.c_int, [P, P, P, ctypes.c_int, I64, I64, I64, I64, P, P]),
         "fk_update": (ctypes.c_int, [P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, P, SZ, P]),
+        "fk_update_noalloc": (ctypes.c_int, [P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, P]),
         "fk_lloyd": (ctypes.c_int, [P, ctypes.c_int, I64, I64, I64, I64, P, I32, ctypes.c_float,
                                     P, P, ctypes.POINTER(I32), P, SZ, P]),
         "fk_workspace_size_host": (SZ, [ctypes.c_int, I64, I64, I64, I64]),
@@ -183,6 +184,24 @@ def fk_update(x, ids, c, counts=None, shift=None, ws=None):
                           _dev(shift, "shift", torch.float32, (B,)), _dev(ws, "ws", torch.uint8),
                           ws.numel(), _stream(x))
     _check(st, "fk_update")
+    return c, counts, shift
+
+
+FK_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def fk_update_noalloc(x, ids, c, counts, shift):
+    """fk_update with the library's own device scratch (no workspace); the
+    caller passes every output. In-place update of c; returns (c, counts, shift)."""
+    torch = _torch()
+    code = dtype_code(x.dtype)
+    B, N, d = x.shape
+    K = c.shape[1]
+    st = load().fk_update_noalloc(_dev(x, "x"), _dev(ids, "ids", torch.int32, (B, N)), code, B,
+                                  N, d, K, _dev(c, "c", torch.float32, (B, K, d)),
+                                  _dev(counts, "counts", torch.int32, (B, K)),
+                                  _dev(shift, "shift", torch.float32, (B,)), _stream(x))
+    _check(st, "fk_update_noalloc")
     return c, counts, shift
 
 

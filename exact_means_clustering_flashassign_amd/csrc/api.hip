@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "fk_internal.hpp"
@@ -201,6 +202,47 @@ hipEvent_t trace_event(int32_t it, int which) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Workspace of fk_update_noalloc: one array per GPU, part of the library's
+// code object (each device that loads the library holds its own copy until
+// the process ends). In host code `scratch` names a host-side stand-in, not
+// device memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is ever handed to a kernel.
+static_assert(FK_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte units");
+static __device__ __align__(256) unsigned char scratch[FK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchPtrs {
+  std::once_flag once[kMaxDevices];
+  void* ptr[kMaxDevices] = {};
+  hipError_t err[kMaxDevices] = {};
+};
+ScratchPtrs g_scratch;
+
+// The current device's scratch address (null with *e set on failure).
+void* scratch_ptr(hipError_t* e) {
+  int dev = -1;
+  *e = hipGetDevice(&dev);
+  if (*e != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *e = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch.once[dev], [dev]() {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch.err[dev] = r;
+    g_scratch.ptr[dev] = r == hipSuccess ? p : nullptr;
+  });
+  *e = g_scratch.err[dev];
+  return g_scratch.ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fk_status_string(fk_status_t st) {
@@ -250,6 +292,23 @@ fk_status_t fk_update(const void* x, const int32_t* ids, fk_dtype_t dt, int64_t 
     return FK_ERR_WORKSPACE;
   const UpdateWs w = fk::carve_update_ws(ws, B, N, d, K);
   const hipError_t e = fk::launch_update(x, ids, dt, B, N, d, K, c, counts, shift, w, stream);
+  if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
+fk_status_t fk_update_noalloc(const void* x, const int32_t* ids, fk_dtype_t dt, int64_t B,
+                              int64_t N, int64_t d, int64_t K, float* c, int32_t* counts,
+                              float* shift, hipStream_t stream) {
+  if (!valid_dt(dt) || !valid_sizes(B, N, d, K)) return FK_ERR_INVALID;
+  if (B > 0 && (!c || !counts || !shift)) return FK_ERR_INVALID;
+  if (B * N > 0 && (!x || !ids)) return FK_ERR_INVALID;
+  if (B == 0) return FK_OK;
+  if (fk::update_ws_bytes(B, N, d, K) > (size_t)FK_NOALLOC_SCRATCH_BYTES) return FK_ERR_WORKSPACE;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_ptr(&e);
+  if (!ws) return FK_ERR_HIP;
+  const UpdateWs w = fk::carve_update_ws(ws, B, N, d, K);
+  e = fk::launch_update(x, ids, dt, B, N, d, K, c, counts, shift, w, stream);
   if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
   return hip_status(e);
 }

@@ -144,6 +144,25 @@ fk_status_t fk_update(const void* x, const int32_t* ids, fk_dtype_t dt,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * fk_update without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and results as fk_update, with
+ * the workspace taken from a device array that is part of the library
+ * (FK_NOALLOC_SCRATCH_BYTES bytes on each GPU that runs it, held until the
+ * process ends). The call allocates nothing. Problems whose
+ * fk_workspace_size(dt,B,N,d,K) exceeds FK_NOALLOC_SCRATCH_BYTES are
+ * rejected with FK_ERR_WORKSPACE. Every call on one GPU uses that GPU's one
+ * array: calls that overlap on a GPU (other streams, other threads) race and
+ * give undefined results; calls ordered on one stream are safe. The array
+ * keeps the last call's contents; nothing in it is assumed zero.
+ * Arguments, layouts and the other errors as fk_update.
+ */
+#define FK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fk_status_t fk_update_noalloc(const void* x, const int32_t* ids, fk_dtype_t dt,
+                              int64_t B, int64_t N, int64_t d, int64_t K,
+                              float* c, int32_t* counts, float* shift, hipStream_t stream);
+
+/*
  * Lloyd's loop: centers <- init (widened to fp32); then for t < max_iter:
  * fk_norms, fk_assign, fk_update; stop after iteration t when
  * max_b shift[b] < tol (strict, so tol == 0 runs exactly max_iter iterations).
