@@ -79,11 +79,20 @@ def cpu_baseline(w, name: str, min_seconds: float = 10.0):
     import oracle
     import synthdata
 
+    # every host core the process may run on, with the BLAS pool set to that
+    # many threads
+    cores = len(os.sched_getaffinity(0))
+    blas = "unknown"
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            cores = max(p.get("num_threads", cores) for p in info)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pass
     nb, rows = CPU_SAMPLE[name]
     nb, rows = min(nb, w.B), min(rows or w.N, w.N)
     x64 = synthdata.to_f64(np.ascontiguousarray(w.x[:nb, :rows]), w.dtype)
@@ -94,10 +103,12 @@ def cpu_baseline(w, name: str, min_seconds: float = 10.0):
         oracle.lloyd(x64, c0, 1, 0.0, w.dtype, want_near=False)
         total += time.perf_counter() - t0
         reps += 1
+    if limiter is not None:
+        limiter.restore_original_limits()
     per_iter_full = total / reps * (w.B / nb) * (w.N / rows)
     part = f"{nb} of the {w.B} problems" + ("" if rows == w.N else f", first {rows} of {w.N} rows")
-    return {"value": 1.0 / per_iter_full, "unit": "iter/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": 1.0 / per_iter_full, "unit": "iter/s", "cores": int(cores),
+            "kind": "oracle", "blas": blas,
             "sample": f"1 Lloyd iteration on {part} (full K, d), fp64 NumPy on the host, "
                       f"{reps} run(s) in {total:.1f} s, scaled by problems and rows to the whole batch"}
 

@@ -138,7 +138,10 @@ class FlashKMeans:
         return self
 
     def fit_predict(self, data, init=None):
-        """Fit, then return the final assignment of every point."""
+        """Fit, then return the ids of the last assignment step of the loop:
+        those computed against the centroids before the last update, not a
+        fresh assignment against the returned centroids (call predict() for
+        that; the two agree once the loop has reached a fixed point)."""
         xb, flat = self._prepare(data)
         ids, centers, n_iter = batch_kmeans_Euclid(xb, self.k, self.tol, self.verbose,
                                                    self.niter, init, self.seed)

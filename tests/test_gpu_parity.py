@@ -300,26 +300,6 @@ def test_free_running(fk, trajectories, name, n, b, T):
     print(name, "first in-band flip at iteration", first_flip)
 
 
-def test_free_running_tol_stop(fk):
-    """The headline recipe's tol rule, reduced: same stop iteration as the oracle."""
-    w = synthdata.make_workload("api_example", scale_n=3000, B=2)
-    res = oracle.lloyd(w.x64(), w.init64(), 100, w.tol, w.dtype, record=True)
-    x_dev, init_dev = to_dev(w.x, w.dtype), to_dev(w.init, w.dtype)
-    flips = 0
-    for t in range(1, res.n_iter + 1):
-        ids, centers, _ = fk.fk_lloyd(x_dev, init_dev, t, 0.0)
-        flips += check_ids(ids.cpu().numpy(), res.trace[t - 1]["assign"])["n_flip_in_band"]
-        if flips:
-            break
-    ids, centers, n_iter = fk.fk_lloyd(x_dev, init_dev, 100, w.tol)
-    shifts = np.array([tr["shift"].max() for tr in res.trace])
-    borderline = np.any(np.abs(shifts - w.tol) <= 1e-3 * w.tol)
-    print("oracle n_iter", res.n_iter, "gpu n_iter", n_iter, "flips", flips)
-    if not flips and not borderline:
-        assert n_iter == res.n_iter
-        assert centroid_rel_err(centers.cpu().numpy(), res.centers) <= CENTROID_RTOL
-
-
 # ---------------------------------------------------------------------------
 # full workload sizes, sampled
 # ---------------------------------------------------------------------------
