@@ -206,11 +206,14 @@ def fk_update_noalloc(x, ids, c, counts, shift):
 
 
 def fk_lloyd(x, init, max_iter: int, tol: float, ids=None, centers=None, ws=None):
-    """Lloyd's loop from init (B,K,d) in x's dtype -> (ids, centers fp32, n_iter)."""
+    """Lloyd's loop from init (B,K,d) in x's dtype -> (ids, centers fp32, n_iter).
+    init=None resumes from the fp32 centres in `centers` (updated in place)."""
     torch = _torch()
     code = dtype_code(x.dtype)
     B, N, d = x.shape
-    K = init.shape[1]
+    if init is None and centers is None:
+        raise ValueError("resuming (init=None) needs the fp32 centers to start from")
+    K = (init if init is not None else centers).shape[1]
     if ids is None:
         ids = torch.empty((B, N), dtype=torch.int32, device=x.device)
     if centers is None:
@@ -218,7 +221,8 @@ def fk_lloyd(x, init, max_iter: int, tol: float, ids=None, centers=None, ws=None
     if ws is None:
         ws = workspace(x.dtype, B, N, d, K, x.device)
     n_iter = ctypes.c_int32(0)
-    st = load().fk_lloyd(_dev(x, "x"), code, B, N, d, K, _dev(init, "init", x.dtype, (B, K, d)),
+    ip = None if init is None else _dev(init, "init", x.dtype, (B, K, d))
+    st = load().fk_lloyd(_dev(x, "x"), code, B, N, d, K, ip,
                          int(max_iter), float(tol), _dev(ids, "ids", torch.int32, (B, N)),
                          _dev(centers, "centers", torch.float32, (B, K, d)),
                          ctypes.byref(n_iter), _dev(ws, "ws", torch.uint8), ws.numel(),
@@ -236,16 +240,20 @@ def fk_lloyd_host(x_host, init, max_iter: int, tol: float, chunk: int, ids=None,
                   ws=None):
     """Lloyd's loop over points in host memory, streamed in chunks of `chunk`
     points per problem -> (ids, centers fp32, n_iter). x_host: a contiguous
-    CPU tensor (B,N,d), best page-locked (pin_memory); init (B,K,d) on the GPU."""
+    CPU tensor (B,N,d), best page-locked (pin_memory); init (B,K,d) on the GPU,
+    or None to resume from the fp32 centres in `centers`."""
     torch = _torch()
     if not isinstance(x_host, torch.Tensor) or x_host.device.type != "cpu":
         raise ValueError("x_host must be a CPU tensor")
     if not x_host.is_contiguous() or x_host.dim() != 3:
         raise ValueError("x_host must be a contiguous (B, N, d) tensor")
+    if init is None and centers is None:
+        raise ValueError("resuming (init=None) needs the fp32 centers to start from")
     code = dtype_code(x_host.dtype)
     B, N, d = x_host.shape
-    K = init.shape[1]
-    dev = init.device
+    start = init if init is not None else centers
+    K = start.shape[1]
+    dev = start.device
     if ids is None:
         ids = torch.empty((B, N), dtype=torch.int32, device=dev)
     if centers is None:
@@ -259,11 +267,12 @@ def fk_lloyd_host(x_host, init, max_iter: int, tol: float, chunk: int, ids=None,
         ws = raw[off:off + n]
     n_iter = ctypes.c_int32(0)
     st = load().fk_lloyd_host(x_host.data_ptr(), code, B, N, d, K,
-                              _dev(init, "init", x_host.dtype, (B, K, d)), int(max_iter),
+                              None if init is None else _dev(init, "init", x_host.dtype,
+                                                             (B, K, d)), int(max_iter),
                               float(tol), int(chunk), _dev(ids, "ids", torch.int32, (B, N)),
                               _dev(centers, "centers", torch.float32, (B, K, d)),
                               ctypes.byref(n_iter), _dev(ws, "ws", torch.uint8), ws.numel(),
-                              _stream(init))
+                              _stream(start))
     _check(st, "fk_lloyd_host")
     return ids, centers, int(n_iter.value)
 

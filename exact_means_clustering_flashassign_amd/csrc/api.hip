@@ -318,14 +318,15 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
                      int32_t* n_iter, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_dt(dt) || !valid_sizes(B, N, d, K)) return FK_ERR_INVALID;
   if (max_iter < 0 || !(tol >= 0.f) || !n_iter) return FK_ERR_INVALID;
-  if (B > 0 && (!init || !centers)) return FK_ERR_INVALID;
+  if (B > 0 && !centers) return FK_ERR_INVALID;
   if (B * N > 0 && (!x || !ids)) return FK_ERR_INVALID;
   *n_iter = 0;
   if (B == 0) return FK_OK;
   if (!ws || ((uintptr_t)ws & 255) || ws_bytes < fk_workspace_size(dt, B, N, d, K))
     return FK_ERR_WORKSPACE;
   const LloydWs w = carve_lloyd(ws, dt, B, N, d, K);
-  hipError_t e = fk::launch_widen(init, centers, dt, B * K * d, stream);
+  // no init: resume from the fp32 centres already in `centers`
+  hipError_t e = init ? fk::launch_widen(init, centers, dt, B * K * d, stream) : hipSuccess;
   if (e != hipSuccess) return FK_ERR_HIP;
   if (max_iter == 0) return hip_status(fk::launch_fill_i32(ids, 0, B * N, stream));
 
@@ -413,14 +414,15 @@ fk_status_t fk_lloyd_host(const void* x_host, fk_dtype_t dt, int64_t B, int64_t 
                           void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_dt(dt) || !valid_sizes(B, N, d, K) || chunk < 1) return FK_ERR_INVALID;
   if (max_iter < 0 || !(tol >= 0.f) || !n_iter) return FK_ERR_INVALID;
-  if (B > 0 && (!init || !centers)) return FK_ERR_INVALID;
+  if (B > 0 && !centers) return FK_ERR_INVALID;
   if (B * N > 0 && (!x_host || !ids)) return FK_ERR_INVALID;
   *n_iter = 0;
   if (B == 0) return FK_OK;
   if (!ws || ((uintptr_t)ws & 255) || ws_bytes < fk_workspace_size_host(dt, B, chunk, d, K))
     return FK_ERR_WORKSPACE;
   const HostWs w = carve_host(ws, dt, B, chunk, d, K);
-  if (fk::launch_widen(init, centers, dt, B * K * d, stream) != hipSuccess) return FK_ERR_HIP;
+  if (init && fk::launch_widen(init, centers, dt, B * K * d, stream) != hipSuccess)
+    return FK_ERR_HIP;
   if (max_iter == 0) {
     if (fk::launch_fill_i32(ids, 0, B * N, stream) != hipSuccess) return FK_ERR_HIP;
     return hip_status(hipStreamSynchronize(stream));

@@ -26,6 +26,8 @@
 // best score and row, then reloaded with -||c||^2/2 of the next tile's rows.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fk_internal.hpp"
 
 namespace fk {
@@ -251,6 +253,318 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS staging, for whole rows (16-byte aligned, d a multiple of
+// 128). Same tiles, accumulators and argmax as above, but both operands go
+// from memory straight into LDS with 16-byte buffer loads that write LDS,
+// and both MFMA operands are read from LDS:
+//   - d-chunks of 64 (4 k-steps); a staged load writes 64 consecutive
+//     16-byte slots, i.e. whole rows, so the point rows stream in whole
+//     cache lines (a register load of an MFMA fragment touches 32 rows at 32
+//     bytes each, and those partial-line requests, not HBM, were the limit);
+//   - centroid chunks are double-buffered and shared by the block; each wave
+//     stages its own 64 point rows into a ring of four half-chunk slots (two
+//     k-steps each), refilled as soon as the wave has read a slot, so a
+//     point load has about 1.5 chunks to land;
+//   - a wave's memory loads retire in issue order: each chunk issues the next
+//     chunk's centroid loads first, and just before the chunk's closing
+//     barrier the wave waits until only the point loads issued after them
+//     are outstanding.
+// Rows are stored unpadded (a staged load fills whole rows) with their
+// 16-byte units permuted by an XOR of the row index, so the fragment reads
+// (consecutive rows, one unit) fall on distinct banks. Every slot and buffer
+// is its own LDS array and the chunk loop is unrolled by two, so each read
+// names its array at compile time and the compiler's wait before a read
+// covers only the loads into that array.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediate: at most vm vector-memory and lgkm LDS/scalar
+// operations outstanding (expcnt not waited on).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+constexpr int kLC = 64;                         // d-chunk of the LDS-staged kernel
+constexpr int kLKS = kLC / 16;                  // k-steps per chunk
+constexpr int kCRowB = kLC * 2;                 // bytes of a staged centroid row (128)
+constexpr int kXRowB = kLC;                     // bytes of a staged half-chunk point row (64)
+constexpr int kWaveRows = kNF * 32;             // point rows per wave
+constexpr int kXSlotB = kWaveRows * kXRowB;     // bytes of one wave's half-chunk slot (4 KB)
+
+// unit permutations: centroid row r keeps unit u (of 8) at u ^ cperm(r),
+// point row r keeps unit u (of 4) at u ^ xperm(r)
+__device__ __forceinline__ int cperm(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int xperm(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <int DT, int NSUB>
+__global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ c,
+    const float* __restrict__ cnorm, int32_t* __restrict__ ids, int N, int d, int K,
+    int blocks_per_batch, int total, int nblocks) {
+  constexpr int TK = NSUB * 32;                   // centroids per K tile
+  constexpr int CTILEB = TK * kCRowB;             // bytes of a staged centroid chunk
+  constexpr int RPW = TK / kWaves;                // centroid rows staged per wave
+  constexpr int NCL = RPW / 8;                    // centroid loads per thread (8 rows each)
+  constexpr int NXL = kWaveRows / 16;             // point loads per half-chunk (16 rows each)
+  constexpr int Q = NSUB * kLKS;                  // (row block, k-step) pairs per chunk
+  static_assert(RPW % 8 == 0 && TK <= kThreads, "staging split");
+  __shared__ __align__(256) unsigned char cs0[CTILEB];
+  __shared__ __align__(256) unsigned char cs1[CTILEB];
+  __shared__ __align__(256) unsigned char xs0[kWaves * kXSlotB];   // even chunks, k-steps 0-1
+  __shared__ __align__(256) unsigned char xs1[kWaves * kXSlotB];   // even chunks, k-steps 2-3
+  __shared__ __align__(256) unsigned char xs2[kWaves * kXSlotB];   // odd chunks, k-steps 0-1
+  __shared__ __align__(256) unsigned char xs3[kWaves * kXSlotB];   // odd chunks, k-steps 2-3
+  __shared__ __align__(16) float lds_h[2][kWaves * 64];   // ||c||^2 by K-tile parity
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, r32 = lane & 31;
+  const int nchunks = d / kLC;                    // even
+  const int ktiles = (K + TK - 1) / TK;
+  const int T = ktiles * nchunks;                 // chunks per point block
+  const uint32_t rowb = (uint32_t)d * 2;          // bytes per row in HBM
+
+  // point block v -> problem, first row, and the rotation of its d-chunk
+  // order: blocks running at the same time read different column slices of
+  // their rows, so their requests spread over the memory channels instead of
+  // all hitting the few that hold one slice
+  auto locate = [&](int64_t v, int& pb, int& row0, int& rot) {
+    const int64_t logical = xcd_remap(v, total);
+    pb = __builtin_amdgcn_readfirstlane((int)(logical / blocks_per_batch));
+    row0 = __builtin_amdgcn_readfirstlane((int)(logical % blocks_per_batch) * kBN);
+    rot = __builtin_amdgcn_readfirstlane((int)(logical % nchunks));
+  };
+
+  // Centroid chunk t of (problem pb) into dst: load j of wave w fills rows
+  // w*RPW + 8j .. +7; lane l writes slot l % 8 of row 8j + l / 8, i.e. unit
+  // (l % 8) ^ cperm(row). Rows past K lie past the buffer's range and read as
+  // zero (their norms are -inf: they never win).
+  auto stage_c = [&](unsigned char* dst, float* hdst, int pb, int rot, int t) {
+    const int kt = t / nchunks;
+    int ch = t - kt * nchunks + rot;
+    ch = ch >= nchunks ? ch - nchunks : ch;
+    const int rows = min(K - kt * TK, TK);
+    const uint16_t* tb = c + ((int64_t)pb * K + (int64_t)kt * TK) * d;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(tb), 0, __builtin_amdgcn_readfirstlane(rows * (int)rowb), kRawBufferWord3);
+#pragma unroll
+    for (int j = 0; j < NCL; ++j) {
+      const int row = wave * RPW + 8 * j + (lane >> 3);
+      const uint32_t voff = (uint32_t)row * rowb + (uint32_t)(ch * kCRowB) +
+                            (uint32_t)(((lane & 7) ^ cperm(row)) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_t*)(dst + (wave * RPW + 8 * j) * kCRowB), 16, voff, 0, 0, 0);
+    }
+    // ||c||^2 of rows kt*TK + wave*64 + lane into hdst (64 per wave, so
+    // every wave issues the same loads; rows past K read as zero and rows
+    // past the tile are never used). Every chunk stages the norms of its
+    // successor's K tile into the slot of the next tile, which only the next
+    // tile's start reads.
+    const auto rn = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(cnorm + (int64_t)pb * K), 0, __builtin_amdgcn_readfirstlane(K * 4),
+        kRawBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rn, (lds_void_t*)(hdst + wave * 64), 4, (uint32_t)(kt * TK + lane) * 4 + wave * 256, 0,
+        0, 0);
+  };
+  // Half hh (k-steps 2hh, 2hh+1) of point chunk t of the wave's 64 rows
+  // (from row0 + wave*64) into the wave's part of slot array dst: load j
+  // fills rows 16j .. 16j+15; lane l writes slot l % 4 of row 16j + l / 4,
+  // i.e. unit (l % 4) ^ xperm(row). Rows past N read as zero (their ids are
+  // never stored).
+  auto stage_x = [&](unsigned char* dst, int pb, int row0, int rot, int t, int hh) {
+    int ch = t % nchunks + rot;
+    ch = ch >= nchunks ? ch - nchunks : ch;
+    const int r0 = row0 + wave * kWaveRows;
+    const uint16_t* xb = x + ((int64_t)pb * N + r0) * d;
+    const int rows = min(max(N - r0, 0), kWaveRows);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(xb), 0, __builtin_amdgcn_readfirstlane(rows * (int)rowb), kRawBufferWord3);
+#pragma unroll
+    for (int j = 0; j < NXL; ++j) {
+      const int row = 16 * j + (lane >> 2);
+      const uint32_t voff = (uint32_t)row * rowb + (uint32_t)(ch * kCRowB + hh * kXRowB) +
+                            (uint32_t)(((lane & 3) ^ xperm(row)) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_t*)(dst + wave * kXSlotB + 16 * j * kXRowB), 16, voff, 0, 0, 0);
+    }
+  };
+
+  // A fragment of (row block sub, k-step kk): lane (r32, half) reads unit
+  // 2kk + half of centroid row sub*32 + r32, at byte
+  // sub*32*128 + (a_lane[sub & 1] ^ (kk * 32)).
+  const uint32_t a_lane0 = (uint32_t)r32 * kCRowB + (uint32_t)((half ^ cperm(r32)) * 16);
+  const uint32_t a_lane1 = (uint32_t)r32 * kCRowB + (uint32_t)((half ^ cperm(32 + r32)) * 16);
+  auto read_a = [&](const unsigned char* buf, int q) -> uint4 {
+    const int sub = q % NSUB, kk = q / NSUB;
+    return *reinterpret_cast<const uint4*>(
+        buf + (((sub & 1 ? a_lane1 : a_lane0) ^ (uint32_t)(kk << 5)) +
+               (uint32_t)(sub * 32 * kCRowB)));
+  };
+  // B fragment f of k-step kk (within its half-chunk slot): lane (r32, half)
+  // reads unit 2(kk % 2) + half of the wave's point row f*32 + r32.
+  const uint32_t b_lane = (uint32_t)wave * kXSlotB + (uint32_t)r32 * kXRowB +
+                          (uint32_t)((half ^ xperm(r32)) * 16);
+  auto read_b = [&](const unsigned char* slot, int f, int kk) -> uint4 {
+    return *reinterpret_cast<const uint4*>(
+        slot + ((b_lane ^ (uint32_t)((kk & 1) << 5)) + (uint32_t)(f * 32 * kXRowB)));
+  };
+
+  floatx16_t acc[NSUB][kNF];
+  float best[kNF];
+  int bidx[kNF];
+
+  int64_t v = blockIdx.x;
+  int pb, row0, rot;
+  locate(v, pb, row0, rot);
+  int64_t vn = v + nblocks;
+  int npb = pb, nrow0 = row0, nrot = rot;
+  if (vn < total) locate(vn, npb, nrow0, nrot);
+  bool has_next = vn < total;
+
+  // prologue: centroid chunk 0, point chunk 0 (both halves), point chunk 1's
+  // first half (a chunk issues its successor's second half and the first
+  // half of the chunk after that)
+  stage_c(cs0, lds_h[0], pb, rot, 0);
+  stage_x(xs0, pb, row0, rot, 0, 0);
+  stage_x(xs1, pb, row0, rot, 0, 1);
+  stage_x(xs2, pb, row0, rot, 1, 0);               // every point block has T >= 2 chunks
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+  __syncthreads();
+
+  int tc = 0;                                     // K tiles started by this block
+  for (;;) {
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) {
+      best[f] = -INFINITY;
+      bidx[f] = 0;
+    }
+    for (int kt = 0; kt < ktiles; ++kt) {
+      // accumulators start at zero; the argmax adds -||c||^2/2 of the rows
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+        for (int f = 0; f < kNF; ++f)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[sub][f][r] = 0.f;
+      // Chunk t of the current point block, of parity P (every K tile has
+      // an even number of chunks, so the parity loop, unrolled, names every
+      // buffer at compile time): read centroids from cs[P] and points from
+      // xs[2P], xs[2P+1]; meanwhile stage the next step's centroid chunk and
+      // second point half, and the step after next's first point half. Past
+      // the last point block the staging repeats data that nothing reads.
+      for (int ch = 0; ch < nchunks; ch += 2) {
+#pragma unroll
+        for (int P = 0; P < 2; ++P) {
+          const int t = kt * nchunks + ch + P;
+          const unsigned char* cc = P ? cs1 : cs0;
+          unsigned char* cn = P ? cs0 : cs1;
+          const unsigned char* xh0 = P ? xs2 : xs0;
+          const unsigned char* xh1 = P ? xs3 : xs1;
+          unsigned char* xn1 = P ? xs1 : xs3;        // step + 1, second half
+          // step + 1 and step + 2: (point block, chunk)
+          const bool s1_in = t + 1 < T, s1_nx = !s1_in && has_next;
+          const int s1_pb = s1_nx ? npb : pb;
+          const int s1_row0 = s1_nx ? nrow0 : row0;
+          const int s1_rot = s1_nx ? nrot : rot;
+          const int s1_t = s1_in ? t + 1 : (has_next ? 0 : t);
+          const bool s2_in = t + 2 < T, s2_nx = !s2_in && has_next;
+          const int s2_pb = s2_nx ? npb : pb;
+          const int s2_row0 = s2_nx ? nrow0 : row0;
+          const int s2_rot = s2_nx ? nrot : rot;
+          const int s2_t = s2_in ? t + 2 : (has_next ? t + 2 - T : t);
+          stage_c(cn, lds_h[(tc + 1) & 1], s1_pb, s1_rot, s1_t);
+          stage_x(xn1, s1_pb, s1_row0, s1_rot, s1_t, 1);
+          // every staging load stays ahead of the point loads issued below
+          __builtin_amdgcn_sched_barrier(0);
+          uint4 ar[4], br[2][kNF];
+          ar[0] = read_a(cc, 0);
+          ar[1] = read_a(cc, 1);
+          ar[2] = read_a(cc, 2);
+#pragma unroll
+          for (int f = 0; f < kNF; ++f) br[0][f] = read_b(xh0, f, 0);
+#pragma unroll
+          for (int q = 0; q < Q; ++q) {
+            const int sub = q % NSUB, kk = q / NSUB;
+            if (sub == 0 && kk + 1 == 2) {
+              // this chunk's second point half was staged at the start of
+              // the previous chunk; the loads issued since (its first half
+              // of the next chunk, this chunk's centroids and norm, the next
+              // chunk's second half) may still be in flight
+              asm volatile("" ::: "memory");
+              __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * NXL + NCL + 1, 15));
+              asm volatile("" ::: "memory");
+            }
+            if (sub == 0 && kk + 1 < kLKS) {           // the next k-step's point fragments
+#pragma unroll
+              for (int f = 0; f < kNF; ++f)
+                br[(kk + 1) & 1][f] = read_b(kk + 1 < 2 ? xh0 : xh1, f, kk + 1);
+            }
+            if (q + 3 < Q) ar[(q + 3) % 4] = read_a(cc, q + 3);
+#pragma unroll
+            for (int f = 0; f < kNF; ++f)
+              acc[sub][f] = Mfma<DT>::run(ar[q % 4], br[kk & 1][f], acc[sub][f]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q == 2 * NSUB - 1) {
+              // k-steps 0-1 are done: their slot takes step + 2's first half
+              stage_x(P ? xs2 : xs0, s2_pb, s2_row0, s2_rot, s2_t, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          // This wave's centroid and norm loads have landed once at most the
+          // 2 * NXL point loads issued after them are outstanding. The
+          // barrier has no memory fence (a fence would also wait for those
+          // point loads); the empty asm statements keep the compiler from
+          // moving LDS accesses across it.
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * NXL, 0));
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+        }
+      }
+      // scores x.c - ||c||^2/2 (-inf past K), then the running argmax
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        floatx16_t h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = sub * 32 + 8 * i + 4 * half;
+          const float4 hv = *reinterpret_cast<const float4*>(&lds_h[tc & 1][r]);
+          const int left = K - kt * TK - r;       // rows r .. r+3 exist while left > j
+          h[4 * i + 0] = left > 0 ? -0.5f * hv.x : -INFINITY;
+          h[4 * i + 1] = left > 1 ? -0.5f * hv.y : -INFINITY;
+          h[4 * i + 2] = left > 2 ? -0.5f * hv.z : -INFINITY;
+          h[4 * i + 3] = left > 3 ? -0.5f * hv.w : -INFINITY;
+        }
+#pragma unroll
+        for (int f = 0; f < kNF; ++f) argmax_update(acc[sub][f] + h, kt * TK + sub * 32, best[f], bidx[f]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      ++tc;
+    }
+    int32_t* ib = ids + (int64_t)pb * N;
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) {
+      const int idx = merge_halves(best[f], bidx[f], half);
+      const int n = row0 + wave * kWaveRows + f * 32 + r32;
+      if (half == 0 && n < N) ib[n] = idx;
+    }
+    if (!has_next) {
+      // the repeated staging loads of the last chunks still write LDS: let
+      // them land before the block ends
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+      break;
+    }
+    v = vn;
+    pb = npb;
+    row0 = nrow0;
+    rot = nrot;
+    vn = v + nblocks;
+    has_next = vn < total;
+    if (has_next) locate(vn, npb, nrow0, nrot);
+  }
+}
+
 // 16-byte vector loads need rows of whole 8-element vectors and aligned bases.
 bool vec_ok(const void* x, const void* c, int64_t d) {
   return d % 8 == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)c % 16) == 0;
@@ -288,6 +602,28 @@ hipError_t launch_splitd(const uint16_t* x, const uint16_t* c, const float* cn, 
 }
 
 template <int DT, int NSUB>
+hipError_t launch_splitd_lds(const uint16_t* x, const uint16_t* c, const float* cn, int64_t total,
+                             int bpb, int64_t N, int64_t d, int64_t K, int32_t* ids,
+                             hipStream_t s) {
+  static int cache[64];
+  auto kern = assign_splitd_lds_kernel<DT, NSUB>;
+  const int resident = resident_blocks(kern, kThreads, cache);
+  if (resident <= 0) return hipErrorInvalidConfiguration;
+  int64_t nblocks = resident >= 8 ? resident / 8 * 8 : resident;
+  if (nblocks > total) nblocks = total;
+  kern<<<(unsigned)nblocks, kThreads, 0, s>>>(x, c, cn, ids, (int)N, (int)d, (int)K, bpb,
+                                              (int)total, (int)nblocks);
+  return hipGetLastError();
+}
+
+// FK_SPLITD_REGISTER_STAGING=1 keeps whole-row problems on the register-staged
+// kernel (for comparisons; both give the same ids).
+bool force_register_staging() {
+  const char* e = getenv("FK_SPLITD_REGISTER_STAGING");
+  return e && e[0] == '1';
+}
+
+template <int DT, int NSUB>
 hipError_t run_splitd(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
                       int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
   const int bpb = (int)((N + kBN - 1) / kBN);
@@ -295,6 +631,8 @@ hipError_t run_splitd(const void* x, const void* c, const float* cn, int64_t B, 
   if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const uint16_t* xp = (const uint16_t*)x;
   const uint16_t* cp = (const uint16_t*)c;
+  if (vec_ok(x, c, d) && d % (2 * kLC) == 0 && !force_register_staging())
+    return launch_splitd_lds<DT, NSUB>(xp, cp, cn, total, bpb, N, d, K, ids, s);
   if (vec_ok(x, c, d) && d % kDC == 0)
     return launch_splitd<DT, NSUB, true, true>(xp, cp, cn, total, bpb, N, d, K, ids, s);
   if (vec_ok(x, c, d))

@@ -52,6 +52,18 @@ template <> struct Elem<FK_BF16> {
   __device__ static __forceinline__ uint16_t narrow(float f) { return f32_to_bf16_bits(f); }
 };
 
+// Word 3 of a raw (unformatted, stride 0) buffer resource.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// A pointer the caller knows to be the same in every lane, moved to scalar
+// registers (a buffer resource must be scalar).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // 32x32x16 MFMA with fp32 accumulate; A rows = centroids, B cols = points.
 template <int DT> struct Mfma;
 template <> struct Mfma<FK_F16> {

@@ -247,6 +247,11 @@ SIMDS_PER_CU = 4
 STALL_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
                   "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
                   "SQ_VALU_MFMA_COEXEC_CYCLES", "GRBM_GUI_ACTIVE")
+# Third pass (the workload only): how busy the LDS is. SQ_LDS_IDX_ACTIVE
+# counts the cycles each CU's LDS serves indexed reads and writes.
+LDS_COUNTERS = ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL",
+                "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_LDS_STORE_BANDWIDTH",
+                "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_UNALIGNED_STALL", "GRBM_GUI_ACTIVE")
 
 
 def read_dispatch_counters(path):
@@ -290,7 +295,8 @@ def mfma_derived(m, cus, flop_per_launch=None, peak_tflops=None, nominal_mhz=240
       clock (MHz)     = GRBM_GUI_ACTIVE / xcds / kernel duration (us)
       MFMA busy       = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / xcds * CUs * 4 SIMDs)
       achieved        = flop per launch / duration
-      frac at clock   = achieved / (peak * clock / nominal clock)"""
+      frac at clock   = achieved / (peak * clock / nominal clock)
+      LDS busy        = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / xcds * CUs)"""
     d = {}
     g = m.get("GRBM_GUI_ACTIVE")
     dur = m.get("dur_ns")
@@ -301,6 +307,11 @@ def mfma_derived(m, cus, flop_per_launch=None, peak_tflops=None, nominal_mhz=240
         d["mfma_busy"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * SIMDS_PER_CU)
     if cyc and m.get("SQ_VALU_MFMA_COEXEC_CYCLES") is not None:
         d["mfma_coexec"] = m["SQ_VALU_MFMA_COEXEC_CYCLES"] / (cyc * cus * SIMDS_PER_CU)
+    if cyc and m.get("SQ_LDS_IDX_ACTIVE") is not None:
+        d["lds_util"] = m["SQ_LDS_IDX_ACTIVE"] / (cyc * cus)
+        if m.get("SQ_INSTS_LDS_LOAD_BANDWIDTH") is not None:
+            # 64-byte units read per CU per busy cycle
+            d["lds_read_bytes_per_cu_cycle"] = 64 * m["SQ_INSTS_LDS_LOAD_BANDWIDTH"] / (cyc * cus)
     w = m.get("SQ_WAVE_CYCLES")
     if w:
         for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
@@ -326,13 +337,15 @@ def counters_text(cmds, entries, cus, xcds=8):
             f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x {cus} CUs x "
             f"{SIMDS_PER_CU} SIMDs);",
             "frac at clock = achieved / (nominal peak x measured clock / 2400 MHz);",
-            "*_per_wave_cycle = counter / SQ_WAVE_CYCLES (second pass).", ""]
+            "*_per_wave_cycle = counter / SQ_WAVE_CYCLES (second pass);",
+            f"LDS busy = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / {xcds} x {cus} CUs) (third pass).",
+            ""]
     for name, e in entries.items():
         m, dv = e["means"], e["derived"]
         out.append(f"{name}: {short_name(m['kernel'])} ({m['dispatches']} dispatches"
                    + (f", kernel source digest {e['digest']}" if e.get("digest") else "") + ")")
         out.append(f"  duration avg {m.get('dur_ns', 0) / 1e3:.1f} us")
-        for k in dict.fromkeys(MFMA_COUNTERS + STALL_COUNTERS):
+        for k in dict.fromkeys(MFMA_COUNTERS + STALL_COUNTERS + LDS_COUNTERS):
             if k in m:
                 out.append(f"  {k:28s} {m[k]:.6g}")
         for k, v in dv.items():
@@ -358,10 +371,13 @@ def counters_pass(args) -> int:
             "--tol-run", "0"]
     pcmd = ["python3", os.path.join(ROOT, "bench.py"), "--mfma-peak", "--steps", "3",
             "--peak-iters", "4000"]
-    sets = {"mfma": args.counter_list.split(","), "stalls": list(STALL_COUNTERS)}
+    sets = {"mfma": args.counter_list.split(","), "stalls": list(STALL_COUNTERS),
+            "lds": list(LDS_COUNTERS)}
     passes = {}
     for prog, cmd in (("workload", wcmd), ("probe", pcmd)):
         for cset, ctrs in sets.items():
+            if prog == "probe" and cset == "lds":
+                continue                   # the probe touches no LDS
             tag = f"counters_{cset}_{prog}"
             passes[tag] = (["rocprofv3", "--pmc", *ctrs, "--kernel-trace", "--output-format",
                             "csv", "-d", os.path.join(raw, tag), "-o", "run", "--"] + cmd)

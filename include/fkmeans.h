@@ -167,15 +167,19 @@ fk_status_t fk_update_noalloc(const void* x, const int32_t* ids, fk_dtype_t dt,
  * fk_norms, fk_assign, fk_update; stop after iteration t when
  * max_b shift[b] < tol (strict, so tol == 0 runs exactly max_iter iterations).
  *   x (B,N,d) dt, init (B,K,d) dt in; ids (B,N) int32 out (from the last
- *   assignment; all 0 when max_iter == 0); centers (B,K,d) fp32 out (after
- *   the last update); *n_iter (host) = completed iterations.
+ *   assignment; all 0 when max_iter == 0); centers (B,K,d) fp32 in/out:
+ *   after the last update on return; *n_iter (host) = completed iterations.
+ *   init == NULL resumes: the loop starts from the fp32 centres `centers`
+ *   already holds (an earlier call's result), so T iterations and then
+ *   T' more from its centres give bit for bit the results of T + T'
+ *   iterations in one call (a fixed iteration count; with tol > 0 the
+ *   second call's first shift is taken against those same centres).
  * With tol > 0, iteration t + 1 is enqueued before t's shift has reached the
  * host; when t turns out to be the last, the ids and centres of t (kept in
  * the workspace) replace what t + 1 wrote, so the results are exactly those
  * of stopping after t. Deterministic like fk_update (K <= 65536).
- * init is in dt: a run continued from the fp32 centres of an earlier call
- * starts from those centres rounded to dt, so such a resume is approximate
- * (exact when the centres are representable in dt).
+ * Passing an earlier call's centres as init instead, rounded to dt, is an
+ * approximate resume: clusters that stay empty keep the rounded centre.
  * The batched API and its tol argument: [hysenlabs] "Exact K-Means, with the
  * assignment step written in Triton"; one step = one assignment plus one
  * centroid update: [paixiang] "什么是 Flash-KMeans".
@@ -201,6 +205,7 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
  *   centers, n_iter, max_iter, tol and the stop rule as fk_lloyd.
  *   chunk >= 1: points per problem per copy (clamped to N).
  *   ws: fk_workspace_size_host(dt, B, chunk, d, K) bytes, 256-byte aligned.
+ *   init == NULL resumes from `centers` as in fk_lloyd.
  * The call creates one non-blocking copy stream and four events, and
  * returns after all its work is done (it synchronises `stream`). Centroids
  * may differ from fk_lloyd's in the last bits (summation order).

@@ -107,6 +107,12 @@ def test_validation_rejects_before_launch(lib):
     assert call(3, float("nan"), ctypes.byref(n_iter)) == INVALID
     assert call(3, 0.0, None) == INVALID
     assert call(3, 0.0, ctypes.byref(n_iter)) == WORKSPACE and n_iter.value == 0
+    # resume (no init) needs the centres to start from; with them it only
+    # lacks the workspace here
+    assert lib.fk_lloyd(dummy, 1, 1, 16, 8, 4, null, 3, 0.0, dummy, null, ctypes.byref(n_iter),
+                        null, 0, null) == INVALID
+    assert lib.fk_lloyd(dummy, 1, 1, 16, 8, 4, null, 3, 0.0, dummy, dummy, ctypes.byref(n_iter),
+                        null, 0, null) == WORKSPACE
     # empty batch: nothing to do, n_iter = 0
     n_iter.value = 5
     assert lib.fk_lloyd(null, 1, 0, 16, 8, 4, null, 3, 0.0, null, null, ctypes.byref(n_iter),

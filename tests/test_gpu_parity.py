@@ -103,6 +103,11 @@ ASSIGN_CASES = [
     ("f16", 1, 200, 1000, 150, False),
     ("bf16", 1, 150, 2048, 60, False),
     ("f16", 1, 400, 640, 300, False),       # two 256-row K tiles over five d-chunks
+    # direct-to-LDS staging (whole rows, an even number of 128-wide d-chunks):
+    ("bf16", 2, 5000, 768, 700, False),     # three K tiles, the last ragged (188 rows)
+    ("f16", 1, 3000, 512, 257, True),       # forced at d = 512: a one-row last K tile
+    ("bf16", 3, 2100, 1280, 100, False),    # 128-row tiles, ten d-chunks, ragged N
+    ("f16", 2, 70000, 1024, 40, False),     # more point blocks than resident blocks
     ("f16", 2, 1000, 128, 300, True),       # split-D forced at small d
     ("bf16", 1, 500, 60, 130, True),
     ("f32", 1, 2048, 32, 16, False),
@@ -114,6 +119,7 @@ ASSIGN_CASES = [
     ("f32", 1, 500, 100, 70, True),         # fp32 split-D (forced at small d)
     ("f32", 1, 400, 300, 50, False),        # fp32 split-D (d > 256)
     ("f32", 2, 1000, 600, 300, False),      # fp32 split-D, two 256-row K tiles
+    ("f32", 1, 1500, 384, 200, False),      # fp32 split-D with direct-to-LDS staging
     ("f16", 1, 5, 16, 1, False),            # K = 1
     ("f16", 1, 10, 16, 40, False),          # K > N
     ("bf16", 3, 33, 64, 7, False),          # N below one tile
@@ -138,6 +144,33 @@ def test_assign_parity(fk, monkeypatch, dtype, B, N, d, K, force):
     if K >= 2:   # centroid 1 duplicates 0: it wins only where 0 would (an exact tie)
         assert (a.ids[ids == 1] == 0).all()
     print(stats)
+
+
+@pytest.mark.parametrize("dtype,B,N,d,K", [("bf16", 2, 6000, 1024, 256),
+                                             ("f16", 1, 5000, 768, 600),
+                                             ("f32", 1, 3000, 256, 100)])
+def test_splitd_staging_paths_agree(fk, monkeypatch, dtype, B, N, d, K):
+    """Whole-row split-D problems staged straight into LDS and staged through
+    registers (FK_SPLITD_REGISTER_STAGING=1): both against the oracle under
+    the band rule. The two add -||c||^2/2 at different points of the fp32
+    sum, so they may differ only on near-tie rows (in-band for both)."""
+    monkeypatch.setenv("FK_FORCE_SPLITD", "1")
+    seed = stable_seed(dtype, B, N, d, K, "staging")
+    x, _, _ = synthdata.make_mixture(B, N, d, 1, dtype, n_comp=max(2, K // 3), mean_std=1.5,
+                                  seed=seed)
+    x64 = synthdata.to_f64(x, dtype)
+    c_hat = make_centroids(x64, K, dtype, seed + 1)
+    x_dev = to_dev(x, dtype)
+    monkeypatch.delenv("FK_SPLITD_REGISTER_STAGING", raising=False)
+    _, _, ids_lds = gpu_norms_assign(fk, x_dev, c_hat, dtype)
+    monkeypatch.setenv("FK_SPLITD_REGISTER_STAGING", "1")
+    _, _, ids_reg = gpu_norms_assign(fk, x_dev, c_hat, dtype)
+    a = oracle.assign(x64, c_hat, form="expanded")
+    st_lds = check_ids(ids_lds, a, f"split-D LDS staging {dtype} B{B} N{N} d{d} K{K}")
+    st_reg = check_ids(ids_reg, a, f"split-D register staging {dtype} B{B} N{N} d{d} K{K}")
+    differ = int((ids_lds != ids_reg).sum())
+    assert differ <= st_lds["n_band"] + st_reg["n_band"], (differ, st_lds, st_reg)
+    print(st_lds, st_reg, f"rows that differ: {differ}")
 
 
 # ---------------------------------------------------------------------------

@@ -168,3 +168,36 @@ def test_full_size_recipe_lockstep(fk, name, rows, clusters):
         c_prev = c_t
     print(f"{name}: {w.max_iter} iterations in lockstep; in-band flips on sampled rows "
           f"{flips}; n_flip_outside_band = 0")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_resume_from_centres(fk, dtype):
+    """Lloyd's whole state is its fp32 centres: T iterations, then the rest
+    resumed from the returned centres (init=None), equal one run bit for bit,
+    for a fixed iteration count (10 = 4 + 6) and for a tol-stopped run (the
+    resumed call stops at the same iteration). Clusters of thousands of points
+    make the first call end on the long clusters' deferred division and the
+    resumed call start right after it; a centroid far from every point keeps
+    its cluster empty throughout."""
+    x, init, _ = synthdata.make_mixture(2, 30000, 128, 24, dtype, n_comp=12, mean_std=2.0,
+                                        seed=43)
+    init = synthdata.to_f64(init, dtype)
+    init[:, 1] = 64.0                        # cluster 1 never wins a point
+    init = synthdata.from_f64(init, dtype)
+    x_dev, init_dev = to_dev(x, dtype), to_dev(init, dtype)
+    ids10, c10, n = fk.fk_lloyd(x_dev, init_dev, 10, 0.0)
+    assert n == 10
+    _, c4, _ = fk.fk_lloyd(x_dev, init_dev, 4, 0.0)
+    ids_r, c_r, n_r = fk.fk_lloyd(x_dev, None, 6, 0.0, centers=c4.clone())
+    assert n_r == 6
+    assert np.array_equal(ids_r.cpu().numpy(), ids10.cpu().numpy())
+    assert np.array_equal(c_r.cpu().numpy().view(np.uint32), c10.cpu().numpy().view(np.uint32))
+    tol = 1e-3
+    ids_t, c_t, n_t = fk.fk_lloyd(x_dev, init_dev, 100, tol)
+    assert 6 <= n_t < 100, n_t
+    ids_r, c_r, n_r = fk.fk_lloyd(x_dev, None, 100, tol, centers=c4.clone())
+    assert n_r == n_t - 4, (n_t, n_r)
+    assert np.array_equal(ids_r.cpu().numpy(), ids_t.cpu().numpy())
+    assert np.array_equal(c_r.cpu().numpy().view(np.uint32), c_t.cpu().numpy().view(np.uint32))
+    print(f"{dtype}: resume after 4 of 10 iterations and of a tol run of {n_t} iterations: "
+          f"bit-identical")
