@@ -331,6 +331,67 @@ def mfma_peak(fk, torch, args):
     }), flush=True)
 
 
+def contention(fk, torch, synthdata, args):
+    """The update under contention: the large-K shape (B=1, N=2^24, d=128,
+    K=32768, fp16) with cluster ids drawn from Zipf(1.1) (hot clusters: the
+    hottest holds about 2.4M points) against uniform ids (the control), each
+    updated by the sort-inverse fk_update and by the one-atomic-per-element
+    scatter update (libfkbaseline). Update-only: the same x and ids for every
+    call, HIP events on torch's current stream. One JSON line."""
+    dev = torch.device("cuda:0")
+    w = synthdata.make_workload("large_k_zipf")
+    B, N, d, K = w.B, w.N, w.d, w.K
+    x = synthdata.to_torch(w.x, w.dtype).to(dev)
+    fk.load_baseline()
+    c0 = synthdata.to_torch(w.init, w.dtype).to(dev).float()
+    ws = fk.workspace(x.dtype, B, N, d, K, dev)
+    counts = torch.empty((B, K), dtype=torch.int32, device=dev)
+    sums = torch.empty((B, K, d), dtype=torch.float32, device=dev)
+    shift = torch.empty((B,), dtype=torch.float32, device=dev)
+    reps = max(args.steps, 1)
+    x_bytes = B * N * d * elem_bytes(w.dtype)
+    u_bytes = update_bytes(B, N, d, K, elem_bytes(w.dtype))
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    rows = {}
+    for kind, ids_np in (("zipf1.1", synthdata.zipf_ids(B, N, K, seed=7)),
+                         ("uniform", synthdata.uniform_ids(B, N, K, seed=7))):
+        ids = torch.from_numpy(ids_np).to(dev)
+        hot = int(torch.bincount(ids.view(-1).long(), minlength=K).max().item())
+        c = c0.clone()
+        sort_ms = timed(lambda: fk.fk_update(x, ids, c, counts=counts, shift=shift, ws=ws))
+        atomic_ms = timed(lambda: fk.fkb_update_atomic(x, ids, c, counts=counts, sums=sums))
+        rows[kind] = {"hottest_cluster_points": hot,
+                      "sort_inverse_ms": sort_ms, "scatter_atomic_ms": atomic_ms,
+                      "speedup": atomic_ms / sort_ms,
+                      "sort_inverse_frac_of_hbm": u_bytes / (sort_ms * 1e-3) / 1e9 / PEAK_HBM,
+                      "scatter_atomic_effective_GBps": x_bytes / (atomic_ms * 1e-3) / 1e9}
+        del ids
+    z = rows["zipf1.1"]
+    print(json.dumps({
+        "metric": "update under contention: sort-inverse vs scatter-atomic, ms per update",
+        "value": z["sort_inverse_ms"], "unit": "ms", "n_gpus": 1, "steps": reps,
+        "warmup": max(args.warmup, 1), "ms_per_step": z["sort_inverse_ms"],
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"large-K update: B={B} N={N} d={d} K={K} {w.dtype}, "
+                               "Zipf(1.1) ids vs uniform ids", "B": B, "N": N, "d": d, "K": K},
+        "variants": rows,
+        "algorithmic_bytes_per_update": u_bytes,
+    }), flush=True)
+
+
 def copy_calibration(mib: int, dev):
     """A plain elementwise kernel over a buffer of known size, for scaling
     the HBM byte counters (reads and writes mib MiB each)."""
@@ -370,6 +431,9 @@ def main():
                     help="instead: the MFMA peak probe (--steps timed launches)")
     ap.add_argument("--peak-iters", type=int, default=20000,
                     help="loop iterations (32 MFMAs each) per wave of the MFMA peak probe")
+    ap.add_argument("--contention", action="store_true",
+                    help="instead: the update under contention at the large-K shape (Zipf(1.1) "
+                         "ids against uniform ids, sort-inverse against scatter-atomic)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -390,6 +454,9 @@ def main():
         return
     if args.host_sweep:
         host_sweep(fk, torch, synthdata, args)
+        return
+    if args.contention:
+        contention(fk, torch, synthdata, args)
         return
     w = synthdata.make_workload(args.workload)
     if args.host_stream > 0:

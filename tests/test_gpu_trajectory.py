@@ -28,7 +28,7 @@ import pytest
 
 import oracle
 import synthdata
-from gpu_helpers import CENTROID_RTOL, centroid_rel_err, check_ids, to_dev
+from gpu_helpers import CENTROID_RTOL, centroid_rel_err, check_ids, f64_to_storage, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -183,7 +183,7 @@ def test_resume_from_centres(fk, dtype):
                                         seed=43)
     init = synthdata.to_f64(init, dtype)
     init[:, 1] = 64.0                        # cluster 1 never wins a point
-    init = synthdata.from_f64(init, dtype)
+    init = f64_to_storage(init, dtype)
     x_dev, init_dev = to_dev(x, dtype), to_dev(init, dtype)
     ids10, c10, n = fk.fk_lloyd(x_dev, init_dev, 10, 0.0)
     assert n == 10
