@@ -392,6 +392,119 @@ def contention(fk, torch, synthdata, args):
     }), flush=True)
 
 
+SMALL_TILES = ("8w128", "4w128", "4w64")
+SPLIT_TILES = ("lds8", "lds4", "reg8", "reg4")
+
+
+def tile_sweep(fk, torch, args):
+    """Every assign tile candidate (FK_TILE) timed on a grid of shapes: the
+    small-D tiles over d in {32, 64, 128} (fp16), the split-D tiles over d in
+    {768, 1024} (bf16), K and the number of points. One JSON line per shape
+    with each candidate's ms and the fastest; the dispatch table comes from
+    these lines. Points and centroids are seeded N(0,1) draws (timing only)."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    grids = []
+    for d in (32, 64, 128):
+        for K in (64, 256, 1024, 4096):
+            for B, N in ((1, 16384), (1, 65536), (4, 65536), (32, 75600)):
+                grids.append(("f16", B, N, d, K, SMALL_TILES))
+    for d in (768, 1024):
+        for K in (64, 256, 1000):
+            for B, N in ((1, 16384), (8, 32768)):
+                grids.append(("bf16", B, N, d, K, SPLIT_TILES))
+    reps = max(args.steps, 1)
+    old = os.environ.get("FK_TILE")
+    for dt, B, N, d, K, tiles in grids:
+        tdt = torch.float16 if dt == "f16" else torch.bfloat16
+        x = torch.randn((B, N, d), generator=gen, device=dev).to(tdt)
+        c = torch.randn((B, K, d), generator=gen, device=dev)
+        c_lp, cn = fk.fk_norms(c, tdt)
+        ids = torch.empty((B, N), dtype=torch.int32, device=dev)
+        row = {}
+        for t in tiles:
+            os.environ["FK_TILE"] = t
+            fk.fk_assign(x, c_lp, cn, ids=ids)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fk.fk_assign(x, c_lp, cn, ids=ids)
+            e1.record()
+            e1.synchronize()
+            row[t] = e0.elapsed_time(e1) / reps
+        best = min(row, key=row.get)
+        print(json.dumps({"dtype": dt, "B": B, "N": N, "d": d, "K": K, "ms": row, "best": best,
+                          "tflops_best": assign_flop(B, N, d, K) / (row[best] * 1e-3) / 1e12}),
+              flush=True)
+        del x, c, c_lp, cn, ids
+    if old is None:
+        os.environ.pop("FK_TILE", None)
+    else:
+        os.environ["FK_TILE"] = old
+
+
+def shard_step(fk, torch, synthdata, args):
+    """One GPU's part of a data-parallel iteration at the workload's shape:
+    N / shards rows of every problem (the recipe at the shard's size: a
+    contiguous block, as each GPU would hold), full K: norms, assign, and the shard-local update that
+    adds per-cluster sums and counts undivided (fk_update_partial), the
+    input of one all-reduce of K*d + K values per problem. One JSON line."""
+    dev = torch.device("cuda:0")
+    N0 = synthdata.SHAPES[args.workload][1]
+    w = synthdata.make_workload(args.workload, scale_n=N0 // args.shard)   # the shard's rows
+    B, N, d, K = w.B, w.N, w.d, w.K
+    x = synthdata.to_torch(w.x, w.dtype).to(dev)
+    c = synthdata.to_torch(w.init, w.dtype).to(dev).float()
+    ids = torch.empty((B, N), dtype=torch.int32, device=dev)
+    sums = torch.empty((B, K, d), dtype=torch.float32, device=dev)
+    counts = torch.empty((B, K), dtype=torch.int32, device=dev)
+    ws = fk.workspace(x.dtype, B, N, d, K, dev)
+    reps = max(args.steps, 1)
+
+    def step():
+        c_lp, cn = fk.fk_norms(c, x.dtype)
+        fk.fk_assign(x, c_lp, cn, ids=ids)
+        sums.zero_()
+        counts.zero_()
+        fk.fk_update_partial(x, ids, sums, counts, ws=ws)
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    c_lp, cn = fk.fk_norms(c, x.dtype)
+    a_ms = timed(lambda: fk.fk_assign(x, c_lp, cn, ids=ids))
+    u_ms = timed(lambda: fk.fk_update_partial(x, ids, sums, counts, ws=ws))
+    s_ms = timed(step)
+    s_el = elem_bytes(w.dtype)
+    flop = assign_flop(B, N, d, K)
+    print(json.dumps({
+        "metric": "one shard's step: norms + assign + partial-sum update, ms",
+        "value": s_ms, "unit": "ms", "n_gpus": 1, "steps": reps, "warmup": max(args.warmup, 1),
+        "ms_per_step": s_ms, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.workload}, shard 1 of {args.shard}: B={B} N={N} d={d} "
+                               f"K={K} {w.dtype}", "B": B, "N": N, "d": d, "K": K,
+                   "shards": args.shard},
+        "assign_ms": a_ms, "assign_tflops": flop / (a_ms * 1e-3) / 1e12,
+        "assign_frac_of_mfma_peak": flop / (a_ms * 1e-3) / 1e12 / PEAK_MFMA_F16,
+        "partial_update_ms": u_ms,
+        "partial_update_frac_of_hbm": update_bytes(B, N, d, K, s_el) / (u_ms * 1e-3) / 1e9 /
+        PEAK_HBM,
+        "allreduce_payload_bytes": B * (K * d + K) * 4,
+    }), flush=True)
+
+
 def copy_calibration(mib: int, dev):
     """A plain elementwise kernel over a buffer of known size, for scaling
     the HBM byte counters (reads and writes mib MiB each)."""
@@ -431,6 +544,12 @@ def main():
                     help="instead: the MFMA peak probe (--steps timed launches)")
     ap.add_argument("--peak-iters", type=int, default=20000,
                     help="loop iterations (32 MFMAs each) per wave of the MFMA peak probe")
+    ap.add_argument("--shard", type=int, default=0, metavar="S",
+                    help="instead: one shard's step (N/S rows per problem, full K) of the workload: "
+                         "norms, assign and the partial-sum update")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="instead: every assign tile candidate timed over a grid of shapes "
+                         "(one JSON line per shape)")
     ap.add_argument("--contention", action="store_true",
                     help="instead: the update under contention at the large-K shape (Zipf(1.1) "
                          "ids against uniform ids, sort-inverse against scatter-atomic)")
@@ -457,6 +576,12 @@ def main():
         return
     if args.contention:
         contention(fk, torch, synthdata, args)
+        return
+    if args.tile_sweep:
+        tile_sweep(fk, torch, args)
+        return
+    if args.shard > 0:
+        shard_step(fk, torch, synthdata, args)
         return
     w = synthdata.make_workload(args.workload)
     if args.host_stream > 0:

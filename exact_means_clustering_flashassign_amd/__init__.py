@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     fk_trace_end,
     fk_update,
     fk_update_noalloc,
+    fk_update_partial,
     FK_NOALLOC_SCRATCH_BYTES,
     fk_version,
     fk_workspace_size,

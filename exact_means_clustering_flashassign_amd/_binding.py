@@ -51,6 +51,8 @@ def load(path: Optional[str] = None):
         "fk_assign": (ctypes.c_int, [P, P, P, ctypes.c_int, I64, I64, I64, I64, P, P]),
         "fk_update": (ctypes.c_int, [P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, P, SZ, P]),
         "fk_update_noalloc": (ctypes.c_int, [P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, P]),
+        "fk_update_partial": (ctypes.c_int, [P, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, SZ,
+                                             P]),
         "fk_lloyd": (ctypes.c_int, [P, ctypes.c_int, I64, I64, I64, I64, P, I32, ctypes.c_float,
                                     P, P, ctypes.POINTER(I32), P, SZ, P]),
         "fk_workspace_size_host": (SZ, [ctypes.c_int, I64, I64, I64, I64]),
@@ -203,6 +205,23 @@ def fk_update_noalloc(x, ids, c, counts, shift):
                                   _dev(shift, "shift", torch.float32, (B,)), _stream(x))
     _check(st, "fk_update_noalloc")
     return c, counts, shift
+
+
+def fk_update_partial(x, ids, sums, counts, ws=None):
+    """Add this block of points' per-cluster sums (B,K,d) fp32 and counts
+    (B,K) int32 into sums and counts (one shard's part of an update)."""
+    torch = _torch()
+    code = dtype_code(x.dtype)
+    B, N, d = x.shape
+    K = sums.shape[1]
+    if ws is None:
+        ws = workspace(x.dtype, B, N, d, K, x.device)
+    st = load().fk_update_partial(_dev(x, "x"), _dev(ids, "ids", torch.int32, (B, N)), code, B,
+                                  N, d, K, _dev(sums, "sums", torch.float32, (B, K, d)),
+                                  _dev(counts, "counts", torch.int32, (B, K)),
+                                  _dev(ws, "ws", torch.uint8), ws.numel(), _stream(x))
+    _check(st, "fk_update_partial")
+    return sums, counts
 
 
 def fk_lloyd(x, init, max_iter: int, tol: float, ids=None, centers=None, ws=None):

@@ -313,6 +313,22 @@ fk_status_t fk_update_noalloc(const void* x, const int32_t* ids, fk_dtype_t dt, 
   return hip_status(e);
 }
 
+fk_status_t fk_update_partial(const void* x, const int32_t* ids, fk_dtype_t dt, int64_t B,
+                              int64_t N, int64_t d, int64_t K, float* sums, int32_t* counts,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dt(dt) || !valid_sizes(B, N, d, K)) return FK_ERR_INVALID;
+  if (B > 0 && (!sums || !counts)) return FK_ERR_INVALID;
+  if (B * N > 0 && (!x || !ids)) return FK_ERR_INVALID;
+  if (B == 0 || N == 0) return FK_OK;
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < fk_workspace_size(dt, B, N, d, K))
+    return FK_ERR_WORKSPACE;
+  const LloydWs w = carve_lloyd(ws, dt, B, N, d, K);
+  const hipError_t e = fk::launch_update_accumulate(x, ids, dt, B, N, d, K, sums, counts,
+                                                    w.counts, w.upd, stream);
+  if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
+  return hip_status(e);
+}
+
 fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t d, int64_t K,
                      const void* init, int32_t max_iter, float tol, int32_t* ids, float* centers,
                      int32_t* n_iter, void* ws, size_t ws_bytes, hipStream_t stream) {

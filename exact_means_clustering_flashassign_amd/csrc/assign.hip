@@ -30,6 +30,8 @@
 // The split-D path (d > 512 units: fp16/bf16 d > 512, fp32 d > 256) lives in
 // assign_splitd.hip.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "fk_internal.hpp"
 
@@ -172,12 +174,14 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   // win. Loads and stores are unconditional (tile indices clamp, every
   // thread owns an lds_h slot) so one tile iteration is a single basic block
   // the scheduler can interleave.
-  // Buffer resources over (at most) 32 whole rows from base: rows at or past
-  // the end of the data read as zero (a raw buffer's range check) instead of
-  // being clamped, and the per-lane offsets are constants of the kernel, so
-  // the loads cost no per-load 64-bit address registers.
-  auto rows_rsrc = [&](const void* base, int rows_left, int row_bytes) {
-    const int n = min(max(rows_left, 0), 32) * row_bytes;
+  // Buffer resources over at most `cap` whole rows from base (the rows one
+  // load instruction covers: a point fragment's 32, or a staging load's
+  // NT / VPR): rows at or past the end of the data read as zero (a raw
+  // buffer's range check) instead of being clamped, and the per-lane offsets
+  // are constants of the kernel, so the loads cost no per-load 64-bit
+  // address registers.
+  auto rows_rsrc = [&](const void* base, int rows_left, int row_bytes, int cap) {
+    const int n = min(max(rows_left, 0), cap) * row_bytes;
     return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), 0,
                                              __builtin_amdgcn_readfirstlane(n), kRawBufferWord3);
   };
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
         const int r0 = t * TK + q * (NT / VPR);
         pre[q] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       rows_rsrc(cb + (int64_t)r0 * d, K - r0, d * 2), cvo, 0, 0));
+                       rows_rsrc(cb + (int64_t)r0 * d, K - r0, d * 2, NT / VPR), cvo, 0, 0));
       }
     } else {
 #pragma unroll
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   // block's first subtile.
   const uint32_t xvo = (uint32_t)(r32 * d + half * 8) * 2;   // lane's bytes within a fragment
   auto frag_rsrc = [&](int pb, int row0, int f) {
-    return rows_rsrc(x + ((int64_t)pb * N + row0 + f * 32) * d, N - (row0 + f * 32), d * 2);
+    return rows_rsrc(x + ((int64_t)pb * N + row0 + f * 32) * d, N - (row0 + f * 32), d * 2, 32);
   };
   uint4 xn[NF][XP > 0 ? XP : 1];
   auto prefetch_x = [&](int pb, int row0) {
@@ -472,22 +476,77 @@ hipError_t run_smalld(const void* x, const void* c, const float* cn, int64_t B, 
   return launch_smalld<DT, KS, NF, TK, WAVES, false, false, false>(xp, cp, cn, total, bpb, N, d, K, ids, s);
 }
 
+// Tile candidates for rows of up to 128 16-bit units (k-steps KS, two point
+// fragments per wave): 8-wave blocks with 128-row centroid tiles (a ring of
+// four tile buffers once a point block has two tiles or more), 4-wave blocks
+// with 128-row tiles, 4-wave blocks with 64-row tiles. Eight waves share each
+// staged tile among 512 points, half the staging work per MFMA of four; four
+// waves make twice as many point blocks, which fills the GPU when there are
+// few points.
+enum SmallTile { kTile8w128 = 0, kTile4w128 = 1, kTile4w64 = 2, kSmallTiles = 3 };
+const char* const kSmallTileNames[kSmallTiles] = {"8w128", "4w128", "4w64"};
+
+template <int DT, int KS>
+hipError_t run_small_tile(int tile, const void* x, const void* c, const float* cn, int64_t B,
+                          int64_t N, int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
+  if (tile == kTile4w128) return run_smalld<DT, KS, 2, 128, 4>(x, c, cn, B, N, d, K, ids, s);
+  if (tile == kTile4w64) return run_smalld<DT, KS, 2, 64, 4>(x, c, cn, B, N, d, K, ids, s);
+  return run_smalld<DT, KS, 2, 128, 8>(x, c, cn, B, N, d, K, ids, s);
+}
+
+// The tile a problem shape gets (rows of `units` 16-bit units, units <= 128),
+// read off the timing sweep of every candidate over d in {32, 64, 128}, K in
+// {64 .. 4096} and 16K .. 2.4M points (bench.py --tile-sweep):
+//   - 128-unit rows: 8-wave blocks once their 512-point blocks cover every
+//     CU; with fewer points, 4-wave blocks with 128-row tiles (twice the
+//     blocks: up to 1.4x faster at 16K-64K points);
+//   - 64-unit rows: 64-row tiles for K < 256; above, 128-row 4-wave tiles,
+//     8-wave blocks only for K >= 1024 with 512-point blocks on at least
+//     twice the CUs (within 5% of each other there);
+//   - 32-unit rows: 64-row tiles for K < 256, 128-row 4-wave tiles above
+//     (up to 1.3x at K = 4096).
+// FK_TILE=<name> forces a candidate.
+int small_tile(int64_t units, int64_t K, int64_t B, int64_t N) {
+  if (const char* e = getenv("FK_TILE")) {
+    for (int i = 0; i < kSmallTiles; ++i)
+      if (strcmp(e, kSmallTileNames[i]) == 0) return i;
+  }
+  const int64_t blocks8 = B * ((N + 511) / 512);    // point blocks of the 8-wave tile
+  const int64_t cus = device_cus() > 0 ? device_cus() : 256;
+  if (units > 64) return blocks8 >= cus ? kTile8w128 : kTile4w128;
+  if (K < 256) return kTile4w64;
+  if (units > 32 && K >= 1024 && blocks8 >= 2 * cus) return kTile8w128;
+  return kTile4w128;
+}
+
 // Shapes per d: k-steps KS (16 elements each), point fragments NF per wave,
-// tile rows TK, waves per block. d <= 128 uses 8-wave blocks with 128-row
-// tiles: each staged tile feeds 512 points, half the staging work per MFMA
-// of 4-wave blocks with 64-row tiles.
+// tile rows TK, waves per block; rows of up to 128 units take the tile the
+// table above picks.
 template <int DT>
 hipError_t smalld_dt(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
                      int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
-  if (d <= 32) return run_smalld<DT, 2, 2, 64, 4>(x, c, cn, B, N, d, K, ids, s);
-  if (d <= 64) return run_smalld<DT, 4, 2, 64, 4>(x, c, cn, B, N, d, K, ids, s);
-  if (d <= 128) return run_smalld<DT, 8, 2, 128, 8>(x, c, cn, B, N, d, K, ids, s);
+  if (d <= 128) {
+    const int tile = small_tile(d, K, B, N);
+    if (d <= 32) return run_small_tile<DT, 2>(tile, x, c, cn, B, N, d, K, ids, s);
+    if (d <= 64) return run_small_tile<DT, 4>(tile, x, c, cn, B, N, d, K, ids, s);
+    return run_small_tile<DT, 8>(tile, x, c, cn, B, N, d, K, ids, s);
+  }
   if (d <= 256) return run_smalld<DT, 16, 2, 64, 4>(x, c, cn, B, N, d, K, ids, s);
   if (d <= 512) return run_smalld<DT, 32, 1, 64, 4>(x, c, cn, B, N, d, K, ids, s);
   return hipErrorNotSupported;
 }
 
 }  // namespace
+
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0 &&
+      hipDeviceGetAttribute(&cache[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cache[dev] = 0;
+  return cache[dev];
+}
 
 // The small-D tiles fit LDS for every d <= 512 16-bit units (largest:
 // 2 x 32 x 520 x 2 B); an fp32 row of d elements is 2d units.

@@ -25,6 +25,8 @@
 // At the last chunk of a K tile the accumulators are scanned for each lane's
 // best score and row, then reloaded with -||c||^2/2 of the next tile's rows.
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <type_traits>
 
@@ -616,22 +618,45 @@ hipError_t launch_splitd_lds(const uint16_t* x, const uint16_t* c, const float* 
   return hipGetLastError();
 }
 
-// FK_SPLITD_REGISTER_STAGING=1 keeps whole-row problems on the register-staged
-// kernel (for comparisons; both give the same ids).
-bool force_register_staging() {
-  const char* e = getenv("FK_SPLITD_REGISTER_STAGING");
-  return e && e[0] == '1';
+// Split-D tile candidates: the centroid tile (256 or 128 rows) and the
+// staging (straight into LDS, for whole rows with d a multiple of 128; else
+// through registers). FK_TILE=<name> forces one (where it applies);
+// FK_SPLITD_REGISTER_STAGING=1 keeps whole-row problems on register staging.
+enum SplitTile { kSplitLds8 = 0, kSplitLds4 = 1, kSplitReg8 = 2, kSplitReg4 = 3, kSplitTiles = 4 };
+const char* const kSplitTileNames[kSplitTiles] = {"lds8", "lds4", "reg8", "reg4"};
+
+// The staging and tile rows a problem gets, read off the timing sweep of
+// the four candidates over d in {768, 1024}, K in {64, 256, 1000} and 16K ..
+// 262K points (bench.py --tile-sweep): 128-row tiles for K <= 128 (one tile:
+// up to 1.4x faster), 256-row tiles above (x is read once for K <= 256); LDS
+// staging once the 256-point blocks cover every CU (up to 1.3x), register
+// staging below that (up to 1.1x). FK_TILE or FK_SPLITD_REGISTER_STAGING
+// override.
+void split_tile(int64_t K, int64_t blocks, bool& lds, bool& rows128) {
+  const int64_t cus = device_cus() > 0 ? device_cus() : 256;
+  rows128 = K <= 128;
+  lds = rows128 || blocks >= cus;
+  if (const char* e = getenv("FK_TILE")) {
+    for (int i = 0; i < kSplitTiles; ++i)
+      if (strcmp(e, kSplitTileNames[i]) == 0) {
+        lds = i == kSplitLds8 || i == kSplitLds4;
+        rows128 = i == kSplitLds4 || i == kSplitReg4;
+        return;
+      }
+  }
+  const char* r = getenv("FK_SPLITD_REGISTER_STAGING");
+  if (r && r[0] == '1') lds = false;
 }
 
 template <int DT, int NSUB>
 hipError_t run_splitd(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
-                      int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
+                      int64_t d, int64_t K, int32_t* ids, bool lds, hipStream_t s) {
   const int bpb = (int)((N + kBN - 1) / kBN);
   const int64_t total = B * bpb;
   if (total > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const uint16_t* xp = (const uint16_t*)x;
   const uint16_t* cp = (const uint16_t*)c;
-  if (vec_ok(x, c, d) && d % (2 * kLC) == 0 && !force_register_staging())
+  if (lds && vec_ok(x, c, d) && d % (2 * kLC) == 0)
     return launch_splitd_lds<DT, NSUB>(xp, cp, cn, total, bpb, N, d, K, ids, s);
   if (vec_ok(x, c, d) && d % kDC == 0)
     return launch_splitd<DT, NSUB, true, true>(xp, cp, cn, total, bpb, N, d, K, ids, s);
@@ -642,14 +667,15 @@ hipError_t run_splitd(const void* x, const void* c, const float* cn, int64_t B, 
   return hipErrorNotSupported;
 }
 
-// K <= 128: one 128-row tile; otherwise 256-row tiles. Element-wise loads
-// (unaligned or d % 8 != 0) keep 128-row tiles: with 256 the accumulators
-// leave no registers for them.
+// Element-wise loads (unaligned or d % 8 != 0) keep 128-row tiles: with 256
+// the accumulators leave no registers for them.
 template <int DT>
 hipError_t splitd_dt(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
                      int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
-  if (K <= 128 || !vec_ok(x, c, d)) return run_splitd<DT, 4>(x, c, cn, B, N, d, K, ids, s);
-  return run_splitd<DT, 8>(x, c, cn, B, N, d, K, ids, s);
+  bool lds, rows128;
+  split_tile(K, B * ((N + kBN - 1) / kBN), lds, rows128);
+  if (rows128 || !vec_ok(x, c, d)) return run_splitd<DT, 4>(x, c, cn, B, N, d, K, ids, lds, s);
+  return run_splitd<DT, 8>(x, c, cn, B, N, d, K, ids, lds, s);
 }
 
 }  // namespace

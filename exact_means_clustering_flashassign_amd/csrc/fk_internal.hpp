@@ -259,6 +259,8 @@ hipError_t launch_widen(const void* src, float* dst, int dt, int64_t count, hipS
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t count, hipStream_t s);
 
 // Assignment paths. Each returns hipErrorNotSupported when it cannot run the shape.
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus();
 bool smalld_supported(int dt, int64_t d);
 hipError_t launch_assign_smalld(const void* x, const void* c_lp, const float* cnorm, int dt,
                                 int64_t B, int64_t N, int64_t d, int64_t K, int32_t* ids,

@@ -163,6 +163,25 @@ fk_status_t fk_update_noalloc(const void* x, const int32_t* ids, fk_dtype_t dt,
                               float* c, int32_t* counts, float* shift, hipStream_t stream);
 
 /*
+ * One shard's part of a data-parallel update: the points of this call are
+ * one contiguous block of each problem's rows, and their per-cluster sums
+ * and counts are added to sums and counts, undivided; once every shard has
+ * added its part (an all-reduce of K*d + K values per problem), dividing
+ * gives the centroids. Same sort-inverse path as fk_update (per-cluster
+ * segments reduced on chip), with the segment sums added to sums.
+ * [hysenlabs] "Multi-GPU scaling without a NCCL dependency" (contiguous
+ * blocks of points per GPU, partial sums reduced across GPUs).
+ *   x (B,N,d) dt, ids (B,N) int32 in; sums (B,K,d) fp32, counts (B,K) int32
+ *   in/out (accumulated; zero them before the first shard).
+ *   ws: fk_workspace_size(dt, B, N, d, K) bytes, 256-byte aligned.
+ * Sums are fp32 adds in a fixed order per call (deterministic for K <=
+ * 65536); adding into non-zero sums rounds once more per call.
+ */
+fk_status_t fk_update_partial(const void* x, const int32_t* ids, fk_dtype_t dt, int64_t B,
+                              int64_t N, int64_t d, int64_t K, float* sums, int32_t* counts,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Lloyd's loop: centers <- init (widened to fp32); then for t < max_iter:
  * fk_norms, fk_assign, fk_update; stop after iteration t when
  * max_b shift[b] < tol (strict, so tol == 0 runs exactly max_iter iterations).

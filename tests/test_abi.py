@@ -107,6 +107,12 @@ def test_validation_rejects_before_launch(lib):
     assert call(3, float("nan"), ctypes.byref(n_iter)) == INVALID
     assert call(3, 0.0, None) == INVALID
     assert call(3, 0.0, ctypes.byref(n_iter)) == WORKSPACE and n_iter.value == 0
+    # shard-local partial update: sums and counts required, then the workspace
+    assert lib.fk_update_partial(dummy, dummy, 1, 1, 16, 8, 4, null, dummy, dummy, 1 << 20,
+                                 null) == INVALID
+    assert lib.fk_update_partial(dummy, dummy, 1, 1, 16, 8, 4, dummy, dummy, null, 0,
+                                 null) == WORKSPACE
+    assert lib.fk_update_partial(null, null, 1, 0, 16, 8, 4, null, null, null, 0, null) == 0
     # resume (no init) needs the centres to start from; with them it only
     # lacks the workspace here
     assert lib.fk_lloyd(dummy, 1, 1, 16, 8, 4, null, 3, 0.0, dummy, null, ctypes.byref(n_iter),

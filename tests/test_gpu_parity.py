@@ -98,6 +98,8 @@ ASSIGN_CASES = [
     ("bf16", 1, 400, 255, 90, False),
     ("f16", 1, 300, 500, 70, False),
     ("bf16", 1, 300, 512, 33, False),
+    ("f16", 2, 1500, 32, 90, False),        # whole 32-unit rows: 64 rows per staging load
+    ("bf16", 1, 3000, 64, 300, False),      # whole 64-unit rows, three tiles
     ("bf16", 1, 300, 513, 40, False),       # split-D from here on
     ("bf16", 2, 1000, 1024, 256, False),
     ("f16", 1, 200, 1000, 150, False),
@@ -510,3 +512,70 @@ def test_trace_records_phases(fk):
     tr = fk.fk_trace_end()
     assert tr["iterations"] == 5
     assert tr["assign_ms"] > 0 and tr["update_ms"] > 0 and tr["norms_ms"] > 0
+
+
+# ---------------------------------------------------------------------------
+# tile candidates (FK_TILE) and the shard-local partial update
+# ---------------------------------------------------------------------------
+TILE_CASES = [
+    # tile, dtype, B, N, d, K
+    ("8w128", "f16", 2, 3000, 128, 1000),     # the ring: eight tiles per point block
+    ("8w128", "bf16", 1, 5000, 64, 300),      # 64-unit rows, three tiles, ragged K
+    ("8w128", "f16", 1, 2100, 32, 100),       # one tile (no ring), ragged N
+    ("4w128", "f16", 2, 3000, 128, 1000),
+    ("4w128", "bf16", 3, 2500, 40, 257),      # column-padded rows, a one-row last tile
+    ("4w128", "f32", 1, 2000, 64, 200),       # fp32: 128-unit rows
+    ("4w64", "f16", 2, 3000, 128, 1000),
+    ("4w64", "bf16", 1, 5000, 64, 65),
+    ("4w64", "f16", 1, 700, 17, 130),
+    ("lds8", "bf16", 2, 3000, 1024, 300),     # split-D candidates
+    ("lds4", "bf16", 2, 3000, 1024, 300),     # 128-row tiles: three K tiles
+    ("reg8", "f16", 1, 2000, 768, 600),
+    ("reg4", "f16", 1, 2000, 640, 200),
+    ("lds4", "f32", 1, 1500, 384, 100),
+]
+
+
+@pytest.mark.parametrize("tile,dtype,B,N,d,K", TILE_CASES)
+def test_assign_tile_candidates(fk, monkeypatch, tile, dtype, B, N, d, K):
+    """Each tile candidate the dispatch table can pick, forced with FK_TILE,
+    against the oracle (band rule)."""
+    monkeypatch.setenv("FK_TILE", tile)
+    monkeypatch.delenv("FK_FORCE_SPLITD", raising=False)
+    seed = stable_seed(tile, dtype, B, N, d, K)
+    x, _, _ = synthdata.make_mixture(B, N, d, 1, dtype, n_comp=max(2, K // 3), mean_std=1.5,
+                                  seed=seed)
+    x64 = synthdata.to_f64(x, dtype)
+    c_hat = make_centroids(x64, K, dtype, seed + 1)
+    _, _, ids = gpu_norms_assign(fk, to_dev(x, dtype), c_hat, dtype)
+    a = oracle.assign(x64, c_hat, form="direct" if N * K * d < 2e7 else "expanded")
+    print(tile, check_ids(ids, a, f"tile {tile} {dtype} B{B} N{N} d{d} K{K}"))
+
+
+@pytest.mark.parametrize("dtype,B,N,d,K,shards", [("f16", 2, 30000, 128, 300, 3),
+                                                   ("bf16", 1, 50000, 1024, 64, 4),
+                                                   ("f32", 1, 9000, 33, 5, 2)])
+def test_update_partial_over_shards(fk, dtype, B, N, d, K, shards):
+    """fk_update_partial on contiguous row blocks (ragged), accumulated into
+    zeroed sums and counts: counts equal the oracle's bit for bit, the means
+    sums/counts are within 2e-3 of the oracle's centroids."""
+    torch = _torch()
+    seed = stable_seed(dtype, B, N, d, K, shards)
+    x, _, _ = synthdata.make_mixture(B, N, d, 1, dtype, n_comp=8, mean_std=1.0, seed=seed)
+    x64 = synthdata.to_f64(x, dtype)
+    ids = _ids("zipf", B, N, K, seed + 1)
+    bounds = np.linspace(0, N, shards + 1).astype(int)
+    bounds[1:-1] += 7                             # ragged blocks
+    sums = torch.zeros((B, K, d), dtype=torch.float32, device="cuda")
+    counts = torch.zeros((B, K), dtype=torch.int32, device="cuda")
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        xs = to_dev(np.ascontiguousarray(x[:, lo:hi]), dtype)
+        fk.fk_update_partial(xs, torch.from_numpy(np.ascontiguousarray(ids[:, lo:hi])).cuda(),
+                             sums, counts)
+    torch.cuda.synchronize()
+    u = oracle.update(x64, ids, np.zeros((B, K, d)))
+    np.testing.assert_array_equal(counts.cpu().numpy(), u.counts)
+    ne = u.counts > 0
+    means = sums.cpu().numpy()[ne] / u.counts[ne][:, None]
+    err = centroid_rel_err(means[None], u.centers[ne][None])
+    assert err <= CENTROID_RTOL, err
