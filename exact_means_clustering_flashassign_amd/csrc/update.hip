@@ -960,7 +960,17 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + wv;
   if (wid >= total_waves) return;                // whole wave; no block barrier follows
   const int per_batch = runs * slices;
-  const int b = (int)(wid / per_batch);
+  // Problems in the order that finds the most of x still in the memory-side
+  // cache (MALL): the assign walks each XCD's contiguous eighth of the
+  // (problem, point block) range in order, so the last problem of every
+  // eighth was read last; take those first, then the ones before them. The
+  // next assign then starts on the problems read last here.
+  int b = (int)(wid / per_batch);
+  const int64_t nb = total_waves / per_batch;
+  if (nb % 8 == 0) {
+    const int b8 = (int)(nb / 8);
+    b = (b % 8) * b8 + (b8 - 1 - b / 8);
+  }
   const int rem = (int)(wid % per_batch);
   const int run = rem / slices, slice = rem % slices;
   const int p0 = run * kSegRun;
