@@ -195,9 +195,10 @@ __device__ __forceinline__ bool is_long(int lo, int hi) { return hi - lo > kSegR
 // of Q1 rows 32i .. 32i+31 in order; each exists only for full blocks. A long
 // cluster with positions [lo, hi) then sums to
 //   slot1[lo/256] + (slot0 of runs lo/256+1 .. (hi-1)/256, in run order)
-// where whole aligned blocks of 32 (1024) runs are taken from Q1 (Q2). The
-// order depends only on lo and hi, so the result does not depend on how the
-// GPU schedules its waves.
+// where whole aligned blocks of 32 (1024) runs are taken from Q1 (Q2) when a
+// problem has more than kPieceDirectRuns runs (else every piece is added in
+// run order). The order depends only on lo, hi and the problem size, so the
+// result does not depend on how the GPU schedules its waves.
 constexpr int kQ1 = 32;     // runs per Q1 block
 constexpr int kQ2 = 32;     // Q1 blocks per Q2 block
 
@@ -206,7 +207,12 @@ struct LongPieces {
   const float* q1 = nullptr;       // (B, nq1, d)
   const float* q2 = nullptr;       // (B, nq2, d)
   int runs = 0, nq1 = 0, nq2 = 0;
+  bool blocks = true;              // Q1/Q2 sums exist (runs > kPieceDirectRuns)
 };
+
+// Up to this many runs per problem, no Q1/Q2 sums are formed (two launches
+// less): a long segment's pieces are added one by one, at most this many.
+constexpr int kPieceDirectRuns = 1024;
 
 // Column c of the sum of long segment [lo, hi) of problem b.
 __device__ __forceinline__ float long_sum(const LongPieces& lp, int64_t b, int64_t d, int lo,
@@ -217,6 +223,10 @@ __device__ __forceinline__ float long_sum(const LongPieces& lp, int64_t b, int64
   const float* q2 = lp.q2 + (int64_t)b * lp.nq2 * d + c;
   float t = 0.f;
   int r = rlo + 1;
+  if (!lp.blocks) {
+    for (; r < e; ++r) t += pb[(int64_t)r * 2 * d];
+    return pb[((int64_t)rlo * 2 + 1) * d] + t;
+  }
   for (; r < e && (r % kQ1) != 0; ++r) t += pb[(int64_t)r * 2 * d];
   for (; r + kQ1 <= e && (r % (kQ1 * kQ2)) != 0; r += kQ1) t += q1[(int64_t)(r / kQ1) * d];
   for (; r + kQ1 * kQ2 <= e; r += kQ1 * kQ2) t += q2[(int64_t)(r / (kQ1 * kQ2)) * d];

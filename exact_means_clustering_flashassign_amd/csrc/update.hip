@@ -44,7 +44,9 @@
 //             one piece per run it touches, each piece stored to its run's
 //             slot (see LongPieces).
 //   q1/q2     sums of the head pieces of every full block of 32 runs (Q1),
-//             and of 32 Q1 rows (Q2), in order.
+//             and of 32 Q1 rows (Q2), in order; only for problems of more
+//             than kPieceDirectRuns runs (below that a long sum adds its
+//             pieces one by one).
 //   finalize  elementwise over (cluster, column) of long clusters:
 //             c = (sum of its pieces in fixed order) / count, squared moves
 //             into the block's partial; with a shift buffer, shift_reduce
@@ -1610,6 +1612,7 @@ LongPieces long_pieces(const UpdateWs& ws) {
   lp.runs = ws.runs;
   lp.nq1 = ws.nq1;
   lp.nq2 = ws.nq2;
+  lp.blocks = ws.runs > kPieceDirectRuns;
   return lp;
 }
 
@@ -1759,12 +1762,13 @@ hipError_t launch_update(const void* x, const int32_t* ids, int dt, int64_t B, i
   const int64_t grid = B * fb;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (B * ws.nq1 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (ws.runs >= kQ1) {                          // some full Q1 block
+  const bool blocks = ws.runs > kPieceDirectRuns;   // else long sums add their pieces directly
+  if (blocks && ws.runs >= kQ1) {                // some full Q1 block
     q1blocks_kernel<<<(unsigned)(B * ws.nq1), kThreads, 0, s>>>(long_pieces(ws), ws.q1,
                                                                 ws.has_long, (int)d);
     FK_CHECK(hipGetLastError());
   }
-  if (ws.runs >= kQ1 * kQ2) {                    // some full Q2 block
+  if (blocks && ws.runs >= kQ1 * kQ2) {          // some full Q2 block
     q2blocks_kernel<<<(unsigned)(B * ws.nq2), kThreads, 0, s>>>(long_pieces(ws), ws.q1, ws.q2,
                                                                 ws.has_long, (int)d);
     FK_CHECK(hipGetLastError());

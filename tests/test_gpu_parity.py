@@ -191,6 +191,7 @@ UPDATE_CASES = [
     ("f16", 1, 9000, 2000, 20, "uniform"),     # d above one segreduce pass
     ("f16", 2, 300000, 32, 8, "zipf"),         # clusters over 32 runs: Q1 block sums
     ("bf16", 1, 300000, 64, 5, "one"),         # one cluster over 1024 runs: a Q2 block sum
+    ("f16", 1, 262144, 48, 4, "one"),          # 1024 runs, no block sums: 1023 pieces added one by one
     ("f32", 1, 70000, 36, 3, "zipf"),          # long pieces with d % 4 == 0, fp32 slices
     ("f16", 1, 70000, 33, 3, "zipf"),          # long pieces with ragged d (scalar stores)
     ("f16", 2, 20000, 64, 5000, "zipf"),       # ids over 11 bits: the two-pass LDS sort
