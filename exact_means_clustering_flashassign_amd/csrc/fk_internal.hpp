@@ -296,6 +296,7 @@ struct UpdateWs {
   int32_t* rcolsum;     // (passes, B, chunk groups, 256) digit counts per group of chunks
   int32_t* rgbase;      // (B, chunk groups, 256) first output position per group and digit
   int32_t* cursor;      // (B,K) scatter cursors (K above 2^16 only)
+  int32_t* ktot;        // (B, K / 256 blocks) cluster counts per block of 256 (large G*K only)
   int runs, nq1, nq2;
 };
 size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K);

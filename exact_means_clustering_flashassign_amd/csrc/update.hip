@@ -248,9 +248,8 @@ __device__ __forceinline__ int column_prefix(int32_t* hb, int64_t K, int G, int 
   return run;
 }
 
-// offsets: G > 0: column prefixes of H and counts first, then offsets, run
-// starts and the long-cluster flag; G == 0:
-// counts given, offsets only.
+// offsets (one block per problem, G*K small): column prefixes of H and the
+// counts first, then offsets, run starts and the long-cluster flag.
 __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
     int32_t* __restrict__ H, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ run_first, int32_t* __restrict__ has_long, int K, int G, int runs) {
@@ -261,18 +260,7 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   if (t == 0) nlong = 0;
   int32_t* hb = H + (int64_t)b * G * K;
   int32_t* cb = counts + (int64_t)b * K;
-  if (G > 0) {
-    for (int k = t; k < K; k += kSortThreads) cnt[k] = column_prefix(hb, K, G, k);
-  } else {
-    for (int k0 = t; k0 < K; k0 += kSortThreads * 8) {   // 8 loads in flight per thread
-      int v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = k0 + q * kSortThreads < K ? cb[k0 + q * kSortThreads] : 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (k0 + q * kSortThreads < K) cnt[k0 + q * kSortThreads] = v[q];
-    }
-  }
+  for (int k = t; k < K; k += kSortThreads) cnt[k] = column_prefix(hb, K, G, k);
   __syncthreads();
   const int per = (K + kSortThreads - 1) / kSortThreads;
   const int lo = min(t * per, K), hi = min(lo + per, K);
@@ -285,9 +273,9 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   int mylong = 0;
   for (int i = lo; i < hi; ++i) {
     const int c = cnt[i];
-    if (G > 0) cb[i] = c;
+    cb[i] = c;
     cnt[i] = run;
-    if (G > 0 && c > 0) mark_runs(rf, i, run, run + c);
+    if (c > 0) mark_runs(rf, i, run, run + c);
     mylong += is_long(run, run + c) ? 1 : 0;
     run += c;
   }
@@ -295,20 +283,104 @@ __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
   if (t == 0) cnt[K] = total;
   __syncthreads();
   for (int k = t; k <= K; k += kSortThreads) ob[k] = cnt[k];   // coalesced
-  if (G == 0) return;                            // run starts, flag, counters: prep_kernel
   if (t == 0) has_long[b] = nlong;
   for (int64_t r = (total + (int64_t)kSegRun - 1) / kSegRun + t; r < runs; r += kSortThreads)
     rf[r] = K;                                   // runs past the last valid position
 }
 
-// Large G*K: column prefixes on a grid, one thread per (problem, cluster).
+// Sum over the kThreads threads of a block (every thread gets it). wsum:
+// kThreads / 64 ints of LDS.
+__device__ __forceinline__ int block_sum256(int v, int32_t* wsum) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int all = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) all += wsum[i];
+  __syncthreads();
+  return all;
+}
+
+// Large G*K: column prefixes on a grid, one thread per (problem, cluster);
+// block j of a problem also stores the total count of its kThreads clusters
+// in ktot[b * kblocks + j].
 __global__ __launch_bounds__(kThreads) void colscan_kernel(int32_t* __restrict__ H,
-                                                           int32_t* __restrict__ counts, int K,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ ktot, int K,
                                                            int G, int kblocks) {
-  const int b = blockIdx.x / kblocks;
-  const int k = (blockIdx.x % kblocks) * kThreads + threadIdx.x;
-  if (k >= K) return;
-  counts[(int64_t)b * K + k] = column_prefix(H + (int64_t)b * G * K, K, G, k);
+  __shared__ int32_t wsum[kThreads / 64];
+  const int b = blockIdx.x / kblocks, j = blockIdx.x % kblocks;
+  const int k = j * kThreads + threadIdx.x;
+  int c = 0;
+  if (k < K) {
+    c = column_prefix(H + (int64_t)b * G * K, K, G, k);
+    counts[(int64_t)b * K + k] = c;
+  }
+  const int tot = block_sum256(c, wsum);
+  if (threadIdx.x == 0) ktot[blockIdx.x] = tot;
+}
+
+// Large G*K, after colscan: block j of problem b owns clusters
+// [j * kThreads, (j + 1) * kThreads). Their first sorted positions are the
+// sum of the totals of the blocks before (ktot) plus an exclusive scan of
+// their counts. A run whose first position lies in one of these clusters
+// gets it: the last cluster of the block that starts at or before that
+// position (an empty cluster starts where the next one does). The last block
+// writes the total and gives the runs past it K. The long-cluster flag is set
+// (finalize checks every cluster).
+__global__ __launch_bounds__(kThreads) void offsets_runs_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ ktot,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ run_first,
+    int32_t* __restrict__ has_long, int K, int runs, int kblocks) {
+  __shared__ int32_t wsum[kThreads / 64];
+  __shared__ int32_t start[kThreads + 1];
+  const int b = blockIdx.x / kblocks, j = blockIdx.x % kblocks, t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  int before = 0;
+  for (int i = t; i < j; i += kThreads) before += ktot[(int64_t)b * kblocks + i];
+  const int base = block_sum256(before, wsum);
+  const int k = j * kThreads + t;
+  const int c = k < K ? counts[(int64_t)b * K + k] : 0;
+  int incl = c;                                  // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int wbefore = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) {
+    const int v = wsum[i];
+    wbefore += i < w ? v : 0;
+    all += v;
+  }
+  const int lo = base + wbefore + incl - c;
+  int32_t* ob = offsets + (int64_t)b * (K + 1);
+  if (k < K) ob[k] = lo;
+  start[t] = lo;
+  if (t == 0) start[kThreads] = base + all;
+  const bool last = j == kblocks - 1;
+  if (last && t == 0) ob[K] = base + all;
+  if (j == 0 && t == 0) has_long[b] = 1;
+  __syncthreads();
+  int32_t* rf = run_first + (int64_t)b * runs;
+  const int64_t pa = start[0], pe = start[kThreads];
+  for (int64_t r = (pa + kSegRun - 1) / kSegRun + t; r * kSegRun < pe; r += kThreads) {
+    const int pos = (int)(r * kSegRun);
+    int a = 0, z = kThreads - 1;                 // start[a] <= pos throughout
+    while (a < z) {
+      const int m = (a + z + 1) >> 1;
+      if (start[m] <= pos) a = m;
+      else z = m - 1;
+    }
+    rf[r] = j * kThreads + a;
+  }
+  if (last)
+    for (int64_t r = (pe + kSegRun - 1) / kSegRun + t; r < runs; r += kThreads)
+      rf[r] = K;                                 // runs past the last valid position
 }
 
 // Direct scatter (ids in at most kDirectKeyBits bits, chunks of at most
@@ -1528,7 +1600,7 @@ int64_t radix_rgroups(int64_t N) { return (radix_chunks(N) + kRadixRows - 1) / k
 
 struct WsLayout {
   int64_t runs, nq1, nq2, slices, G, GR, RG;
-  bool radix, two_sets, cursor;
+  bool radix, two_sets, cursor, ktot;
 };
 
 WsLayout ws_layout(int64_t B, int64_t N, int64_t d, int64_t K) {
@@ -1542,6 +1614,7 @@ WsLayout ws_layout(int64_t B, int64_t N, int64_t d, int64_t K) {
   L.radix = pp == kPermRadix;
   L.two_sets = L.radix && radix_passes(K) > 2;
   L.cursor = pp == kPermAtomic;
+  L.ktot = L.G > 0 && L.G * K > kFusedOffsetsMax;   // colscan + offsets_runs
   L.GR = L.radix ? radix_chunks(N) : 0;
   L.RG = L.radix ? radix_rgroups(N) : 0;
   return L;
@@ -1561,6 +1634,7 @@ size_t update_ws_bytes(int64_t B, int64_t N, int64_t d, int64_t K) {
          align256((size_t)radix_passes(K) * B * L.RG * kRadix * 4) +
          align256((size_t)B * L.RG * kRadix * 4);
   if (L.cursor) n += align256((size_t)B * K * 4);
+  if (L.ktot) n += align256((size_t)B * ((K + kThreads - 1) / kThreads) * 4);
   return n;
 }
 
@@ -1598,6 +1672,8 @@ UpdateWs carve_update_ws(void* base, int64_t B, int64_t N, int64_t d, int64_t K)
     w.rgbase = reinterpret_cast<int32_t*>(take((size_t)B * L.RG * kRadix * 4));
   }
   if (L.cursor) w.cursor = reinterpret_cast<int32_t*>(take((size_t)B * K * 4));
+  w.ktot = L.ktot ? reinterpret_cast<int32_t*>(take((size_t)B * ((K + kThreads - 1) / kThreads) * 4))
+                  : nullptr;
   w.runs = (int)L.runs;
   w.nq1 = (int)L.nq1;
   w.nq2 = (int)L.nq2;
@@ -1678,16 +1754,11 @@ hipError_t run_sort(const int32_t* ids, int dt, int64_t B, int64_t N, int64_t d,
       FK_CHECK(hipGetLastError());
     } else {
       const int kblocks = (int)((K + kThreads - 1) / kThreads);
-      colscan_kernel<<<(unsigned)(B * kblocks), kThreads, 0, s>>>(ws.hist, counts, (int)K, G,
-                                                                  kblocks);
+      colscan_kernel<<<(unsigned)(B * kblocks), kThreads, 0, s>>>(ws.hist, counts, ws.ktot,
+                                                                  (int)K, G, kblocks);
       FK_CHECK(hipGetLastError());
-      offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
-                                                             ws.run_first, ws.has_long, (int)K,
-                                                             0, runs);
-      FK_CHECK(hipGetLastError());
-      const int pb = (int)((K + 255) / 256 < 256 ? (K + 255) / 256 : 256);
-      prep_kernel<<<(unsigned)(B * pb), kThreads, 0, s>>>(ws.offsets, ws.run_first, ws.has_long,
-                                                           (int)K, runs, pb);
+      offsets_runs_kernel<<<(unsigned)(B * kblocks), kThreads, 0, s>>>(
+          counts, ws.ktot, ws.offsets, ws.run_first, ws.has_long, (int)K, runs, kblocks);
       FK_CHECK(hipGetLastError());
     }
     if (pp == kPermDirect) {

@@ -196,6 +196,8 @@ UPDATE_CASES = [
     ("f16", 1, 70000, 33, 3, "zipf"),          # long pieces with ragged d (scalar stores)
     ("f16", 2, 20000, 64, 5000, "zipf"),       # ids over 11 bits: the two-pass LDS sort
     ("bf16", 1, 50000, 64, 2047, "uniform"),   # the widest ids of the direct scatter
+    ("f16", 1, 200000, 64, 4096, "zipf"),      # chunks x clusters above one offsets block
+    ("bf16", 3, 120000, 32, 3000, "uniform"),  # the same, three problems
 ]
 
 
