@@ -620,6 +620,9 @@ __global__ __launch_bounds__(kSortThreads) void scatter_stable_kernel(
 //                  Writes the key and the point index, or after the last pass
 //                  only the point index, into perm.
 // Keys outside [0, K) are taken as K: they sort after every real key.
+// Two passes over at most 2^24 points keep one 32-bit word per point between
+// them: the first pass writes (key >> 8) << 24 | point index (the low digit
+// is no longer needed), the second sorts by its top byte.
 constexpr int kRadix = 256;
 constexpr int kRadixChunk = 16384;
 constexpr int kRadixSub = 4096;
@@ -629,9 +632,10 @@ __device__ __forceinline__ uint32_t radix_key(int32_t k, int K) {
   return (unsigned)k < (unsigned)K ? (uint32_t)k : (uint32_t)K;
 }
 
+// raw: the keys are packed words of the first pass, taken as they are.
 __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
     const int32_t* __restrict__ keys, int32_t* __restrict__ rhist, int32_t* __restrict__ colsum,
-    int N, int K, int G, int RG, int shift) {
+    int N, int K, int G, int RG, int shift, bool raw) {
   __shared__ int32_t h[kWavesSort][kRadix];       // one histogram per wave
   const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
   const int w = t >> 6;
@@ -644,7 +648,8 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
 #pragma unroll
     for (int q = 0; q < kSortUnroll; ++q) {
       const int i = m + q * kSortThreads + t;
-      const uint32_t kv = radix_key(kb[min(i, n1 - 1)], K);   // unconditional: loads in flight together
+      const int32_t kr = kb[min(i, n1 - 1)];     // unconditional: loads in flight together
+      const uint32_t kv = raw ? (uint32_t)kr : radix_key(kr, K);
       dg[q] = i < n1 ? (kv >> shift) & (kRadix - 1) : 0xFFFFFFFFu;
     }
 #pragma unroll
@@ -687,6 +692,8 @@ __global__ __launch_bounds__(kSortThreads) void radix_scan_kernel(const int32_t*
 
 // keys_in null: the keys are the ids themselves and the point index is the
 // position (first pass). keys_out null: last pass, only the index goes out.
+// pack_out: keys_out receives the packed words (idx_out unused); packed_in:
+// keys_in holds them (idx_in unused), sorted by their top byte (shift 24).
 // Each sub-chunk is reordered by digit in LDS first (the second walk keeps
 // its keys in registers, then stores them at their local sorted places), so
 // the global stores go out as runs of consecutive addresses, one run per
@@ -695,7 +702,8 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ keys_in,
     const int32_t* __restrict__ idx_in, const int32_t* __restrict__ rhist,
     const int32_t* __restrict__ rgbase, int32_t* __restrict__ keys_out,
-    int32_t* __restrict__ idx_out, int N, int K, int G, int RG, int shift) {
+    int32_t* __restrict__ idx_out, int N, int K, int G, int RG, int shift, bool pack_out,
+    bool packed_in) {
   __shared__ int32_t skey[kRadixSub];
   __shared__ int32_t sidx[kRadixSub];
   __shared__ int32_t hist[kRadix * kWavesSort];
@@ -733,7 +741,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
   }
   __syncthreads();
   int32_t* ko = keys_out ? keys_out + (int64_t)b * N : nullptr;
-  int32_t* xo = idx_out + (int64_t)b * N;
+  int32_t* xo = idx_out ? idx_out + (int64_t)b * N : nullptr;
   const int n0 = g * kRadixChunk, n1 = min(n0 + kRadixChunk, N);
   for (int m0 = n0; m0 < n1; m0 += kRadixSub) {
     const int m = min(kRadixSub, n1 - m0);
@@ -742,12 +750,12 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     for (int j = 0; j < SPW; ++j) {               // unconditional: loads in flight together
       const int i = min(m0 + j * kSortThreads + t, n1 - 1);
       kk[j] = kb[i];
-      xx[j] = xb ? xb[i] : i;
+      xx[j] = packed_in ? kk[j] & 0xFFFFFF : (xb ? xb[i] : i);
     }
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int l = j * kSortThreads + t;
-      skey[l] = (int32_t)radix_key(kk[j], K);
+      skey[l] = packed_in ? kk[j] : (int32_t)radix_key(kk[j], K);
       sidx[l] = xx[j];
     }
     for (int r = lane; r < kRadix; r += 64) hist[w * kRadix + r] = 0;
@@ -806,8 +814,12 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     for (int l = t; l < m; l += kSortThreads) {
       const int key = skey[l];
       const int pos = gbase[((uint32_t)key >> shift) & (kRadix - 1)] + l;
-      if (ko) ko[pos] = key;
-      xo[pos] = sidx[l];
+      if (pack_out) {
+        ko[pos] = (int32_t)((((uint32_t)key >> 8) << 24) | (uint32_t)sidx[l]);
+      } else {
+        if (ko) ko[pos] = key;
+        xo[pos] = sidx[l];
+      }
     }
     __syncthreads();
   }
@@ -1703,21 +1715,26 @@ hipError_t run_radix(const int32_t* ids, int64_t B, int64_t N, int64_t K, const 
   zg = zg < 1 ? 1 : (zg > 4096 ? 4096 : zg);
   zero_kernel<<<(unsigned)zg, kThreads, 0, s>>>(ws.rcolsum, ncs);
   FK_CHECK(hipGetLastError());
+  // two passes, point indices in 24 bits: one packed word per point between them
+  const bool pack = passes == 2 && N <= ((int64_t)1 << 24);
   const int32_t* kin = nullptr;
   const int32_t* xin = nullptr;
   for (int q = 0; q < passes; ++q) {
     const bool last = q == passes - 1;
+    const bool pout = pack && q == 0, pin = pack && q == 1;
     int32_t* kout = last ? nullptr : ws.rkeys[q & 1];
-    int32_t* xout = last ? ws.perm : ws.ridx[q & 1];
+    int32_t* xout = last ? ws.perm : (pout ? nullptr : ws.ridx[q & 1]);
     int32_t* cs = ws.rcolsum + (int64_t)q * B * RG * kRadix;
+    const int shift = pin ? 24 : 8 * q;
     radix_hist_kernel<<<(unsigned)(B * G), kSortThreads, 0, s>>>(kin ? kin : ids, ws.rhist, cs,
                                                                 (int)N, (int)K, (int)G, (int)RG,
-                                                                8 * q);
+                                                                shift, pin);
     FK_CHECK(hipGetLastError());
     radix_scan_kernel<<<(unsigned)B, kSortThreads, 0, s>>>(cs, ws.rgbase, (int)RG);
     FK_CHECK(hipGetLastError());
     radix_scatter_kernel<<<(unsigned)(B * G), kSortThreads, 0, s>>>(
-        ids, kin, xin, ws.rhist, ws.rgbase, kout, xout, (int)N, (int)K, (int)G, (int)RG, 8 * q);
+        ids, kin, pin ? nullptr : xin, ws.rhist, ws.rgbase, kout, xout, (int)N, (int)K, (int)G,
+        (int)RG, shift, pout, pin);
     FK_CHECK(hipGetLastError());
     kin = kout;
     xin = xout;
