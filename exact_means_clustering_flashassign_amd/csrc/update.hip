@@ -1071,15 +1071,24 @@ __global__ __launch_bounds__(kThreads) void segreduce_kernel(
   float moved = 0.f;                             // squared moves of this wave's short clusters
   [&]() {
 
+  // the run's staged positions are loaded together with its first cluster
+  // (clamped loads, all in flight at once), then stored to LDS once known
+  // to be needed
+  const int pend = min(p0 + STAGE, N);
+  const int32_t* pp = perm + (int64_t)b * N + p0;
+  int pv[STAGE / 64];
+#pragma unroll
+  for (int q = 0; q < STAGE / 64; ++q) pv[q] = pp[min(lane + 64 * q, pend - p0 - 1)];
   int k = run_first[(int64_t)b * runs + run];
   k = k < 0 ? K : k;
   if (k >= K) return;
-  const int pend = min(p0 + STAGE, N);
-  for (int j = lane; j < pend - p0; j += 64) lperm[wv][j] = perm[(int64_t)b * N + p0 + j];
 
   // offsets window: win holds ob[kw + lane]
   int kw = k;
   int win = ob[min(kw + lane, K)];
+#pragma unroll
+  for (int q = 0; q < STAGE / 64; ++q)
+    if (lane + 64 * q < pend - p0) lperm[wv][lane + 64 * q] = pv[q];
   auto off = [&](int kk) {
     if ((unsigned)(kk - kw) >= 64u) {            // outside the window (either side)
       kw = kk;
