@@ -66,6 +66,8 @@ constexpr int kMaxLdsBins = 32768;            // 128 KB of LDS bins per block
 constexpr int kSortThreads = 1024;
 constexpr int kSortUnroll = 16;               // ids in flight per thread in the sort kernels
 constexpr int64_t kFusedOffsetsMax = 1 << 16; // G*K up to this: one offsets block per problem
+constexpr int kRadixDigits = 256;             // values of one radix pass's key byte
+constexpr int kRadixGroup = 64;               // radix chunks per group of column sums
 constexpr size_t kStableLdsMax = 144 * 1024;  // dynamic LDS of one stable-scatter block, at most
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -196,30 +198,54 @@ __host__ __device__ __forceinline__ int key_bits(int64_t K) {
 //   offsets  per problem: H's columns become exclusive prefix sums over g,
 //            their totals are the counts, whose exclusive prefix sum gives
 //            the segment offsets; also the run starts and the long-cluster
-//            flag (one block per problem when G*K is small; colscan + offsets
-//            + prep otherwise);
+//            flag (one block per problem when G*K is small; colscan +
+//            offsets_runs on a grid otherwise);
 //   perm     chunks that fit LDS: scatter_stable_kernel; otherwise the radix
 //            passes.
+// When radix passes follow (large G*K, chunks of at most one step below or a
+// whole number of steps), hist2 also gives the first pass what its histogram
+// kernel would: each step of kSortThreads * kSortUnroll ids is one radix chunk
+// whose counts per low key byte (ids outside [0, K) taken as K) go to rdig row
+// (b, g * steps + step), and the blocks clear `zero` (the later passes' group
+// sums) for their atomics.
 __global__ __launch_bounds__(kSortThreads) void hist2_kernel(const int32_t* __restrict__ ids,
                                                              int32_t* __restrict__ H, int N, int K,
-                                                             int G, int chunk) {
+                                                             int G, int chunk,
+                                                             int32_t* __restrict__ rdig,
+                                                             int32_t* __restrict__ zero,
+                                                             int64_t nzero) {
   extern __shared__ int32_t bins[];
+  __shared__ int32_t dig[kRadixDigits];          // the current step's digit counts (rdig only)
+  constexpr int STEP = kSortThreads * kSortUnroll;
   const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
+  const int steps = (chunk + STEP - 1) / STEP;   // rdig rows per chunk
   for (int i = t; i < K; i += kSortThreads) bins[i] = 0;
-  __syncthreads();
+  if (zero)
+    for (int64_t i = (int64_t)blockIdx.x * kSortThreads + t; i < nzero;
+         i += (int64_t)gridDim.x * kSortThreads)
+      zero[i] = 0;
   const int32_t* ib = ids + (int64_t)b * N;
   const int n0 = g * chunk, n1 = min(n0 + chunk, N);
-  for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
+  for (int j = 0; j < steps; ++j) {
+    const int m = n0 + j * STEP;
+    if (rdig && t < kRadixDigits) dig[t] = 0;
+    __syncthreads();
     int kk[kSortUnroll];
 #pragma unroll
     for (int q = 0; q < kSortUnroll; ++q) {
       const int n = m + q * kSortThreads + t;
-      const int v = ib[min(n, n1 - 1)];           // unconditional: loads in flight together
-      kk[q] = n < n1 ? v : -1;
+      kk[q] = ib[min(n, n1 - 1)];                // unconditional: loads in flight together
     }
 #pragma unroll
-    for (int q = 0; q < kSortUnroll; ++q)
-      if ((unsigned)kk[q] < (unsigned)K) atomicAdd(&bins[kk[q]], 1);
+    for (int q = 0; q < kSortUnroll; ++q) {
+      if (m + q * kSortThreads + t >= n1) continue;
+      const bool in = (unsigned)kk[q] < (unsigned)K;
+      if (in) atomicAdd(&bins[kk[q]], 1);
+      if (rdig) atomicAdd(&dig[(in ? kk[q] : K) & (kRadixDigits - 1)], 1);
+    }
+    __syncthreads();
+    if (rdig && t < kRadixDigits)
+      rdig[(((int64_t)b * G + g) * steps + j) * kRadixDigits + t] = dig[t];
   }
   __syncthreads();
   int32_t* hr = H + ((int64_t)b * G + g) * K;
@@ -302,14 +328,60 @@ __device__ __forceinline__ int block_sum256(int v, int32_t* wsum) {
   return all;
 }
 
+// First output position of each radix digit in each group of chunks of one
+// problem, from the groups' digit counts cs (RG x kRadixDigits): the keys
+// with a smaller digit plus the keys with this digit in earlier groups. A
+// block of kRadixDigits threads, thread r for digit r. wsum: 4 ints of LDS.
+__device__ void radix_group_starts(const int32_t* __restrict__ cs, int32_t* __restrict__ out,
+                                   int RG, int32_t* wsum) {
+  static_assert(kThreads == kRadixDigits, "one thread per digit");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int tot = 0;
+  for (int rg = 0; rg < RG; ++rg) tot += cs[(int64_t)rg * kRadixDigits + t];
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int i = 0; i < kRadixDigits / 64; ++i) before += i < w ? wsum[i] : 0;
+  int run = before + incl - tot;
+  for (int rg = 0; rg < RG; ++rg) {
+    const int c = cs[(int64_t)rg * kRadixDigits + t];
+    out[(int64_t)rg * kRadixDigits + t] = run;
+    run += c;
+  }
+}
+
 // Large G*K: column prefixes on a grid, one thread per (problem, cluster);
 // block j of a problem also stores the total count of its kThreads clusters
 // in ktot[b * kblocks + j].
+// With rdig (radix passes follow): B * RG more blocks, block (b, rg) summing
+// the first pass's digit counts of radix chunks [rg * kRadixGroup, ...) (GR
+// per problem) into csum0 (no atomics).
 __global__ __launch_bounds__(kThreads) void colscan_kernel(int32_t* __restrict__ H,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ ktot, int K,
-                                                           int G, int kblocks) {
+                                                           int G, int kblocks, int B,
+                                                           const int32_t* __restrict__ rdig,
+                                                           int32_t* __restrict__ csum0, int GR,
+                                                           int RG) {
   __shared__ int32_t wsum[kThreads / 64];
+  if ((int64_t)blockIdx.x >= (int64_t)B * kblocks) {
+    const int i = (int)(blockIdx.x - B * kblocks);
+    const int b = i / RG, rg = i % RG, t = threadIdx.x;
+    const int g0 = rg * kRadixGroup, g1 = min(g0 + kRadixGroup, GR);
+    const int32_t* rd = rdig + (int64_t)b * GR * kRadixDigits;
+    int c = 0;
+#pragma unroll 8
+    for (int gg = g0; gg < g1; ++gg) c += rd[(int64_t)gg * kRadixDigits + t];
+    csum0[((int64_t)b * RG + rg) * kRadixDigits + t] = c;
+    return;
+  }
   const int b = blockIdx.x / kblocks, j = blockIdx.x % kblocks;
   const int k = j * kThreads + threadIdx.x;
   int c = 0;
@@ -329,12 +401,21 @@ __global__ __launch_bounds__(kThreads) void colscan_kernel(int32_t* __restrict__
 // position (an empty cluster starts where the next one does). The last block
 // writes the total and gives the runs past it K. The long-cluster flag is set
 // (finalize checks every cluster).
+// With csum0 (radix passes follow): B more blocks, block b turning problem
+// b's first-pass group digit counts into the group starts rgbase.
 __global__ __launch_bounds__(kThreads) void offsets_runs_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ ktot,
     int32_t* __restrict__ offsets, int32_t* __restrict__ run_first,
-    int32_t* __restrict__ has_long, int K, int runs, int kblocks) {
+    int32_t* __restrict__ has_long, int K, int runs, int kblocks, int B,
+    const int32_t* __restrict__ csum0, int32_t* __restrict__ rgbase, int RG) {
   __shared__ int32_t wsum[kThreads / 64];
   __shared__ int32_t start[kThreads + 1];
+  if ((int64_t)blockIdx.x >= (int64_t)B * kblocks) {
+    const int bb = (int)(blockIdx.x - B * kblocks);
+    radix_group_starts(csum0 + (int64_t)bb * RG * kRadixDigits,
+                       rgbase + (int64_t)bb * RG * kRadixDigits, RG, wsum);
+    return;
+  }
   const int b = blockIdx.x / kblocks, j = blockIdx.x % kblocks, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   int before = 0;
@@ -604,7 +685,8 @@ __global__ __launch_bounds__(kSortThreads) void scatter_stable_kernel(
 // LSD radix passes over a whole problem (chunks too large for LDS, or large
 // K): pass q sorts stably by bits [8q, 8q + 8) of the key, so after the last
 // pass the order is by key and, within a key, by point index. Each pass is a
-// counting sort over chunks of kRadixChunk positions:
+// counting sort over chunks of positions (kRadixChunk, or the split sort's
+// chunks when it ran first with a large count matrix):
 //   radix_hist     block (b, g): counts of each digit in chunk g -> rhist row
 //                  g, also added (integer atomics) to its group of
 //                  kRadixRows chunks' column sums
@@ -623,10 +705,10 @@ __global__ __launch_bounds__(kSortThreads) void scatter_stable_kernel(
 // Two passes over at most 2^24 points keep one 32-bit word per point between
 // them: the first pass writes (key >> 8) << 24 | point index (the low digit
 // is no longer needed), the second sorts by its top byte.
-constexpr int kRadix = 256;
-constexpr int kRadixChunk = 16384;
+constexpr int kRadix = kRadixDigits;
+constexpr int kRadixChunk = 16384;             // chunk length without a split sort before
 constexpr int kRadixSub = 4096;
-constexpr int kRadixRows = 64;
+constexpr int kRadixRows = kRadixGroup;
 
 __device__ __forceinline__ uint32_t radix_key(int32_t k, int K) {
   return (unsigned)k < (unsigned)K ? (uint32_t)k : (uint32_t)K;
@@ -635,13 +717,13 @@ __device__ __forceinline__ uint32_t radix_key(int32_t k, int K) {
 // raw: the keys are packed words of the first pass, taken as they are.
 __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
     const int32_t* __restrict__ keys, int32_t* __restrict__ rhist, int32_t* __restrict__ colsum,
-    int N, int K, int G, int RG, int shift, bool raw) {
+    int N, int K, int G, int RG, int shift, bool raw, int rc) {
   __shared__ int32_t h[kWavesSort][kRadix];       // one histogram per wave
   const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
   const int w = t >> 6;
   for (int r = t; r < kWavesSort * kRadix; r += kSortThreads) (&h[0][0])[r] = 0;
   __syncthreads();
-  const int n0 = g * kRadixChunk, n1 = min(n0 + kRadixChunk, N);
+  const int n0 = g * rc, n1 = min(n0 + rc, N);
   const int32_t* kb = keys + (int64_t)b * N;
   for (int m = n0; m < n1; m += kSortThreads * kSortUnroll) {
     uint32_t dg[kSortUnroll];
@@ -670,24 +752,13 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
 
 // One block per problem: rgbase[b][rg][r] = (keys with a smaller digit) +
 // (keys with digit r in chunk groups before rg).
-__global__ __launch_bounds__(kSortThreads) void radix_scan_kernel(const int32_t* __restrict__ colsum,
-                                                                  int32_t* __restrict__ rgbase,
-                                                                  int RG) {
-  __shared__ int32_t wtot[kWavesSort];
-  const int b = blockIdx.x, t = threadIdx.x;
-  const int32_t* cs = colsum + (int64_t)b * RG * kRadix;
-  int tot = 0;
-  if (t < kRadix)
-    for (int rg = 0; rg < RG; ++rg) tot += cs[(int64_t)rg * kRadix + t];
-  int all;
-  int run = block_exclusive_scan(t < kRadix ? tot : 0, wtot, all);
-  if (t >= kRadix) return;
-  int32_t* out = rgbase + (int64_t)b * RG * kRadix;
-  for (int rg = 0; rg < RG; ++rg) {
-    const int c = cs[(int64_t)rg * kRadix + t];
-    out[(int64_t)rg * kRadix + t] = run;
-    run += c;
-  }
+__global__ __launch_bounds__(kThreads) void radix_scan_kernel(const int32_t* __restrict__ colsum,
+                                                              int32_t* __restrict__ rgbase,
+                                                              int RG) {
+  __shared__ int32_t wsum[kThreads / 64];
+  const int b = blockIdx.x;
+  radix_group_starts(colsum + (int64_t)b * RG * kRadix, rgbase + (int64_t)b * RG * kRadix, RG,
+                     wsum);
 }
 
 // keys_in null: the keys are the ids themselves and the point index is the
@@ -703,7 +774,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const int32_t* __restrict__ idx_in, const int32_t* __restrict__ rhist,
     const int32_t* __restrict__ rgbase, int32_t* __restrict__ keys_out,
     int32_t* __restrict__ idx_out, int N, int K, int G, int RG, int shift, bool pack_out,
-    bool packed_in) {
+    bool packed_in, int rc) {
   __shared__ int32_t skey[kRadixSub];
   __shared__ int32_t sidx[kRadixSub];
   __shared__ int32_t hist[kRadix * kWavesSort];
@@ -742,7 +813,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
   __syncthreads();
   int32_t* ko = keys_out ? keys_out + (int64_t)b * N : nullptr;
   int32_t* xo = idx_out ? idx_out + (int64_t)b * N : nullptr;
-  const int n0 = g * kRadixChunk, n1 = min(n0 + kRadixChunk, N);
+  const int n0 = g * rc, n1 = min(n0 + rc, N);
   for (int m0 = n0; m0 < n1; m0 += kRadixSub) {
     const int m = min(kRadixSub, n1 - m0);
     int kk[SPW], xx[SPW];
@@ -1615,9 +1686,41 @@ PermPath perm_path(int64_t B, int64_t N, int64_t K) {
 
 int radix_passes(int64_t K) { return (key_bits(K) + 7) / 8; }
 
-// Radix chunks per problem and their groups.
-int64_t radix_chunks(int64_t N) { return N > 0 ? (N + kRadixChunk - 1) / kRadixChunk : 1; }
-int64_t radix_rgroups(int64_t N) { return (radix_chunks(N) + kRadixRows - 1) / kRadixRows; }
+// The split sort's count matrix needs the grid kernels (colscan, offsets_runs).
+bool big_count_matrix(int G, int64_t K) { return G > 0 && (int64_t)G * K > kFusedOffsetsMax; }
+
+// Radix passes after a split sort with a large count matrix whose chunks are
+// at most one hist2 step or a whole number of steps: hist2 counts the first
+// pass's digits per step, and the radix chunks are those steps (the whole
+// split chunk when it is shorter). Otherwise chunks of kRadixChunk.
+static_assert(kRadixChunk == kSortThreads * kSortUnroll, "a radix chunk is one hist2 step");
+bool radix_after_split(int64_t B, int64_t N, int64_t K) {
+  const int64_t G = split_groups(B, N, K);
+  if (perm_path(B, N, K) != kPermRadix || !big_count_matrix((int)G, K)) return false;
+  const int64_t chunk = (N + G - 1) / G;
+  return chunk <= kRadixChunk || chunk % kRadixChunk == 0;
+}
+int64_t radix_chunk_len(int64_t B, int64_t N, int64_t K) {
+  if (!radix_after_split(B, N, K)) return kRadixChunk;
+  const int64_t G = split_groups(B, N, K);
+  const int64_t chunk = (N + G - 1) / G;
+  return chunk < kRadixChunk ? chunk : kRadixChunk;
+}
+
+// Radix chunks per problem and their groups. After the split sort they are
+// exactly hist2's digit rows, G chunks of `steps` each (trailing ones may be
+// empty).
+int64_t radix_chunks(int64_t B, int64_t N, int64_t K) {
+  if (radix_after_split(B, N, K)) {
+    const int64_t G = split_groups(B, N, K);
+    const int64_t chunk = (N + G - 1) / G;
+    return G * ((chunk + kRadixChunk - 1) / kRadixChunk);
+  }
+  return N > 0 ? (N + kRadixChunk - 1) / kRadixChunk : 1;
+}
+int64_t radix_rgroups(int64_t B, int64_t N, int64_t K) {
+  return (radix_chunks(B, N, K) + kRadixRows - 1) / kRadixRows;
+}
 
 struct WsLayout {
   int64_t runs, nq1, nq2, slices, G, GR, RG;
@@ -1635,9 +1738,9 @@ WsLayout ws_layout(int64_t B, int64_t N, int64_t d, int64_t K) {
   L.radix = pp == kPermRadix;
   L.two_sets = L.radix && radix_passes(K) > 2;
   L.cursor = pp == kPermAtomic;
-  L.ktot = L.G > 0 && L.G * K > kFusedOffsetsMax;   // colscan + offsets_runs
-  L.GR = L.radix ? radix_chunks(N) : 0;
-  L.RG = L.radix ? radix_rgroups(N) : 0;
+  L.ktot = big_count_matrix((int)L.G, K);          // colscan + offsets_runs
+  L.GR = L.radix ? radix_chunks(B, N, K) : 0;
+  L.RG = L.radix ? radix_rgroups(B, N, K) : 0;
   return L;
 }
 
@@ -1713,17 +1816,24 @@ LongPieces long_pieces(const UpdateWs& ws) {
   return lp;
 }
 
-// perm by LSD radix passes (8 key bits each) over whole problems.
+// perm by LSD radix passes (8 key bits each) over whole problems. After a
+// split sort with a large count matrix (radix_after_split) the first pass's
+// digit counts and group starts are already there (hist2, colscan,
+// offsets_runs) and the later passes' group sums already cleared.
 hipError_t run_radix(const int32_t* ids, int64_t B, int64_t N, int64_t K, const UpdateWs& ws,
                      hipStream_t s) {
-  const int64_t G = radix_chunks(N), RG = radix_rgroups(N);
+  const int64_t G = radix_chunks(B, N, K), RG = radix_rgroups(B, N, K);
+  const int64_t rc = radix_chunk_len(B, N, K);
+  const bool first_done = radix_after_split(B, N, K);
   const int passes = radix_passes(K);
   if (B * G > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const int64_t ncs = passes * B * RG * kRadix;
-  int64_t zg = (ncs + kThreads - 1) / kThreads;
-  zg = zg < 1 ? 1 : (zg > 4096 ? 4096 : zg);
-  zero_kernel<<<(unsigned)zg, kThreads, 0, s>>>(ws.rcolsum, ncs);
-  FK_CHECK(hipGetLastError());
+  if (!first_done) {
+    const int64_t ncs = passes * B * RG * kRadix;
+    int64_t zg = (ncs + kThreads - 1) / kThreads;
+    zg = zg < 1 ? 1 : (zg > 4096 ? 4096 : zg);
+    zero_kernel<<<(unsigned)zg, kThreads, 0, s>>>(ws.rcolsum, ncs);
+    FK_CHECK(hipGetLastError());
+  }
   // two passes, point indices in 24 bits: one packed word per point between them
   const bool pack = passes == 2 && N <= ((int64_t)1 << 24);
   const int32_t* kin = nullptr;
@@ -1735,15 +1845,16 @@ hipError_t run_radix(const int32_t* ids, int64_t B, int64_t N, int64_t K, const 
     int32_t* xout = last ? ws.perm : (pout ? nullptr : ws.ridx[q & 1]);
     int32_t* cs = ws.rcolsum + (int64_t)q * B * RG * kRadix;
     const int shift = pin ? 24 : 8 * q;
-    radix_hist_kernel<<<(unsigned)(B * G), kSortThreads, 0, s>>>(kin ? kin : ids, ws.rhist, cs,
-                                                                (int)N, (int)K, (int)G, (int)RG,
-                                                                shift, pin);
-    FK_CHECK(hipGetLastError());
-    radix_scan_kernel<<<(unsigned)B, kSortThreads, 0, s>>>(cs, ws.rgbase, (int)RG);
-    FK_CHECK(hipGetLastError());
+    if (q > 0 || !first_done) {
+      radix_hist_kernel<<<(unsigned)(B * G), kSortThreads, 0, s>>>(
+          kin ? kin : ids, ws.rhist, cs, (int)N, (int)K, (int)G, (int)RG, shift, pin, (int)rc);
+      FK_CHECK(hipGetLastError());
+      radix_scan_kernel<<<(unsigned)B, kThreads, 0, s>>>(cs, ws.rgbase, (int)RG);
+      FK_CHECK(hipGetLastError());
+    }
     radix_scatter_kernel<<<(unsigned)(B * G), kSortThreads, 0, s>>>(
         ids, kin, pin ? nullptr : xin, ws.rhist, ws.rgbase, kout, xout, (int)N, (int)K, (int)G,
-        (int)RG, shift, pout, pin);
+        (int)RG, shift, pout, pin, (int)rc);
     FK_CHECK(hipGetLastError());
     kin = kout;
     xin = xout;
@@ -1770,8 +1881,16 @@ hipError_t run_sort(const int32_t* ids, int dt, int64_t B, int64_t N, int64_t d,
       (void)hipGetLastError();
       attr = true;
     }
+    // radix passes after a large count matrix: hist2 also counts the first
+    // pass's digits (chunks shared) and clears the later passes' group sums
+    const bool fuse = radix_after_split(B, N, K);
+    const int64_t GR = fuse ? radix_chunks(B, N, K) : 0;
+    const int64_t RG = fuse ? radix_rgroups(B, N, K) : 0;
+    int32_t* rdig = fuse ? ws.rhist : nullptr;
+    int32_t* zero = fuse ? ws.rcolsum + B * RG * kRadix : nullptr;
+    const int64_t nzero = fuse ? (radix_passes(K) - 1) * B * RG * kRadix : 0;
     hist2_kernel<<<(unsigned)(B * G), kSortThreads, lds, s>>>(ids, ws.hist, (int)N, (int)K, G,
-                                                             chunk);
+                                                             chunk, rdig, zero, nzero);
     FK_CHECK(hipGetLastError());
     if ((int64_t)G * K <= kFusedOffsetsMax) {
       offsets_kernel<<<(unsigned)B, kSortThreads, lds1, s>>>(ws.hist, counts, ws.offsets,
@@ -1780,11 +1899,14 @@ hipError_t run_sort(const int32_t* ids, int dt, int64_t B, int64_t N, int64_t d,
       FK_CHECK(hipGetLastError());
     } else {
       const int kblocks = (int)((K + kThreads - 1) / kThreads);
-      colscan_kernel<<<(unsigned)(B * kblocks), kThreads, 0, s>>>(ws.hist, counts, ws.ktot,
-                                                                  (int)K, G, kblocks);
+      if (B * (kblocks + RG) > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+      colscan_kernel<<<(unsigned)(B * (kblocks + RG)), kThreads, 0, s>>>(
+          ws.hist, counts, ws.ktot, (int)K, G, kblocks, (int)B, rdig, ws.rcolsum, (int)GR,
+          (int)RG);
       FK_CHECK(hipGetLastError());
-      offsets_runs_kernel<<<(unsigned)(B * kblocks), kThreads, 0, s>>>(
-          counts, ws.ktot, ws.offsets, ws.run_first, ws.has_long, (int)K, runs, kblocks);
+      offsets_runs_kernel<<<(unsigned)(B * kblocks + (fuse ? B : 0)), kThreads, 0, s>>>(
+          counts, ws.ktot, ws.offsets, ws.run_first, ws.has_long, (int)K, runs, kblocks, (int)B,
+          ws.rcolsum, ws.rgbase, (int)RG);
       FK_CHECK(hipGetLastError());
     }
     if (pp == kPermDirect) {
