@@ -10,6 +10,13 @@
 
 #include "fk_internal.hpp"
 
+namespace fk {
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace fk
+
 namespace {
 
 using fk::UpdateWs;
@@ -181,24 +188,54 @@ struct StreamSet {
 
 // ---------------------------------------------------------------------------
 // trace
+// Per iteration: the norms kernel's start and end, the assign kernel's start
+// and end (stamped by the kernels' own launches, so the trace adds nothing to
+// the stream between them), and, for the last iteration a call traces, a
+// marker after its update. An iteration's update runs from its assign's end
+// to the next iteration's norms start, or to that marker.
+enum TraceEv { kNormsStart, kNormsEnd, kAssignStart, kAssignEnd, kUpdateEnd, kTraceEvs };
 struct Trace {
   bool on = false;
   int32_t capacity = 0;
   int32_t used = 0;
-  std::vector<hipEvent_t> ev;   // 4 per iteration: norms, assign, update, end
+  std::vector<hipEvent_t> ev;       // kTraceEvs per iteration
+  std::vector<char> has_end;        // kUpdateEnd recorded
 };
 Trace g_trace;
 
 void trace_release() {
   for (hipEvent_t e : g_trace.ev) (void)hipEventDestroy(e);
   g_trace.ev.clear();
+  g_trace.has_end.clear();
   g_trace.on = false;
   g_trace.capacity = g_trace.used = 0;
 }
 
 hipEvent_t trace_event(int32_t it, int which) {
-  return g_trace.ev[(size_t)it * 4 + which];
+  return g_trace.ev[(size_t)it * kTraceEvs + which];
 }
+
+// Hands the next timed launch a start and end event; if no kernel took them
+// (nothing to launch), they become plain stream markers at that point.
+struct TimedPhase {
+  bool on;
+  TimedPhase(bool tr, hipEvent_t a, hipEvent_t b) : on(tr) {
+    if (on) fk::launch_events() = fk::LaunchEvents{a, b};
+  }
+  hipError_t finish(hipStream_t s) {
+    if (!on) return hipSuccess;
+    on = false;
+    fk::LaunchEvents& le = fk::launch_events();
+    if (!le.start && !le.stop) return hipSuccess;
+    const fk::LaunchEvents ev = le;
+    le = fk::LaunchEvents();
+    hipError_t e = hipEventRecord(ev.start, s);
+    return e != hipSuccess ? e : hipEventRecord(ev.stop, s);
+  }
+  ~TimedPhase() {
+    if (on) fk::launch_events() = fk::LaunchEvents();
+  }
+};
 
 }  // namespace
 
@@ -357,27 +394,37 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
   if (test && !rb.ok) return FK_ERR_HIP;
   int32_t done = 0, pending = -1;
   const size_t ids_bytes = (size_t)B * N * 4, c_bytes = (size_t)B * K * d * 4;
+  const int32_t first_slot = g_trace.used;
   for (int32_t t = 0; t < max_iter; ++t) {
     const bool tr = g_trace.on && g_trace.used < g_trace.capacity;
     const int32_t slot = g_trace.used;
-    if (tr && hipEventRecord(trace_event(slot, 0), stream) != hipSuccess) return FK_ERR_HIP;
     // without the tol test, the previous update's long clusters are divided
     // by this norms pass (it reads the centres anyway): one launch less
-    e = fk::launch_norms(centers, w.c_lp, w.cnorm, dt, B * K, d, stream,
-                         defer && t > 0 ? fk::pending_finish(w.upd, K) : fk::PendingFinish());
-    if (e != hipSuccess) return FK_ERR_HIP;
-    if (tr && hipEventRecord(trace_event(slot, 1), stream) != hipSuccess) return FK_ERR_HIP;
-    e = run_assign(x, w.c_lp, w.cnorm, dt, B, N, d, K, ids, stream);
-    if (e == hipErrorNotSupported || e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
-    if (e != hipSuccess) return FK_ERR_HIP;
-    if (tr && hipEventRecord(trace_event(slot, 2), stream) != hipSuccess) return FK_ERR_HIP;
+    {
+      TimedPhase ph(tr, tr ? trace_event(slot, kNormsStart) : nullptr,
+                    tr ? trace_event(slot, kNormsEnd) : nullptr);
+      e = fk::launch_norms(centers, w.c_lp, w.cnorm, dt, B * K, d, stream,
+                           defer && t > 0 ? fk::pending_finish(w.upd, K) : fk::PendingFinish());
+      if (e != hipSuccess || ph.finish(stream) != hipSuccess) return FK_ERR_HIP;
+    }
+    {
+      TimedPhase ph(tr, tr ? trace_event(slot, kAssignStart) : nullptr,
+                    tr ? trace_event(slot, kAssignEnd) : nullptr);
+      e = run_assign(x, w.c_lp, w.cnorm, dt, B, N, d, K, ids, stream);
+      if (e == hipErrorNotSupported || e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
+      if (e != hipSuccess || ph.finish(stream) != hipSuccess) return FK_ERR_HIP;
+    }
     // the shift is only read for the tol test
     e = fk::launch_update(x, ids, dt, B, N, d, K, centers, w.counts, test ? w.shift : nullptr,
                           w.upd, stream, defer);
     if (e == hipErrorInvalidConfiguration) return FK_ERR_UNSUPPORTED;
     if (e != hipSuccess) return FK_ERR_HIP;
     if (tr) {
-      if (hipEventRecord(trace_event(slot, 3), stream) != hipSuccess) return FK_ERR_HIP;
+      // the last iteration this call can trace ends with a marker of its own
+      if (slot == g_trace.capacity - 1 || t == max_iter - 1) {
+        if (hipEventRecord(trace_event(slot, kUpdateEnd), stream) != hipSuccess) return FK_ERR_HIP;
+        g_trace.has_end[slot] = 1;
+      }
       ++g_trace.used;
     }
     done = t + 1;
@@ -413,6 +460,12 @@ fk_status_t fk_lloyd(const void* x, fk_dtype_t dt, int64_t B, int64_t N, int64_t
   }
   if (defer && done > 0 && fk::launch_finish(centers, w.upd, B, d, K, stream) != hipSuccess)
     return FK_ERR_HIP;
+  // a tol stop ends the loop early: its last traced iteration gets the marker
+  if (g_trace.on && g_trace.used > first_slot && !g_trace.has_end[g_trace.used - 1]) {
+    if (hipEventRecord(trace_event(g_trace.used - 1, kUpdateEnd), stream) != hipSuccess)
+      return FK_ERR_HIP;
+    g_trace.has_end[g_trace.used - 1] = 1;
+  }
   if (test && hipStreamSynchronize(stream) != hipSuccess) return FK_ERR_HIP;
   *n_iter = done;
   return FK_OK;
@@ -502,7 +555,8 @@ fk_status_t fk_lloyd_host(const void* x_host, fk_dtype_t dt, int64_t B, int64_t 
 fk_status_t fk_trace_begin(int32_t capacity) {
   if (capacity < 1) return FK_ERR_INVALID;
   trace_release();
-  g_trace.ev.resize((size_t)capacity * 4);
+  g_trace.ev.resize((size_t)capacity * kTraceEvs);
+  g_trace.has_end.assign((size_t)capacity, 0);
   for (auto& e : g_trace.ev) {
     if (hipEventCreate(&e) != hipSuccess) {
       e = nullptr;
@@ -523,10 +577,20 @@ fk_status_t fk_trace_end(fk_trace_t* out) {
   fk_status_t st = FK_OK;
   for (int32_t i = 0; i < g_trace.used && st == FK_OK; ++i) {
     float a = 0.f, b = 0.f, c = 0.f;
-    if (hipEventSynchronize(trace_event(i, 3)) != hipSuccess ||
-        hipEventElapsedTime(&a, trace_event(i, 0), trace_event(i, 1)) != hipSuccess ||
-        hipEventElapsedTime(&b, trace_event(i, 1), trace_event(i, 2)) != hipSuccess ||
-        hipEventElapsedTime(&c, trace_event(i, 2), trace_event(i, 3)) != hipSuccess) {
+    // the update ends at the next iteration's norms start, or at the marker
+    const bool own_end = g_trace.has_end[i] || i + 1 == g_trace.used;
+    const hipEvent_t uend =
+        own_end ? trace_event(i, kUpdateEnd) : trace_event(i + 1, kNormsStart);
+    if (!g_trace.has_end[i] && own_end) {        // no marker was recorded: nothing to end on
+      st = FK_ERR_INVALID;
+      break;
+    }
+    if (hipEventSynchronize(uend) != hipSuccess ||
+        hipEventElapsedTime(&a, trace_event(i, kNormsStart), trace_event(i, kNormsEnd)) !=
+            hipSuccess ||
+        hipEventElapsedTime(&b, trace_event(i, kAssignStart), trace_event(i, kAssignEnd)) !=
+            hipSuccess ||
+        hipEventElapsedTime(&c, trace_event(i, kAssignEnd), uend) != hipSuccess) {
       st = FK_ERR_HIP;
       break;
     }

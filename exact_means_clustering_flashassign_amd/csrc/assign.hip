@@ -450,9 +450,8 @@ hipError_t launch_smalld(const uint16_t* x, const uint16_t* c, const float* cn, 
   // a multiple of 8 so each block's point blocks stay on its XCD
   int64_t nblocks = resident >= 8 ? resident / 8 * 8 : resident;
   if (nblocks > total) nblocks = total;
-  kern<<<(unsigned)nblocks, WAVES * 64, 0, s>>>(x, c, cn, ids, (int)N, (int)d, (int)K, bpb,
-                                                (int)total, (int)nblocks);
-  return hipGetLastError();
+  return launch_timed(kern, dim3((unsigned)nblocks), dim3(WAVES * 64), s, x, c, cn, ids, (int)N,
+                      (int)d, (int)K, bpb, (int)total, (int)nblocks);
 }
 
 template <int DT, int KS, int NF, int TK, int WAVES>

@@ -598,9 +598,8 @@ hipError_t launch_splitd(const uint16_t* x, const uint16_t* c, const float* cn, 
   // a multiple of 8 so each block's point blocks stay on its XCD
   int64_t nblocks = resident >= 8 ? resident / 8 * 8 : resident;
   if (nblocks > total) nblocks = total;
-  kern<<<(unsigned)nblocks, kThreads, 0, s>>>(x, c, cn, ids, (int)N, (int)d, (int)K, bpb,
-                                              (int)total, (int)nblocks);
-  return hipGetLastError();
+  return launch_timed(kern, dim3((unsigned)nblocks), dim3(kThreads), s, x, c, cn, ids, (int)N,
+                      (int)d, (int)K, bpb, (int)total, (int)nblocks);
 }
 
 template <int DT, int NSUB>
@@ -613,9 +612,8 @@ hipError_t launch_splitd_lds(const uint16_t* x, const uint16_t* c, const float* 
   if (resident <= 0) return hipErrorInvalidConfiguration;
   int64_t nblocks = resident >= 8 ? resident / 8 * 8 : resident;
   if (nblocks > total) nblocks = total;
-  kern<<<(unsigned)nblocks, kThreads, 0, s>>>(x, c, cn, ids, (int)N, (int)d, (int)K, bpb,
-                                              (int)total, (int)nblocks);
-  return hipGetLastError();
+  return launch_timed(kern, dim3((unsigned)nblocks), dim3(kThreads), s, x, c, cn, ids, (int)N,
+                      (int)d, (int)K, bpb, (int)total, (int)nblocks);
 }
 
 // Split-D tile candidates: the centroid tile (256 or 128 rows) and the

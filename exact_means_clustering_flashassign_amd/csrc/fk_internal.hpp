@@ -3,8 +3,11 @@
 // launchers each kernel file exports to the API layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
 
 #include "../../include/fkmeans.h"
 
@@ -256,6 +259,36 @@ __device__ __forceinline__ void pending_segment(const PendingFinish& pf, int64_t
   const int32_t* ob = pf.offsets + b * (pf.K + 1);
   const int l = ob[k], h = ob[k + 1];
   if (is_long(l, h)) lo = l, hi = h;
+}
+
+// ---------------------------------------------------------------------------
+// Timed launches: events that the next launch_timed stamps with that kernel's
+// own start and end (hipExtLaunchKernel), so timing a phase adds no packets
+// to the stream. Set by the caller's trace, taken by one launch (per thread).
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+template <typename... P, typename... A>
+hipError_t launch_timed(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "one value per kernel parameter");
+  LaunchEvents& le = launch_events();
+  if (!le.start && !le.stop) {
+    kernel<<<grid, block, 0, s>>>(static_cast<P>(args)...);
+    return hipGetLastError();
+  }
+  const LaunchEvents ev = le;
+  le = LaunchEvents();
+  std::tuple<P...> vals{static_cast<P>(args)...};
+  void* argv[sizeof...(P) > 0 ? sizeof...(P) : 1];
+  std::apply([&](auto&... v) {
+    size_t i = 0;
+    ((argv[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s,
+                            ev.start, ev.stop, 0);
 }
 
 // ---------------------------------------------------------------------------

@@ -98,8 +98,8 @@ hipError_t run_norms_vec(float* c, uint16_t* c_lp, float* cnorm, int64_t rows, i
   constexpr int RPB = kWaves * (64 / LPR);       // rows per block
   const int64_t grid = (rows + RPB - 1) / RPB;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  norms_vec_kernel<DT, LPR><<<(unsigned)grid, 256, 0, s>>>(c, c_lp, cnorm, rows, (int)d, pf);
-  return hipGetLastError();
+  return launch_timed(norms_vec_kernel<DT, LPR>, dim3((unsigned)grid), dim3(256), s, c, c_lp, cnorm,
+                      rows, (int)d, pf);
 }
 
 // lanes per row: the vectors of a row, rounded up to a power of two in [4, 64]
@@ -183,12 +183,13 @@ hipError_t launch_norms(const float* c_in, void* c_lp, float* cnorm, int dt, int
     return norms_vec_dt<FK_BF16>(c, (uint16_t*)c_lp, cnorm, rows, d, pf, s);
   const unsigned grid = (unsigned)((rows + kWaves - 1) / kWaves);
   if (dt == FK_F16)
-    norms_kernel<FK_F16><<<grid, 256, 0, s>>>(c, (uint16_t*)c_lp, cnorm, rows, d, pf);
-  else if (dt == FK_BF16)
-    norms_kernel<FK_BF16><<<grid, 256, 0, s>>>(c, (uint16_t*)c_lp, cnorm, rows, d, pf);
-  else
-    norms_f32_kernel<<<grid, 256, 0, s>>>(c, (float*)c_lp, cnorm, rows, d, pf);
-  return hipGetLastError();
+    return launch_timed(norms_kernel<FK_F16>, dim3(grid), dim3(256), s, c, (uint16_t*)c_lp, cnorm,
+                        rows, d, pf);
+  if (dt == FK_BF16)
+    return launch_timed(norms_kernel<FK_BF16>, dim3(grid), dim3(256), s, c, (uint16_t*)c_lp, cnorm,
+                        rows, d, pf);
+  return launch_timed(norms_f32_kernel, dim3(grid), dim3(256), s, c, (float*)c_lp, cnorm, rows, d,
+                      pf);
 }
 
 hipError_t launch_widen(const void* src, float* dst, int dt, int64_t count, hipStream_t s) {

@@ -239,13 +239,18 @@ size_t fk_workspace_size_host(fk_dtype_t dt, int64_t B, int64_t chunk, int64_t d
 
 /*
  * Optional timing trace of fk_lloyd (process-wide, not thread-safe).
- * fk_trace_begin(capacity) turns it on: each fk_lloyd iteration records HIP
- * events around its norms, assign and update phases on the call's stream, for
- * up to `capacity` iterations in total. fk_trace_end waits for the events,
- * writes the per-phase totals and turns the trace off.
+ * fk_trace_begin(capacity) turns it on for up to `capacity` iterations in
+ * total. Each traced iteration's norms and assign kernels are launched with
+ * HIP events that the launches themselves stamp at the kernel's start and end
+ * (hipExtLaunchKernel), so the trace puts nothing between kernels; an
+ * iteration's update runs from its assign's end to the next iteration's
+ * norms start, and the last iteration a call traces ends on one stream
+ * marker after its update. fk_trace_end waits for the events, writes the
+ * per-phase totals and turns the trace off.
  */
 typedef struct {
-  int32_t iterations;   /* iterations recorded                      */
+  int32_t iterations;   /* iterations recorded (with tol > 0, the one
+                           run past a stop and undone is included)    */
   double norms_ms;      /* summed GPU time of fk_norms phases        */
   double assign_ms;     /* summed GPU time of the assign kernel      */
   double update_ms;     /* summed GPU time of the update kernels     */

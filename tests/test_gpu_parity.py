@@ -508,13 +508,51 @@ def test_status_codes_through_binding(fk):
     assert e.value.status == 1
 
 
-def test_trace_records_phases(fk):
-    w = synthdata.make_workload("io_breakdown", scale_n=20000, B=2)
+@pytest.mark.parametrize("wl,kw", [("io_breakdown", {"scale_n": 20000, "B": 2}),
+                                   ("split_d", {"scale_n": 4096, "B": 2}),
+                                   ("tiny_f32", {})])
+def test_trace_records_phases(fk, wl, kw):
+    """The trace's phases (kernel-stamped norms and assign, update between
+    them) are positive and add up to at most the call's own time on the
+    stream, and to most of it."""
+    torch = _torch()
+    w = synthdata.make_workload(wl, **kw)
+    x, init = to_dev(w.x, w.dtype), to_dev(w.init, w.dtype)
+    fk.fk_lloyd(x, init, 1, 0.0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fk.fk_trace_begin(8)
-    fk.fk_lloyd(to_dev(w.x, w.dtype), to_dev(w.init, w.dtype), 5, 0.0)
+    e0.record()
+    fk.fk_lloyd(x, init, 5, 0.0)
+    e1.record()
+    torch.cuda.synchronize()
     tr = fk.fk_trace_end()
     assert tr["iterations"] == 5
     assert tr["assign_ms"] > 0 and tr["update_ms"] > 0 and tr["norms_ms"] > 0
+    total = tr["norms_ms"] + tr["assign_ms"] + tr["update_ms"]
+    wall = e0.elapsed_time(e1)
+    print(wl, f"phases {total:.4f} ms of {wall:.4f} ms")
+    assert 0.5 * wall <= total <= 1.02 * wall + 0.02
+
+
+def test_trace_over_calls_and_capacity(fk):
+    """One trace over two calls, its capacity ending inside the second, and a
+    traced run with a tol stop: every traced iteration is counted."""
+    w = synthdata.make_workload("io_breakdown", scale_n=20000, B=2)
+    x, init = to_dev(w.x, w.dtype), to_dev(w.init, w.dtype)
+    fk.fk_trace_begin(3)
+    fk.fk_lloyd(x, init, 2, 0.0)
+    fk.fk_lloyd(x, init, 2, 0.0)
+    tr = fk.fk_trace_end()
+    assert tr["iterations"] == 3
+    assert min(tr["norms_ms"], tr["assign_ms"], tr["update_ms"]) > 0
+    fk.fk_trace_begin(100)
+    _, _, n = fk.fk_lloyd(x, init, 100, 1e-3)
+    tr = fk.fk_trace_end()
+    print(f"tol run: {n} iterations, {tr['iterations']} traced")
+    # a tol stop runs one iteration past the stop, then undoes it
+    assert 1 <= n <= 100 and tr["iterations"] in (n, n + 1)
+    assert min(tr["norms_ms"], tr["assign_ms"], tr["update_ms"]) > 0
 
 
 # ---------------------------------------------------------------------------
