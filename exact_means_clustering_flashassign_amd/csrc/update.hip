@@ -814,21 +814,27 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
   int32_t* ko = keys_out ? keys_out + (int64_t)b * N : nullptr;
   int32_t* xo = idx_out ? idx_out + (int64_t)b * N : nullptr;
   const int n0 = g * rc, n1 = min(n0 + rc, N);
+  // a sub-chunk's keys (and indices) are loaded while the one before is
+  // being sorted (clamped, unconditional loads: all in flight together)
+  int kk[SPW], xx[SPW];
+  auto load_sub = [&](int m0, int (&kv)[SPW], int (&xv)[SPW]) {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int i = min(m0 + j * kSortThreads + t, n1 - 1);
+      kv[j] = kb[i];
+      xv[j] = xb && !packed_in ? xb[i] : i;
+    }
+  };
+  if (n0 < n1) load_sub(n0, kk, xx);
   for (int m0 = n0; m0 < n1; m0 += kRadixSub) {
     const int m = min(kRadixSub, n1 - m0);
-    int kk[SPW], xx[SPW];
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {               // unconditional: loads in flight together
-      const int i = min(m0 + j * kSortThreads + t, n1 - 1);
-      kk[j] = kb[i];
-      xx[j] = packed_in ? kk[j] & 0xFFFFFF : (xb ? xb[i] : i);
-    }
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int l = j * kSortThreads + t;
       skey[l] = packed_in ? kk[j] : (int32_t)radix_key(kk[j], K);
-      sidx[l] = xx[j];
+      sidx[l] = packed_in ? kk[j] & 0xFFFFFF : xx[j];
     }
+    if (m0 + kRadixSub < n1) load_sub(m0 + kRadixSub, kk, xx);
     for (int r = lane; r < kRadix; r += 64) hist[w * kRadix + r] = 0;
     __syncthreads();
     const int per = wave_span(m);
