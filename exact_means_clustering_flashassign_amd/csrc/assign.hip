@@ -61,30 +61,38 @@ struct Argmax {
 
 // Part `part` (0..7) of draining accumulator `acc` of subtile g into st.
 // The work is split so it can be spread over the k-steps of the next
-// subtile: parts 0-3 code the scores and build the max tree, part 4
-// compares, parts 5-7 are empty.
+// subtile in even pieces: parts 0-6 code two or three scores each and fold
+// them into the two partial maxima, part 7 compares. With 8 k-steps a
+// subtile (d = 128) each k-step carries one part per fragment, so the VALU
+// work under each pair of MFMAs stays the same size.
 __device__ __forceinline__ void drain_part(const floatx16_t& acc, int part, int g, Argmax& st,
                                            float (&m)[2], bool& gt) {
   switch (part) {
     case 0:
       m[0] = vmax3(code_slot(acc[0], 0), code_slot(acc[1], 1), code_slot(acc[2], 2));
-      m[1] = vmax3(code_slot(acc[3], 3), code_slot(acc[4], 4), code_slot(acc[5], 5));
       break;
     case 1:
-      m[0] = vmax3(m[0], code_slot(acc[6], 6), code_slot(acc[7], 7));
-      m[1] = vmax3(m[1], code_slot(acc[8], 8), code_slot(acc[9], 9));
+      m[1] = vmax3(code_slot(acc[3], 3), code_slot(acc[4], 4), code_slot(acc[5], 5));
       break;
     case 2:
+      m[0] = vmax3(m[0], code_slot(acc[6], 6), code_slot(acc[7], 7));
+      break;
+    case 3:
+      m[1] = vmax3(m[1], code_slot(acc[8], 8), code_slot(acc[9], 9));
+      break;
+    case 4:
       m[0] = vmax3(m[0], code_slot(acc[10], 10), code_slot(acc[11], 11));
+      break;
+    case 5:
       m[1] = vmax3(m[1], code_slot(acc[12], 12), code_slot(acc[13], 13));
       break;
-    case 3: {
+    case 6: {
       const float c15 = code_slot(acc[15], 15);
       m[0] = vmax3(m[0], m[1], code_slot(acc[14], 14));
       m[0] = vmax3(m[0], c15, c15);
       break;
     }
-    case 4:
+    case 7:
       gt = m[0] > st.best;
       st.best = gt ? m[0] : st.best;
       st.btile = gt ? g : st.btile;
