@@ -704,7 +704,8 @@ __global__ __launch_bounds__(kSortThreads) void scatter_stable_kernel(
 // Keys outside [0, K) are taken as K: they sort after every real key.
 // Two passes over at most 2^24 points keep one 32-bit word per point between
 // them: the first pass writes (key >> 8) << 24 | point index (the low digit
-// is no longer needed), the second sorts by its top byte.
+// is no longer needed), the second sorts by its top byte; both run
+// radix_scatter_packed, which holds one word per key in LDS as well.
 constexpr int kRadix = kRadixDigits;
 constexpr int kRadixChunk = 16384;             // chunk length without a split sort before
 constexpr int kRadixSub = 4096;
@@ -763,9 +764,8 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(const int32_t* __r
 
 // keys_in null: the keys are the ids themselves and the point index is the
 // position (first pass). keys_out null: last pass, only the index goes out.
-// pack_out: keys_out receives the packed words (idx_out unused); packed_in:
-// keys_in holds them (idx_in unused), sorted by their top byte (shift 24).
-// Each sub-chunk is reordered by digit in LDS first (the second walk keeps
+// (Sorts of two passes over at most 2^24 points take the packed kernel
+// below.) Each sub-chunk is reordered by digit in LDS first (the second walk keeps
 // its keys in registers, then stores them at their local sorted places), so
 // the global stores go out as runs of consecutive addresses, one run per
 // digit.
@@ -773,8 +773,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ keys_in,
     const int32_t* __restrict__ idx_in, const int32_t* __restrict__ rhist,
     const int32_t* __restrict__ rgbase, int32_t* __restrict__ keys_out,
-    int32_t* __restrict__ idx_out, int N, int K, int G, int RG, int shift, bool pack_out,
-    bool packed_in, int rc) {
+    int32_t* __restrict__ idx_out, int N, int K, int G, int RG, int shift, int rc) {
   __shared__ int32_t skey[kRadixSub];
   __shared__ int32_t sidx[kRadixSub];
   __shared__ int32_t hist[kRadix * kWavesSort];
@@ -822,7 +821,7 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     for (int j = 0; j < SPW; ++j) {
       const int i = min(m0 + j * kSortThreads + t, n1 - 1);
       kv[j] = kb[i];
-      xv[j] = xb && !packed_in ? xb[i] : i;
+      xv[j] = xb ? xb[i] : i;
     }
   };
   if (n0 < n1) load_sub(n0, kk, xx);
@@ -831,8 +830,8 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int l = j * kSortThreads + t;
-      skey[l] = packed_in ? kk[j] : (int32_t)radix_key(kk[j], K);
-      sidx[l] = packed_in ? kk[j] & 0xFFFFFF : xx[j];
+      skey[l] = (int32_t)radix_key(kk[j], K);
+      sidx[l] = xx[j];
     }
     if (m0 + kRadixSub < n1) load_sub(m0 + kRadixSub, kk, xx);
     for (int r = lane; r < kRadix; r += 64) hist[w * kRadix + r] = 0;
@@ -891,12 +890,141 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     for (int l = t; l < m; l += kSortThreads) {
       const int key = skey[l];
       const int pos = gbase[((uint32_t)key >> shift) & (kRadix - 1)] + l;
-      if (pack_out) {
-        ko[pos] = (int32_t)((((uint32_t)key >> 8) << 24) | (uint32_t)sidx[l]);
-      } else {
-        if (ko) ko[pos] = key;
-        xo[pos] = sidx[l];
+      if (ko) ko[pos] = key;
+      xo[pos] = sidx[l];
+    }
+    __syncthreads();
+  }
+}
+
+// The two passes of a packed sort (keys below 2^16, at most 2^24 points):
+// one 32-bit word per key, both in registers and in LDS.
+//   FIRST: keys are the ids and the point index is the position; the word
+//          is key << 12 | the key's index within its sub-chunk, and the
+//          pass writes the packed word (key >> 8) << 24 | point index;
+//   else:  keys are those packed words, sorted by their top byte, and the
+//          pass writes the point index (the low 24 bits) into perm.
+// Wave w loads its own consecutive range of a sub-chunk (64 keys per step),
+// so the keys stay in registers: one LDS atomic per key on the wave's digit
+// counts gives its rank among the same-digit keys before it in the wave
+// (lanes of one atomic rank in lane order), the counts become starts by a
+// scan over (digit, wave), and each word goes to start + rank in LDS. The
+// global stores then go out in local sorted order: runs of consecutive
+// addresses, one per digit. The next sub-chunk's keys load during the
+// current one.
+template <bool FIRST>
+__global__ __launch_bounds__(kSortThreads) void radix_scatter_packed_kernel(
+    const int32_t* __restrict__ keys, const int32_t* __restrict__ rhist,
+    const int32_t* __restrict__ rgbase, int32_t* __restrict__ out, int N, int K, int G, int RG,
+    int rc) {
+  __shared__ uint32_t sw[kRadixSub];               // words in local sorted order
+  __shared__ int32_t hist[kWavesSort * kRadix];    // per-wave digit counts, then starts
+  __shared__ int32_t carry[kRadix];                // next global position of each digit
+  __shared__ int32_t gbase[kRadix];                // global position minus local position
+  __shared__ int32_t wtot[kWavesSort];
+  constexpr int QS = kSortThreads / kRadix;        // row quarters for the chunk start
+  constexpr int SPW = kRadixSub / kSortThreads;    // keys per lane per sub-chunk
+  constexpr int SHIFT = FIRST ? 12 : 24;           // digit position in a word
+  static_assert(kRadixSub <= 4096, "local index in 12 bits");
+  static_assert(kRadixRows % QS == 0, "rows per quarter");
+  const int b = blockIdx.x / G, g = blockIdx.x % G, t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int32_t* kb = keys + (int64_t)b * N;
+  // chunk start per digit: its group's start plus the group's earlier chunks
+  {
+    const int r = t % kRadix, q = t / kRadix;
+    const int gs = g / kRadixRows * kRadixRows;
+    const int a0 = gs + q * (kRadixRows / QS), a1 = min(a0 + kRadixRows / QS, g);
+    const int32_t* hr = rhist + (int64_t)b * G * kRadix;
+    int v[kRadixRows / QS];
+#pragma unroll
+    for (int j = 0; j < kRadixRows / QS; ++j)   // unconditional: loads in flight together
+      v[j] = hr[(int64_t)min(a0 + j, G - 1) * kRadix + r];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kRadixRows / QS; ++j) sum += a0 + j < a1 ? v[j] : 0;
+    hist[q * kRadix + r] = sum;
+  }
+  __syncthreads();
+  if (t < kRadix) {
+    int c = rgbase[((int64_t)b * RG + g / kRadixRows) * kRadix + t];
+#pragma unroll
+    for (int q = 0; q < QS; ++q) c += hist[q * kRadix + t];
+    carry[t] = c;
+  }
+  __syncthreads();
+  for (int r = lane; r < kRadix; r += 64) hist[w * kRadix + r] = 0;
+  int32_t* ob = out + (int64_t)b * N;
+  const int n0 = g * rc, n1 = min(n0 + rc, N);
+  // the wave's range of sub-chunk m0 and the lane's keys in it (clamped,
+  // unconditional loads: all in flight together)
+  auto span = [&](int m0, int& s0, int& s1) {
+    const int m = min(kRadixSub, n1 - m0), per = wave_span(m);
+    s0 = min(w * per, m);
+    s1 = min(s0 + per, m);
+  };
+  int kk[SPW];
+  auto load_sub = [&](int m0, int (&kv)[SPW]) {
+    int s0, s1;
+    span(m0, s0, s1);
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) kv[j] = kb[min(m0 + s0 + j * 64 + lane, n1 - 1)];
+  };
+  if (n0 < n1) load_sub(n0, kk);
+  __syncthreads();
+  for (int m0 = n0; m0 < n1; m0 += kRadixSub) {
+    const int m = min(kRadixSub, n1 - m0);
+    int s0, s1;
+    span(m0, s0, s1);
+    uint32_t wd[SPW];
+    int rk[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int i = s0 + j * 64 + lane;
+      wd[j] = FIRST ? radix_key(kk[j], K) << 12 | (uint32_t)i : (uint32_t)kk[j];
+    }
+    if (m0 + kRadixSub < n1) load_sub(m0 + kRadixSub, kk);
+    // rank within the wave
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      rk[j] = 0;
+      if (s0 + j * 64 + lane < s1)
+        rk[j] = atomicAdd(&hist[w * kRadix + ((wd[j] >> SHIFT) & (kRadix - 1))], 1);
+    }
+    __syncthreads();
+    // local start of each (digit, wave): digits in order, waves in order
+    int hv[kWavesSort];
+    int tot = 0;
+    if (t < kRadix) {
+#pragma unroll
+      for (int ww = 0; ww < kWavesSort; ++ww) hv[ww] = hist[ww * kRadix + t];
+#pragma unroll
+      for (int ww = 0; ww < kWavesSort; ++ww) tot += hv[ww];
+    }
+    int all;
+    const int lstart = block_exclusive_scan(t < kRadix ? tot : 0, wtot, all);
+    if (t < kRadix) {
+      int run = lstart;
+#pragma unroll
+      for (int ww = 0; ww < kWavesSort; ++ww) {
+        hist[ww * kRadix + t] = run;
+        run += hv[ww];
       }
+      gbase[t] = carry[t] - lstart;
+      carry[t] += tot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+      if (s0 + j * 64 + lane < s1)
+        sw[hist[w * kRadix + ((wd[j] >> SHIFT) & (kRadix - 1))] + rk[j]] = wd[j];
+    __syncthreads();
+    for (int r = lane; r < kRadix; r += 64) hist[w * kRadix + r] = 0;
+    for (int l = t; l < m; l += kSortThreads) {
+      const uint32_t x = sw[l];
+      const int pos = gbase[(x >> SHIFT) & (kRadix - 1)] + l;
+      ob[pos] = FIRST ? (int32_t)((x >> 20) << 24 | (uint32_t)(m0 + (int)(x & 4095)))
+                      : (int32_t)(x & 0xFFFFFF);
     }
     __syncthreads();
   }
@@ -1858,9 +1986,16 @@ hipError_t run_radix(const int32_t* ids, int64_t B, int64_t N, int64_t K, const 
       radix_scan_kernel<<<(unsigned)B, kThreads, 0, s>>>(cs, ws.rgbase, (int)RG);
       FK_CHECK(hipGetLastError());
     }
-    radix_scatter_kernel<<<(unsigned)(B * G), kSortThreads, 0, s>>>(
-        ids, kin, pin ? nullptr : xin, ws.rhist, ws.rgbase, kout, xout, (int)N, (int)K, (int)G,
-        (int)RG, shift, pout, pin, (int)rc);
+    if (pout)
+      radix_scatter_packed_kernel<true><<<(unsigned)(B * G), kSortThreads, 0, s>>>(
+          ids, ws.rhist, ws.rgbase, kout, (int)N, (int)K, (int)G, (int)RG, (int)rc);
+    else if (pin)
+      radix_scatter_packed_kernel<false><<<(unsigned)(B * G), kSortThreads, 0, s>>>(
+          kin, ws.rhist, ws.rgbase, xout, (int)N, (int)K, (int)G, (int)RG, (int)rc);
+    else
+      radix_scatter_kernel<<<(unsigned)(B * G), kSortThreads, 0, s>>>(
+          ids, kin, xin, ws.rhist, ws.rgbase, kout, xout, (int)N, (int)K, (int)G, (int)RG, shift,
+          (int)rc);
     FK_CHECK(hipGetLastError());
     kin = kout;
     xin = xout;
