@@ -465,13 +465,13 @@ __global__ __launch_bounds__(kThreads) void offsets_runs_kernel(
 }
 
 // Direct scatter (ids in at most kDirectKeyBits bits, chunks of at most
-// kStableChunk ids): the chunk's ids are staged in LDS and walked twice, wave
-// w over its own consecutive range in steps of 64, counting into its own
-// counters. The first walk counts each id per wave; prefixes over the waves
-// (per id) and over the ids then give each (id, wave) its first rank among
-// the chunk's points of that id, and where the id's points start in the
-// chunk's id order. The second walk's counters return each point's rank r,
-// and point n goes to
+// kStableChunk ids): wave w loads its own consecutive range of the chunk
+// into registers and walks it once in steps of 64, counting into its own
+// counters; each atomic returns the point's rank among the wave's earlier
+// points of its id. Prefixes over the waves (per id) and over the ids then
+// give each (id, wave) its first rank among the chunk's points of that id,
+// and where the id's points start in the chunk's id order. With r = the
+// wave's first rank plus the point's rank in the wave, point n goes to
 //   perm[offsets[id] + H[g][id] + r]
 // The ranks follow the walk (earlier waves, earlier steps, and within a step
 // the order in which the LDS unit serves one instruction's lanes), never the
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kSortThreads) void scatter_direct_kernel(
   const int n = min(chunk, N - n0);
   if (n <= 0) return;                            // whole block: no barrier follows
   const int K1 = K + 1;
-  int32_t* skey = sdir;                          // chunk: ids, then global positions
+  int32_t* spos = sdir;                          // chunk: global positions in id order
   int32_t* sval = sdir + chunk;                  // chunk: point indices in id order
   int32_t* gstart = sval + chunk;                // K + 1
   int32_t* lstart = gstart + K1;                 // K + 1
@@ -509,18 +509,17 @@ __global__ __launch_bounds__(kSortThreads) void scatter_direct_kernel(
   uint32_t* mycnt = cnt + (w >> 1) * K1;
   const uint32_t inc = 1u << (16 * (w & 1));
   const int sh = 16 * (w & 1);
+  // the wave's consecutive range of the chunk; its ids stay in registers
+  const int per = wave_span(n);
+  const int s0 = min(w * per, n), s1 = min(s0 + per, n);
   const int32_t* ib = ids + (int64_t)b * N + n0;
-  for (int m = 0; m < n; m += kSortThreads * kSortUnroll) {
-    int kk[kSortUnroll];
+  int kk[SMAX];
 #pragma unroll
-    for (int q = 0; q < kSortUnroll; ++q) {
-      const int i = m + q * kSortThreads + t;
-      kk[q] = ib[min(i, n - 1)];                 // unconditional: loads in flight together
-    }
-#pragma unroll
-    for (int q = 0; q < kSortUnroll; ++q) {
-      const int i = m + q * kSortThreads + t;
-      if (i < n) skey[i] = (unsigned)kk[q] < (unsigned)K ? kk[q] : K;
+  for (int j = 0; j < SMAX; ++j) {
+    const int i = s0 + j * 64 + lane;
+    if (j * 64 < per) {                          // wave-uniform
+      const int k = ib[min(i, n - 1)];
+      kk[j] = (unsigned)k < (unsigned)K ? k : K;
     }
   }
   const int32_t* hr = H + ((int64_t)b * G + g) * K;
@@ -528,9 +527,14 @@ __global__ __launch_bounds__(kSortThreads) void scatter_direct_kernel(
   for (int k = t; k < K; k += kSortThreads) gstart[k] = ob[k] + hr[k];
   for (int e = t; e < WP * K1; e += kSortThreads) cnt[e] = 0;
   __syncthreads();
-  const int per = wave_span(n);
-  const int s0 = min(w * per, n), s1 = min(s0 + per, n);
-  for (int i = s0 + lane; i < s1; i += 64) atomicAdd(&mycnt[skey[i]], inc);
+  // one walk: each point's rank among the wave's earlier points of its id
+  int rk[SMAX];
+#pragma unroll
+  for (int j = 0; j < SMAX; ++j) {
+    rk[j] = -1;
+    if (j * 64 < per && s0 + j * 64 + lane < s1)
+      rk[j] = (int)((atomicAdd(&mycnt[kk[j]], inc) >> sh) & 0xFFFFu);
+  }
   __syncthreads();
   // per id: prefix over the waves and the id's total; ids are spread over
   // the threads in consecutive groups so one scan gives their local starts
@@ -559,32 +563,21 @@ __global__ __launch_bounds__(kSortThreads) void scatter_direct_kernel(
     run += c;
   }
   __syncthreads();
-  // second walk: each point's place in the chunk's id order and its global
-  // position, held in registers until every wave has read its ids
-  int lp[SMAX], gp[SMAX];
+  // each point's place in the chunk's id order and its global position
 #pragma unroll
   for (int j = 0; j < SMAX; ++j) {
-    const int i = s0 + j * 64 + lane;
-    lp[j] = gp[j] = -1;
-    if (i < s1) {
-      const int key = skey[i];
-      const int r = (int)((atomicAdd(&mycnt[key], inc) >> sh) & 0xFFFFu);
-      lp[j] = lstart[key] + r;
-      gp[j] = key < K ? gstart[key] + r : -1;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < SMAX; ++j) {
-    if (lp[j] >= 0) {
-      skey[lp[j]] = gp[j];
-      sval[lp[j]] = n0 + s0 + j * 64 + lane;
+    if (rk[j] >= 0) {
+      const int key = kk[j];
+      const int r = (int)((mycnt[key] >> sh) & 0xFFFFu) + rk[j];
+      const int lp = lstart[key] + r;
+      spos[lp] = key < K ? gstart[key] + r : -1;
+      sval[lp] = n0 + s0 + j * 64 + lane;
     }
   }
   __syncthreads();
   int32_t* pb = perm + (int64_t)b * N;
   for (int l = t; l < n; l += kSortThreads) {
-    const int pos = skey[l];
+    const int pos = spos[l];
     if (pos >= 0) pb[pos] = sval[l];
   }
 }
@@ -907,7 +900,8 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
 // Wave w loads its own consecutive range of a sub-chunk (64 keys per step),
 // so the keys stay in registers: one LDS atomic per key on the wave's digit
 // counts gives its rank among the same-digit keys before it in the wave
-// (lanes of one atomic rank in lane order), the counts become starts by a
+// (in the walk's order: earlier steps, and within a step the order in which
+// the LDS unit serves one instruction's lanes), the counts become starts by a
 // scan over (digit, wave), and each word goes to start + rank in LDS. The
 // global stores then go out in local sorted order: runs of consecutive
 // addresses, one per digit. The next sub-chunk's keys load during the
