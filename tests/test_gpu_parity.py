@@ -514,7 +514,8 @@ def test_status_codes_through_binding(fk):
 def test_trace_records_phases(fk, wl, kw):
     """The trace's phases (kernel-stamped norms and assign, update between
     them) are positive and add up to at most the call's own time on the
-    stream, and to most of it."""
+    stream, and (where the device, not the launches, sets the pace) to most
+    of it."""
     torch = _torch()
     w = synthdata.make_workload(wl, **kw)
     x, init = to_dev(w.x, w.dtype), to_dev(w.init, w.dtype)
@@ -532,7 +533,12 @@ def test_trace_records_phases(fk, wl, kw):
     total = tr["norms_ms"] + tr["assign_ms"] + tr["update_ms"]
     wall = e0.elapsed_time(e1)
     print(wl, f"phases {total:.4f} ms of {wall:.4f} ms")
-    assert 0.5 * wall <= total <= 1.02 * wall + 0.02
+    assert total <= 1.02 * wall + 0.02
+    # the tiny problem is launch-bound: its kernels take a few microseconds
+    # each and the stream idles between launches, so only the upper bound
+    # holds there
+    if wl != "tiny_f32":
+        assert 0.5 * wall <= total
 
 
 def test_trace_over_calls_and_capacity(fk):
