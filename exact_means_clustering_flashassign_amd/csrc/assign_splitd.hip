@@ -2,7 +2,9 @@
 // inner D loop.
 //
 // Same contraction and argmax as the small-D path (score_k = x.c_k -
-// ||c_k||^2 / 2, lowest k on ties; the distance matrix is never written), but
+// ||c_k||^2 / 2; the distance matrix is never written; the register-staged
+// kernel keeps the lowest k on exact ties, the LDS-staged one orders scores
+// that agree to the fp32 rounding by a slot code, as small-D does), but
 // a point's fragments no longer fit in registers for the whole K range, so the
 // loop order flips: a block holds a (256 points x TK centroids) score block in
 // accumulator registers and walks d in chunks ("Flash-KMeans: Fast and
@@ -56,6 +58,55 @@ __device__ __forceinline__ void argmax_update(const floatx16_t& acc, int base, f
     const bool gt = v > best;
     best = gt ? v : best;
     bidx = gt ? base + 8 * (r >> 2) + (r & 3) : bidx;
+  }
+}
+
+// The LDS-staged kernel's argmax over one K tile, slot-coded as in the
+// small-D path: each accumulator's 16 scores x.c - ||c||^2/2 (one fma on the
+// accumulator and the staged norm) get their slot in the 4 low mantissa bits,
+// one v_max3 tree gives the lane's best of the 16 and its slot, and a strict
+// '>' against the running best keeps the earlier row block. The code moves a
+// score by less than 2^-19 of its magnitude, so it only orders scores that
+// agree to the fp32 rounding of the accumulation; among those the row is
+// either one. GUARD: the tile runs past K, and rows at or past K (zero rows
+// and zero norms in LDS) are set to a score that never wins.
+template <int NSUB, bool GUARD>
+__device__ __forceinline__ void drain_tile_coded(const floatx16_t (&acc)[NSUB][kNF],
+                                                 const float* __restrict__ hrow, int left0,
+                                                 int base, float (&best)[kNF], int (&bt)[kNF]) {
+#pragma unroll
+  for (int sub = 0; sub < NSUB; ++sub) {
+    float hv[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(hrow + sub * 32 + 8 * i);
+      hv[4 * i + 0] = v.x;
+      hv[4 * i + 1] = v.y;
+      hv[4 * i + 2] = v.z;
+      hv[4 * i + 3] = v.w;
+    }
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) {
+      float sc[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // -0.5 * ||c||^2 is exact, so the fma rounds once, as the sum did
+        const float v = __builtin_fmaf(hv[r], -0.5f, acc[sub][f][r]);
+        sc[r] = code_slot(GUARD && sub * 32 + 8 * (r >> 2) + (r & 3) >= left0 ? kNeverWins : v, r);
+      }
+      float m0 = vmax3(sc[0], sc[1], sc[2]);
+      float m1 = vmax3(sc[3], sc[4], sc[5]);
+      m0 = vmax3(m0, sc[6], sc[7]);
+      m1 = vmax3(m1, sc[8], sc[9]);
+      m0 = vmax3(m0, sc[10], sc[11]);
+      m1 = vmax3(m1, sc[12], sc[13]);
+      m0 = vmax3(m0, m1, sc[14]);
+      m0 = vmax3(m0, sc[15], sc[15]);
+      const bool gt = m0 > best[f];
+      best[f] = gt ? m0 : best[f];
+      bt[f] = gt ? base + sub * 32 : bt[f];
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -524,30 +575,23 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
           asm volatile("" ::: "memory");
         }
       }
-      // scores x.c - ||c||^2/2 (-inf past K), then the running argmax
-#pragma unroll
-      for (int sub = 0; sub < NSUB; ++sub) {
-        floatx16_t h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = sub * 32 + 8 * i + 4 * half;
-          const float4 hv = *reinterpret_cast<const float4*>(&lds_h[tc & 1][r]);
-          const int left = K - kt * TK - r;       // rows r .. r+3 exist while left > j
-          h[4 * i + 0] = left > 0 ? -0.5f * hv.x : -INFINITY;
-          h[4 * i + 1] = left > 1 ? -0.5f * hv.y : -INFINITY;
-          h[4 * i + 2] = left > 2 ? -0.5f * hv.z : -INFINITY;
-          h[4 * i + 3] = left > 3 ? -0.5f * hv.w : -INFINITY;
-        }
-#pragma unroll
-        for (int f = 0; f < kNF; ++f) argmax_update(acc[sub][f] + h, kt * TK + sub * 32, best[f], bidx[f]);
-        __builtin_amdgcn_sched_barrier(0);
+      // scores x.c - ||c||^2/2, then the running argmax (rows of the lane
+      // relative to the tile: sub*32 + 8i + 4*half + j; those at or past
+      // K - kt*TK never win)
+      {
+        const float* hrow = &lds_h[tc & 1][4 * half];
+        const int left0 = K - kt * TK - 4 * half;
+        if (kt * TK + TK <= K)
+          drain_tile_coded<NSUB, false>(acc, hrow, left0, kt * TK, best, bidx);
+        else
+          drain_tile_coded<NSUB, true>(acc, hrow, left0, kt * TK, best, bidx);
       }
       ++tc;
     }
     int32_t* ib = ids + (int64_t)pb * N;
 #pragma unroll
     for (int f = 0; f < kNF; ++f) {
-      const int idx = merge_halves(best[f], bidx[f], half);
+      const int idx = merge_halves(best[f], bidx[f] + slot_row(slot_of(best[f])), half);
       const int n = row0 + wave * kWaveRows + f * 32 + r32;
       if (half == 0 && n < N) ib[n] = idx;
     }

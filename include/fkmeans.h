@@ -97,11 +97,13 @@ fk_status_t fk_norms(const float* c, void* c_lp, float* cnorm, fk_dtype_t dt,
  * i.e. the nearest centroid to x[b,n] among c_lp[b,:].
  * Every type runs on the matrix cores with fp32 accumulation: fp16/bf16
  * products are exact, fp32 products are rounded to fp32. Ties: centroids
- * whose fp32 scores are equal, or (small-D path) agree to within 2^-19 of
- * their size -- the rounding of the fp32 sum itself, since that path carries
- * each score's row in its 4 low mantissa bits -- may resolve to either one;
- * between 32-row blocks and in the split-D path exact ties go to the lower
- * index. The small-D path covers fp16/bf16 d <= 512 and fp32 d <= 256. The
+ * whose fp32 scores are equal, or (small-D path, and the LDS-staged
+ * split-D kernel: aligned rows of a multiple of 128 units, with K <= 128 or
+ * enough points to give every CU a block) agree to within 2^-19 of their size --
+ * the rounding of the fp32 sum itself, since those kernels carry each
+ * score's row in its 4 low mantissa bits -- may resolve to either one;
+ * between 32-row blocks and in the other split-D kernel exact ties go to the
+ * lower index. The small-D path covers fp16/bf16 d <= 512 and fp32 d <= 256. The
  * result is the same on every run.
  * [hysenlabs] "The point of the kernel is that the distance matrix never
  * exists": points processed in tiles, centroids streamed in chunks, the
