@@ -392,7 +392,10 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
   // w*RPW + 8j .. +7; lane l writes slot l % 8 of row 8j + l / 8, i.e. unit
   // (l % 8) ^ cperm(row). Rows past K lie past the buffer's range and read as
   // zero (their norms are -inf: they never win).
-  auto stage_c = [&](unsigned char* dst, float* hdst, int pb, int rot, int t) {
+  // Loads jlo .. jhi-1 of the chunk (and, with norm, the norms' load), so a
+  // chunk's staging can be issued a few loads at a time between its MFMAs.
+  auto stage_c = [&](unsigned char* dst, float* hdst, int pb, int rot, int t, int jlo, int jhi,
+                     bool norm) {
     const int kt = t / nchunks;
     int ch = t - kt * nchunks + rot;
     ch = ch >= nchunks ? ch - nchunks : ch;
@@ -402,6 +405,7 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
         uniform_ptr(tb), 0, __builtin_amdgcn_readfirstlane(rows * (int)rowb), kRawBufferWord3);
 #pragma unroll
     for (int j = 0; j < NCL; ++j) {
+      if (j < jlo || j >= jhi) continue;
       const int row = wave * RPW + 8 * j + (lane >> 3);
       const uint32_t voff = (uint32_t)row * rowb + (uint32_t)(ch * kCRowB) +
                             (uint32_t)(((lane & 7) ^ cperm(row)) * 16);
@@ -413,19 +417,22 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
     // past the tile are never used). Every chunk stages the norms of its
     // successor's K tile into the slot of the next tile, which only the next
     // tile's start reads.
-    const auto rn = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(cnorm + (int64_t)pb * K), 0, __builtin_amdgcn_readfirstlane(K * 4),
-        kRawBufferWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rn, (lds_void_t*)(hdst + wave * 64), 4, (uint32_t)(kt * TK + lane) * 4 + wave * 256, 0,
-        0, 0);
+    if (norm) {
+      const auto rn = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(cnorm + (int64_t)pb * K), 0, __builtin_amdgcn_readfirstlane(K * 4),
+          kRawBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rn, (lds_void_t*)(hdst + wave * 64), 4, (uint32_t)(kt * TK + lane) * 4 + wave * 256, 0,
+          0, 0);
+    }
   };
   // Half hh (k-steps 2hh, 2hh+1) of point chunk t of the wave's 64 rows
   // (from row0 + wave*64) into the wave's part of slot array dst: load j
   // fills rows 16j .. 16j+15; lane l writes slot l % 4 of row 16j + l / 4,
   // i.e. unit (l % 4) ^ xperm(row). Rows past N read as zero (their ids are
   // never stored).
-  auto stage_x = [&](unsigned char* dst, int pb, int row0, int rot, int t, int hh) {
+  auto stage_x = [&](unsigned char* dst, int pb, int row0, int rot, int t, int hh, int jlo,
+                     int jhi) {
     int ch = t % nchunks + rot;
     ch = ch >= nchunks ? ch - nchunks : ch;
     const int r0 = row0 + wave * kWaveRows;
@@ -435,6 +442,7 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
         uniform_ptr(xb), 0, __builtin_amdgcn_readfirstlane(rows * (int)rowb), kRawBufferWord3);
 #pragma unroll
     for (int j = 0; j < NXL; ++j) {
+      if (j < jlo || j >= jhi) continue;
       const int row = 16 * j + (lane >> 2);
       const uint32_t voff = (uint32_t)row * rowb + (uint32_t)(ch * kCRowB + hh * kXRowB) +
                             (uint32_t)(((lane & 3) ^ xperm(row)) * 16);
@@ -478,10 +486,10 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
   // prologue: centroid chunk 0, point chunk 0 (both halves), point chunk 1's
   // first half (a chunk issues its successor's second half and the first
   // half of the chunk after that)
-  stage_c(cs0, lds_h[0], pb, rot, 0);
-  stage_x(xs0, pb, row0, rot, 0, 0);
-  stage_x(xs1, pb, row0, rot, 0, 1);
-  stage_x(xs2, pb, row0, rot, 1, 0);               // every point block has T >= 2 chunks
+  stage_c(cs0, lds_h[0], pb, rot, 0, 0, NCL, true);
+  stage_x(xs0, pb, row0, rot, 0, 0, 0, NXL);
+  stage_x(xs1, pb, row0, rot, 0, 1, 0, NXL);
+  stage_x(xs2, pb, row0, rot, 1, 0, 0, NXL);       // every point block has T >= 2 chunks
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   __syncthreads();
 
@@ -526,10 +534,16 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
           const int s2_row0 = s2_nx ? nrow0 : row0;
           const int s2_rot = s2_nx ? nrot : rot;
           const int s2_t = s2_in ? t + 2 : (has_next ? t + 2 - T : t);
-          stage_c(cn, lds_h[(tc + 1) & 1], s1_pb, s1_rot, s1_t);
-          stage_x(xn1, s1_pb, s1_row0, s1_rot, s1_t, 1);
-          // every staging load stays ahead of the point loads issued below
-          __builtin_amdgcn_sched_barrier(0);
+          // The staging of this chunk is issued one load per (row block,
+          // k-step) pair, between the MFMAs, so the four waves do not queue
+          // all their loads at the address unit at once after the barrier:
+          //   q in [0, NCL):               step + 1's centroid rows (load q;
+          //                                the norms with load 0),
+          //   q in [NSUB, NSUB + NXL):     step + 1's second point half,
+          //   q in [2NSUB, 2NSUB + NXL):   step + 2's first point half (k-steps
+          //                                0-1 are done: their slot is free).
+          // (NCL == NSUB and NXL <= NSUB, so the three ranges are disjoint.)
+          static_assert(NCL == NSUB && NXL <= NSUB, "staging issue order");
           uint4 ar[4], br[2][kNF];
           ar[0] = read_a(cc, 0);
           ar[1] = read_a(cc, 1);
@@ -540,12 +554,12 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
           for (int q = 0; q < Q; ++q) {
             const int sub = q % NSUB, kk = q / NSUB;
             if (sub == 0 && kk + 1 == 2) {
-              // this chunk's second point half was staged at the start of
-              // the previous chunk; the loads issued since (its first half
-              // of the next chunk, this chunk's centroids and norm, the next
-              // chunk's second half) may still be in flight
+              // this chunk's second point half was staged during the
+              // previous chunk; the loads issued since (the first half of
+              // the next chunk, then, in this chunk, the next chunk's
+              // centroids and norms) may still be in flight
               asm volatile("" ::: "memory");
-              __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * NXL + NCL + 1, 15));
+              __builtin_amdgcn_s_waitcnt(waitcnt_imm(NXL + NCL + 1, 15));
               asm volatile("" ::: "memory");
             }
             if (sub == 0 && kk + 1 < kLKS) {           // the next k-step's point fragments
@@ -558,11 +572,14 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
             for (int f = 0; f < kNF; ++f)
               acc[sub][f] = Mfma<DT>::run(ar[q % 4], br[kk & 1][f], acc[sub][f]);
             __builtin_amdgcn_sched_barrier(0);
-            if (q == 2 * NSUB - 1) {
-              // k-steps 0-1 are done: their slot takes step + 2's first half
-              stage_x(P ? xs2 : xs0, s2_pb, s2_row0, s2_rot, s2_t, 0);
-              __builtin_amdgcn_sched_barrier(0);
-            }
+            if (q < NCL)
+              stage_c(cn, lds_h[(tc + 1) & 1], s1_pb, s1_rot, s1_t, q, q + 1, q == 0);
+            else if (q >= NSUB && q < NSUB + NXL)
+              stage_x(xn1, s1_pb, s1_row0, s1_rot, s1_t, 1, q - NSUB, q - NSUB + 1);
+            else if (q >= 2 * NSUB && q < 2 * NSUB + NXL)
+              stage_x(P ? xs2 : xs0, s2_pb, s2_row0, s2_rot, s2_t, 0, q - 2 * NSUB,
+                      q - 2 * NSUB + 1);
+            __builtin_amdgcn_sched_barrier(0);
           }
           // This wave's centroid and norm loads have landed once at most the
           // 2 * NXL point loads issued after them are outstanding. The

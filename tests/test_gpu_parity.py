@@ -508,14 +508,15 @@ def test_status_codes_through_binding(fk):
     assert e.value.status == 1
 
 
-@pytest.mark.parametrize("wl,kw", [("io_breakdown", {"scale_n": 20000, "B": 2}),
+@pytest.mark.parametrize("wl,kw", [("io_breakdown", {}),
                                    ("split_d", {"scale_n": 4096, "B": 2}),
                                    ("tiny_f32", {})])
 def test_trace_records_phases(fk, wl, kw):
     """The trace's phases (kernel-stamped norms and assign, update between
     them) are positive and add up to at most the call's own time on the
-    stream, and (where the device, not the launches, sets the pace) to most
-    of it."""
+    stream, and, where the device and not the host's launches sets the pace
+    (the whole io_breakdown batch, about 0.6 ms an iteration), to most of
+    it."""
     torch = _torch()
     w = synthdata.make_workload(wl, **kw)
     x, init = to_dev(w.x, w.dtype), to_dev(w.init, w.dtype)
@@ -534,10 +535,10 @@ def test_trace_records_phases(fk, wl, kw):
     wall = e0.elapsed_time(e1)
     print(wl, f"phases {total:.4f} ms of {wall:.4f} ms")
     assert total <= 1.02 * wall + 0.02
-    # the tiny problem is launch-bound: its kernels take a few microseconds
-    # each and the stream idles between launches, so only the upper bound
-    # holds there
-    if wl != "tiny_f32":
+    # the small cases are launch-bound: their kernels take microseconds to
+    # tens of microseconds and the stream idles between launches, so only
+    # the upper bound holds there
+    if wl == "io_breakdown":
         assert 0.5 * wall <= total
 
 
