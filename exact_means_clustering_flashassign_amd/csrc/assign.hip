@@ -178,7 +178,8 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
                 : load8<VEC>(row, s * 16 + half * 8, d);
   };
 
-  // Tile loads: rows past K repeat row K-1 and get -inf norms, so they never
+  // Tile loads: rows past K repeat row K-1 and get the never-winning norm term
+  // (kNeverWins, finite so that the slot code stays a number), so they never
   // win. Loads and stores are unconditional (tile indices clamp, every
   // thread owns an lds_h slot) so one tile iteration is a single basic block
   // the scheduler can interleave.
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(WAVES * 64) void assign_smalld_kernel(
   // Two accumulator sets alternate by subtile: while the MFMAs of subtile g
   // fill one set, the argmax of subtile g-1 drains the other, spread over the
   // k-steps, so VALU work issues in the shadow of the matrix core. The first
-  // drain of a point block is of an all -inf set standing for subtile -1.
+  // drain of a point block is of an all-kNeverWins set standing for subtile -1.
   floatx16_t acc[2][NF];
 
   // The switch to the next point block: its first XP k-steps are loaded

@@ -391,7 +391,8 @@ __global__ __launch_bounds__(kThreads) void assign_splitd_lds_kernel(
   // Centroid chunk t of (problem pb) into dst: load j of wave w fills rows
   // w*RPW + 8j .. +7; lane l writes slot l % 8 of row 8j + l / 8, i.e. unit
   // (l % 8) ^ cperm(row). Rows past K lie past the buffer's range and read as
-  // zero (their norms are -inf: they never win).
+  // zero, as do their norms; the argmax of a tile that runs past K masks
+  // them, so they never win.
   // Loads jlo .. jhi-1 of the chunk (and, with norm, the norms' load), so a
   // chunk's staging can be issued a few loads at a time between its MFMAs.
   auto stage_c = [&](unsigned char* dst, float* hdst, int pb, int rot, int t, int jlo, int jhi,
