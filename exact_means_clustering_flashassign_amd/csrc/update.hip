@@ -274,6 +274,21 @@ __device__ __forceinline__ int column_prefix(int32_t* hb, int64_t K, int G, int 
   return run;
 }
 
+// Column k of a problem's H: its total only (H left as it is).
+__device__ __forceinline__ int column_total(const int32_t* hb, int64_t K, int G, int k) {
+  int run = 0;
+  int g = 0;
+  for (; g + 8 <= G; g += 8) {
+    int v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = hb[(g + q) * K + k];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) run += v[q];
+  }
+  for (; g < G; ++g) run += hb[g * K + k];
+  return run;
+}
+
 // offsets (one block per problem, G*K small): column prefixes of H and the
 // counts first, then offsets, run starts and the long-cluster flag.
 __global__ __launch_bounds__(kSortThreads) void offsets_kernel(
@@ -359,7 +374,8 @@ __device__ void radix_group_starts(const int32_t* __restrict__ cs, int32_t* __re
 
 // Large G*K: column prefixes on a grid, one thread per (problem, cluster);
 // block j of a problem also stores the total count of its kThreads clusters
-// in ktot[b * kblocks + j].
+// in ktot[b * kblocks + j]. Without prefix (radix passes build perm, so no
+// scatter reads the per-chunk starts) only the column totals are taken.
 // With rdig (radix passes follow): B * RG more blocks, block (b, rg) summing
 // the first pass's digit counts of radix chunks [rg * kRadixGroup, ...) (GR
 // per problem) into csum0 (no atomics).
@@ -369,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void colscan_kernel(int32_t* __restrict__
                                                            int G, int kblocks, int B,
                                                            const int32_t* __restrict__ rdig,
                                                            int32_t* __restrict__ csum0, int GR,
-                                                           int RG) {
+                                                           int RG, bool prefix) {
   __shared__ int32_t wsum[kThreads / 64];
   if ((int64_t)blockIdx.x >= (int64_t)B * kblocks) {
     const int i = (int)(blockIdx.x - B * kblocks);
@@ -386,7 +402,8 @@ __global__ __launch_bounds__(kThreads) void colscan_kernel(int32_t* __restrict__
   const int k = j * kThreads + threadIdx.x;
   int c = 0;
   if (k < K) {
-    c = column_prefix(H + (int64_t)b * G * K, K, G, k);
+    c = prefix ? column_prefix(H + (int64_t)b * G * K, K, G, k)
+               : column_total(H + (int64_t)b * G * K, K, G, k);
     counts[(int64_t)b * K + k] = c;
   }
   const int tot = block_sum256(c, wsum);
@@ -2037,7 +2054,7 @@ hipError_t run_sort(const int32_t* ids, int dt, int64_t B, int64_t N, int64_t d,
       if (B * (kblocks + RG) > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
       colscan_kernel<<<(unsigned)(B * (kblocks + RG)), kThreads, 0, s>>>(
           ws.hist, counts, ws.ktot, (int)K, G, kblocks, (int)B, rdig, ws.rcolsum, (int)GR,
-          (int)RG);
+          (int)RG, pp != kPermRadix);
       FK_CHECK(hipGetLastError());
       offsets_runs_kernel<<<(unsigned)(B * kblocks + (fuse ? B : 0)), kThreads, 0, s>>>(
           counts, ws.ktot, ws.offsets, ws.run_first, ws.has_long, (int)K, runs, kblocks, (int)B,
