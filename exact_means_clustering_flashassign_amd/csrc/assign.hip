@@ -505,9 +505,10 @@ hipError_t run_small_tile(int tile, const void* x, const void* c, const float* c
 // The tile a problem shape gets (rows of `units` 16-bit units, units <= 128),
 // read off the timing sweep of every candidate over d in {32, 64, 128}, K in
 // {64 .. 4096} and 16K .. 2.4M points (bench.py --tile-sweep):
-//   - 128-unit rows: 8-wave blocks once their 512-point blocks cover every
-//     CU; with fewer points, 4-wave blocks with 128-row tiles (twice the
-//     blocks: up to 1.4x faster at 16K-64K points);
+//   - 128-unit rows: 64-row tiles for K <= 64 (a 128-row tile would be half
+//     padding: 2-12% faster); else 8-wave blocks once their 512-point blocks
+//     cover every CU; with fewer points, 4-wave blocks with 128-row tiles
+//     (twice the blocks: up to 1.4x faster at 16K-64K points);
 //   - 64-unit rows: 64-row tiles for K < 256; above, 128-row 4-wave tiles,
 //     8-wave blocks only for K >= 1024 with 512-point blocks on at least
 //     twice the CUs (within 5% of each other there);
@@ -521,7 +522,7 @@ int small_tile(int64_t units, int64_t K, int64_t B, int64_t N) {
   }
   const int64_t blocks8 = B * ((N + 511) / 512);    // point blocks of the 8-wave tile
   const int64_t cus = device_cus() > 0 ? device_cus() : 256;
-  if (units > 64) return blocks8 >= cus ? kTile8w128 : kTile4w128;
+  if (units > 64) return K <= 64 ? kTile4w64 : (blocks8 >= cus ? kTile8w128 : kTile4w128);
   if (K < 256) return kTile4w64;
   if (units > 32 && K >= 1024 && blocks8 >= 2 * cus) return kTile8w128;
   return kTile4w128;

@@ -689,13 +689,13 @@ const char* const kSplitTileNames[kSplitTiles] = {"lds8", "lds4", "reg8", "reg4"
 // the four candidates over d in {768, 1024}, K in {64, 256, 1000} and 16K ..
 // 262K points (bench.py --tile-sweep): 128-row tiles for K <= 128 (one tile:
 // up to 1.4x faster), 256-row tiles above (x is read once for K <= 256); LDS
-// staging once the 256-point blocks cover every CU (up to 1.3x), register
-// staging below that (up to 1.1x). FK_TILE or FK_SPLITD_REGISTER_STAGING
+// staging wherever the rows allow it (whole 16-byte-aligned rows of a
+// multiple of 128 units: up to 1.3x faster at 262K points, 2-16% at 16K),
+// register staging for other rows. FK_TILE or FK_SPLITD_REGISTER_STAGING
 // override.
-void split_tile(int64_t K, int64_t blocks, bool& lds, bool& rows128) {
-  const int64_t cus = device_cus() > 0 ? device_cus() : 256;
+void split_tile(int64_t K, bool& lds, bool& rows128) {
   rows128 = K <= 128;
-  lds = rows128 || blocks >= cus;
+  lds = true;
   if (const char* e = getenv("FK_TILE")) {
     for (int i = 0; i < kSplitTiles; ++i)
       if (strcmp(e, kSplitTileNames[i]) == 0) {
@@ -733,7 +733,7 @@ template <int DT>
 hipError_t splitd_dt(const void* x, const void* c, const float* cn, int64_t B, int64_t N,
                      int64_t d, int64_t K, int32_t* ids, hipStream_t s) {
   bool lds, rows128;
-  split_tile(K, B * ((N + kBN - 1) / kBN), lds, rows128);
+  split_tile(K, lds, rows128);
   if (rows128 || !vec_ok(x, c, d)) return run_splitd<DT, 4>(x, c, cn, B, N, d, K, ids, lds, s);
   return run_splitd<DT, 8>(x, c, cn, B, N, d, K, ids, lds, s);
 }
