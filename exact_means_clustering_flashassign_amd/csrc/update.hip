@@ -54,6 +54,7 @@
 //             finalize blocks') in a fixed order into shift[b].
 // Empty clusters are never touched, so they keep their centroid. Ids outside
 // [0, K) are skipped: they count nowhere and add to no cluster.
+#include <limits.h>
 #include <stdlib.h>
 
 #include "fk_internal.hpp"
@@ -90,16 +91,35 @@ __global__ __launch_bounds__(kThreads) void fill_f32_kernel(float* __restrict__ 
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
 }
 
+// Inclusive prefix sum / maximum over the 64 lanes of a wave by DPP: within
+// each row of 16 lanes by shifts of 1, 2, 4 and 8 lanes (lanes with no source
+// take 0, or keep their value for the maximum), then across rows by the
+// broadcast of lane 15 into rows 1 and 3 and of lane 31 into rows 2 and 3.
+// Six VALU steps, where a shuffle per step would be an LDS permute each.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ int wave_inclusive_max(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x118, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+
 // Exclusive prefix sum over the kSortThreads threads of a block; `total`
 // receives the block sum. wtot: kSortThreads / 64 ints of LDS.
 __device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wtot, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
+  const int incl = wave_inclusive_sum(v);
   if (lane == 63) wtot[w] = incl;
   __syncthreads();
   int before = 0, all = 0;
@@ -118,12 +138,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wtot, int& t
 // thread 0). wtot: kSortThreads / 64 ints of LDS.
 __device__ __forceinline__ int block_exclusive_max(int v, int32_t* wtot) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl = max(incl, u);
-  }
+  const int incl = wave_inclusive_max(v);
   const int excl_in_wave = __shfl_up(incl, 1, 64);
   if (lane == 63) wtot[w] = incl;
   __syncthreads();
@@ -353,12 +368,7 @@ __device__ void radix_group_starts(const int32_t* __restrict__ cs, int32_t* __re
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   int tot = 0;
   for (int rg = 0; rg < RG; ++rg) tot += cs[(int64_t)rg * kRadixDigits + t];
-  int incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
+  const int incl = wave_inclusive_sum(tot);
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
   int before = 0;
@@ -440,12 +450,7 @@ __global__ __launch_bounds__(kThreads) void offsets_runs_kernel(
   const int base = block_sum256(before, wsum);
   const int k = j * kThreads + t;
   const int c = k < K ? counts[(int64_t)b * K + k] : 0;
-  int incl = c;                                  // inclusive scan within the wave
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
+  const int incl = wave_inclusive_sum(c);        // inclusive scan within the wave
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
   int wbefore = 0, all = 0;
