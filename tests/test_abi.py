@@ -21,7 +21,7 @@ def lib():
     from exact_means_clustering_flashassign_amd import _binding
 
     if not os.path.exists(_binding.LIB_PATH):
-        pytest.fail("libfkmeans.so is not built (run __graft_entry__.build())")
+        pytest.fail("libfkmeans.so is not built (run python -m exact_means_clustering_flashassign_amd.build)")
     return _binding.load()
 
 
@@ -147,7 +147,7 @@ def test_baseline_library_exports_its_header():
     assert names == ["fkb_assign_materialized", "fkb_mfma_peak", "fkb_update_atomic",
                      "fkb_wall_clock_khz"]
     if not os.path.exists(_binding.BASELINE_LIB_PATH):
-        pytest.fail("libfkbaseline.so is not built (run __graft_entry__.build())")
+        pytest.fail("libfkbaseline.so is not built (run python -m exact_means_clustering_flashassign_amd.build)")
     lib = _binding.load_baseline()
     for name in names:
         assert hasattr(lib, name), name
